@@ -1,0 +1,508 @@
+/*
+ * CPU oracle of the routed top-k mixture-of-experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library. The GPU library shares
+ * no code, header, table or constant with it.
+ *
+ * What the layer computes (the first page, the FlyDSL-in-JAX talk summary,
+ * sections 5:56 "Optimierung gerouteter MoE-GEMMs" and 8:14 "End-to-End-Integration
+ * in MaxText"): every token is routed to its top-2 experts; each selected expert
+ * applies a SwiGLU feed-forward block (gate and up projections, SwiGLU, down
+ * projection; glossary entry "SwiGLU"); the k expert outputs are scattered back
+ * to the token and combined with the routing weights. The pages name the pieces
+ * (gather, group GEMM, SwiGLU, scatter, top-2, load-time preshuffle) but write
+ * out no formula; the definitions below are the plainest reading, with the
+ * shapes x[T,H], W_r[E,H], W1/W3[E,I,H], W2[E,H,I] of the Mixtral 8x7B layer.
+ *
+ * Arithmetic: fp64 everywhere, except where a floating-point result decides an
+ * integer that must match the GPU bit for bit. Those decisions are taken in the
+ * GPU's precision, fp32:
+ *   - router logits (they decide the top-k ids), summed in one fixed order;
+ *   - per-token activation quantisation to e4m3fn (fp32 divide, then RNE).
+ * Storage roundings that the method itself prescribes are applied: the bf16
+ * SwiGLU intermediate on the bf16 path, the per-row e4m3fn requantisation of the
+ * intermediate on the fp8 path, and the bf16 output.
+ *
+ * Each function is plain loops; OpenMP only splits independent output rows.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_BF16 = 0, ORACLE_FP8 = 1 };
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+
+/* bf16 is the upper half of an IEEE binary32. */
+double oracle_bf16_to_f64(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round a binary32 to bf16, to nearest with ties to even; NaN stays NaN. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* OCP 8-bit float E4M3 ("fn": finite, no infinities): 1 sign bit, 4 exponent
+ * bits with bias 7, 3 mantissa bits. Exponent field 0 is subnormal
+ * (m * 2^-9); S.1111.111 is NaN; the largest finite magnitude is 448. */
+double oracle_e4m3fn_to_f64(uint8_t q)
+{
+    int s = q >> 7, e = (q >> 3) & 15, m = q & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Nearest e4m3fn code to v, ties to the even code; |v| beyond 448 saturates
+ * to +-448. Positive codes 0x00..0x7E increase with their value, so the two
+ * neighbours of |v| are found by a search over that ordered table. */
+uint8_t oracle_f32_to_e4m3fn(float v)
+{
+    if (isnan(v))
+        return 0x7f;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return sign | 0x7e;
+    int lo = 0, hi = 0x7e; /* value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (oracle_e4m3fn_to_f64((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dl = a - oracle_e4m3fn_to_f64((uint8_t)lo);
+    double dh = oracle_e4m3fn_to_f64((uint8_t)hi) - a;
+    int c;
+    if (dl < dh)
+        c = lo;
+    else if (dh < dl)
+        c = hi;
+    else
+        c = (lo & 1) ? hi : lo;
+    return sign | (uint8_t)c;
+}
+
+static double wval(int dtype, const void* w, size_t idx)
+{
+    if (dtype == ORACLE_BF16)
+        return oracle_bf16_to_f64(((const uint16_t*)w)[idx]);
+    return oracle_e4m3fn_to_f64(((const uint8_t*)w)[idx]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router: logits, top-k, renormalised weights                               */
+
+/* Router logit of token row x against expert row w, in fp32, in the fixed
+ * summation order that is part of this layer's contract:
+ *   - the H products are split over 64 partial sums ("lanes"): element h goes
+ *     to lane (h / 8) mod 64, i.e. lanes own 8-element chunks round robin;
+ *   - each lane adds its products in ascending h, acc = acc + x*w;
+ *   - the 64 partials are then folded pairwise: for off = 32,16,8,4,2,1,
+ *     p[l] = p[l] + p[l+off] for l < off; the logit is p[0].
+ * A bf16*bf16 product has at most 16 significant bits, so it is exact in
+ * fp32 and a fused multiply-add gives the same sums. */
+float oracle_logit(const uint16_t* x, const uint16_t* w, int H)
+{
+    float p[64];
+    for (int l = 0; l < 64; ++l)
+        p[l] = 0.0f;
+    for (int h = 0; h < H; ++h) {
+        int lane = (h / 8) % 64;
+        float prod = (float)oracle_bf16_to_f64(x[h]) * (float)oracle_bf16_to_f64(w[h]);
+        p[lane] = p[lane] + prod;
+    }
+    for (int off = 32; off >= 1; off /= 2)
+        for (int l = 0; l < off; ++l)
+            p[l] = p[l] + p[l + off];
+    return p[0];
+}
+
+/* Top-k of one token's E logits: rank j is the largest logit not yet taken,
+ * ties going to the lower expert index (IEEE comparison: -0 == +0). The
+ * routing weights are the softmax over the k selected logits, which equals the
+ * full softmax renormalised over the selected experts. */
+static void topk_one(const float* l, int E, int k, int32_t* ids, float* w)
+{
+    int taken[64] = {0};
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            if (taken[e])
+                continue;
+            if (best < 0 || l[e] > l[best])
+                best = e;
+        }
+        taken[best] = 1;
+        ids[j] = best;
+    }
+    double den = 0.0, num[64];
+    for (int j = 0; j < k; ++j) {
+        num[j] = exp((double)l[ids[j]] - (double)l[ids[0]]);
+        den += num[j];
+    }
+    for (int j = 0; j < k; ++j)
+        w[j] = (float)(num[j] / den);
+}
+
+/* ids[T,k], w[T,k]; logits[T,E] when non-NULL. bias[E] (fp32, may be NULL) is
+ * added to each logit as one fp32 addition before selection. */
+void oracle_route(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                  int T, int H, int E, int k, int32_t* ids, float* w, float* logits)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        float l[64];
+        for (int e = 0; e < E; ++e) {
+            l[e] = oracle_logit(x + (size_t)t * H, w_router + (size_t)e * H, H);
+            if (bias)
+                l[e] = l[e] + bias[e];
+            if (logits)
+                logits[(size_t)t * E + e] = l[e];
+        }
+        topk_one(l, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+    }
+}
+
+/* Top-k and weights from given logits (used to tell apart summation-order
+ * differences from selection differences). */
+void oracle_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w)
+{
+    for (int t = 0; t < T; ++t)
+        topk_one(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic per-token activation quantisation (fp8 path)                      */
+
+/* scale s_t = amax_t / 448 in fp32 (1 when the row is all zero);
+ * code = e4m3fn(clamp(x / s_t, -448, 448)), the divide in fp32. */
+void oracle_quant_tokens(const uint16_t* x, int T, int H, uint8_t* xq, float* xs)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const uint16_t* r = x + (size_t)t * H;
+        float amax = 0.0f;
+        for (int h = 0; h < H; ++h) {
+            float a = fabsf((float)oracle_bf16_to_f64(r[h]));
+            if (a > amax)
+                amax = a;
+        }
+        float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        xs[t] = s;
+        for (int h = 0; h < H; ++h) {
+            float v = (float)oracle_bf16_to_f64(r[h]) / s;
+            if (v > 448.0f)
+                v = 448.0f;
+            if (v < -448.0f)
+                v = -448.0f;
+            xq[(size_t)t * H + h] = oracle_f32_to_e4m3fn(v);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Grouping token-slots by expert, padded to the M-tile                      */
+
+/* Slot s = t*k + j is the j-th expert choice of token t. For e = 0..E-1 the
+ * group of expert e lists, in ascending s, every slot routed to e, and is then
+ * padded with the sentinel T*k up to a multiple of bm. tile_expert holds the
+ * expert of each bm-row tile. Returns 0, or -1 when an id is out of range. */
+int oracle_align(const int32_t* ids, int T, int k, int E, int bm, int32_t* sorted_slot,
+                 int32_t* tile_expert, int32_t* count, int32_t* offset, int32_t* total)
+{
+    int S = T * k, pos = 0;
+    for (int s = 0; s < S; ++s)
+        if (ids[s] < 0 || ids[s] >= E)
+            return -1;
+    for (int e = 0; e < E; ++e) {
+        offset[e] = pos;
+        int c = 0;
+        for (int s = 0; s < S; ++s)
+            if (ids[s] == e)
+                sorted_slot[pos + c++] = s;
+        count[e] = c;
+        int padded = (c + bm - 1) / bm * bm;
+        for (int p = c; p < padded; ++p)
+            sorted_slot[pos + p] = S;
+        for (int tl = 0; tl < padded / bm; ++tl)
+            tile_expert[pos / bm + tl] = e;
+        pos += padded;
+    }
+    offset[E] = pos;
+    *total = pos;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert feed-forward (SwiGLU) and the weighted combine                     */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Input row x_hat of token t in fp64: the bf16 value, or on the fp8 path the
+ * dequantised code of the per-token quantisation. */
+static void token_row(int dtype, const uint16_t* x, int t, int H, double* xh)
+{
+    const uint16_t* r = x + (size_t)t * H;
+    if (dtype == ORACLE_BF16) {
+        for (int h = 0; h < H; ++h)
+            xh[h] = oracle_bf16_to_f64(r[h]);
+        return;
+    }
+    uint8_t* q = (uint8_t*)malloc((size_t)H);
+    float s;
+    oracle_quant_tokens(r, 1, H, q, &s);
+    for (int h = 0; h < H; ++h)
+        xh[h] = oracle_e4m3fn_to_f64(q[h]) * (double)s;
+    free(q);
+}
+
+/* SwiGLU intermediate of one (token, expert) pair, before storage rounding:
+ * a_i = silu(g_i) * u_i, g = W1[e] x_hat, u = W3[e] x_hat, with dequantised
+ * weights W = code * s[e,i] on the fp8 path. */
+static void swiglu_row(int dtype, const double* xh, const void* w1, const void* w3,
+                       const float* s1, const float* s3, int e, int H, int I, double* a)
+{
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < I; ++i) {
+        size_t row = ((size_t)e * I + i) * (size_t)H;
+        double sg = dtype == ORACLE_FP8 ? (double)s1[(size_t)e * I + i] : 1.0;
+        double su = dtype == ORACLE_FP8 ? (double)s3[(size_t)e * I + i] : 1.0;
+        double g = 0.0, u = 0.0;
+        for (int h = 0; h < H; ++h) {
+            g += xh[h] * (wval(dtype, w1, row + h) * sg);
+            u += xh[h] * (wval(dtype, w3, row + h) * su);
+        }
+        a[i] = silu(g) * u;
+    }
+}
+
+/* The intermediate as stage two reads it: bf16 storage on the bf16 path
+ * (fp32, then bf16, both round-to-nearest-even); on the fp8 path a per-row
+ * requantisation, scale = max|a| / 448 (1 if zero), code = e4m3fn(a / scale),
+ * value = code * scale. */
+static void store_intermediate(int dtype, double* a, int I)
+{
+    if (dtype == ORACLE_BF16) {
+        for (int i = 0; i < I; ++i)
+            a[i] = oracle_bf16_to_f64(oracle_f32_to_bf16((float)a[i]));
+        return;
+    }
+    double amax = 0.0;
+    for (int i = 0; i < I; ++i)
+        if (fabs(a[i]) > amax)
+            amax = fabs(a[i]);
+    double s = amax > 0.0 ? amax / 448.0 : 1.0;
+    for (int i = 0; i < I; ++i) {
+        double v = a[i] / s;
+        if (v > 448.0)
+            v = 448.0;
+        if (v < -448.0)
+            v = -448.0;
+        a[i] = oracle_e4m3fn_to_f64(oracle_f32_to_e4m3fn((float)v)) * s;
+    }
+}
+
+/* Down projection y_h = sum_i a_i * W2[e,h,i]. */
+static void down_row(int dtype, const double* a, const void* w2, const float* s2, int e,
+                     int H, int I, double* y)
+{
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < H; ++h) {
+        size_t row = ((size_t)e * H + h) * (size_t)I;
+        double sd = dtype == ORACLE_FP8 ? (double)s2[(size_t)e * H + h] : 1.0;
+        double acc = 0.0;
+        for (int i = 0; i < I; ++i)
+            acc += a[i] * (wval(dtype, w2, row + i) * sd);
+        y[h] = acc;
+    }
+}
+
+/* SwiGLU intermediate rows for given (token, expert) pairs, before storage
+ * rounding (stage-one parity). act[n, I] in fp64. */
+void oracle_swiglu(int dtype, const uint16_t* x, const void* w1, const void* w3,
+                   const float* s1, const float* s3, int T, int H, int I,
+                   const int32_t* tokens, const int32_t* experts, int n, double* act)
+{
+    double* xh = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int r = 0; r < n; ++r) {
+        (void)T;
+        token_row(dtype, x, tokens[r], H, xh);
+        swiglu_row(dtype, xh, w1, w3, s1, s3, experts[r], H, I, act + (size_t)r * I);
+    }
+    free(xh);
+}
+
+/* Down projection of given intermediate rows (already in the value they are
+ * stored at) through given experts: y[n, H] in fp64 (stage-two parity). */
+void oracle_down(int dtype, const double* act, const void* w2, const float* s2,
+                 int H, int I, const int32_t* experts, int n, double* y)
+{
+    for (int r = 0; r < n; ++r)
+        down_row(dtype, act + (size_t)r * I, w2, s2, experts[r], H, I, y + (size_t)r * H);
+}
+
+/* The whole layer for the listed tokens: route, (quantise), for j in 0..k-1
+ * the selected expert's SwiGLU block, then out = bf16(sum_j w_j * y_j) with the
+ * sum taken in ascending j. out_bf16[n,H]; out_f64[n,H] (the value before the
+ * final rounding) when non-NULL. */
+void oracle_forward(int dtype, const uint16_t* x, const uint16_t* w_router, const float* bias,
+                    const void* w1, const void* w3, const void* w2, const float* s1,
+                    const float* s3, const float* s2, int T, int H, int I, int E, int k,
+                    const int32_t* tokens, int n, uint16_t* out_bf16, double* out_f64)
+{
+    double* xh = (double*)malloc(sizeof(double) * (size_t)H);
+    double* a = (double*)malloc(sizeof(double) * (size_t)I);
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+    double* o = (double*)malloc(sizeof(double) * (size_t)H);
+    int32_t ids[64];
+    float w[64];
+    for (int r = 0; r < n; ++r) {
+        int t = tokens[r];
+        (void)T;
+        oracle_route(x + (size_t)t * H, w_router, bias, 1, H, E, k, ids, w, NULL);
+        token_row(dtype, x, t, H, xh);
+        for (int h = 0; h < H; ++h)
+            o[h] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            swiglu_row(dtype, xh, w1, w3, s1, s3, ids[j], H, I, a);
+            store_intermediate(dtype, a, I);
+            down_row(dtype, a, w2, s2, ids[j], H, I, y);
+            for (int h = 0; h < H; ++h)
+                o[h] = o[h] + (double)w[j] * y[h];
+        }
+        for (int h = 0; h < H; ++h) {
+            if (out_f64)
+                out_f64[(size_t)r * H + h] = o[h];
+            out_bf16[(size_t)r * H + h] = oracle_f32_to_bf16((float)o[h]);
+        }
+    }
+    free(xh);
+    free(a);
+    free(y);
+    free(o);
+}
+
+/* Apply the intermediate storage rounding to n rows of I values in place. */
+void oracle_store_intermediate(int dtype, double* act, int n, int I)
+{
+    for (int r = 0; r < n; ++r)
+        store_intermediate(dtype, act + (size_t)r * I, I);
+}
+
+/* ------------------------------------------------------------------------ */
+/* One-time weight preshuffle into MFMA operand order                        */
+
+/* The layout the GPU library stores expert weights in (load time only, not
+ * arithmetic). A weight matrix with R rows (output features) and K columns
+ * (the reduction) is cut into fragments of 16 rows x KE columns, KE = 32 for
+ * bf16 and 128 for e4m3fn (one matrix-core K step). Fragments are stored
+ * row-block major, then K-block; inside a fragment, lane l = 0..63 holds row
+ * l mod 16 and the KE/4 consecutive columns starting at (l / 16) * KE/4,
+ * lane after lane. For the gate/up pair the rows of one expert are taken in
+ * blocks of 16 alternating W1, W3: composite row c is W1 row (c/32)*16 + c%16
+ * when (c/16) is even, W3 row of the same index when it is odd. */
+/* Source row c of the composite gate/up matrix of one expert. */
+static const uint8_t* w13_row(const uint8_t* w1, const uint8_t* w3, size_t rowbytes, int c)
+{
+    int i = (c / 32) * 16 + c % 16;
+    return (((c / 16) % 2 == 0) ? w1 : w3) + (size_t)i * rowbytes;
+}
+
+void oracle_preshuffle_w13(int dtype, int E, int H, int I, const void* w1, const void* w3,
+                           void* out)
+{
+    int es = dtype == ORACLE_BF16 ? 2 : 1, KE = dtype == ORACLE_BF16 ? 32 : 128;
+    int LB = KE / 4 * es, kblocks = H / KE;
+    size_t per = (size_t)I * H * es;
+    for (int e = 0; e < E; ++e) {
+        const uint8_t* a = (const uint8_t*)w1 + e * per;
+        const uint8_t* b = (const uint8_t*)w3 + e * per;
+        uint8_t* o = (uint8_t*)out + 2 * e * per;
+        for (int rb = 0; rb < 2 * I / 16; ++rb)
+            for (int kb = 0; kb < kblocks; ++kb)
+                for (int l = 0; l < 64; ++l) {
+                    int c = rb * 16 + l % 16;
+                    int k0 = kb * KE + (l / 16) * (KE / 4);
+                    const uint8_t* src = w13_row(a, b, (size_t)H * es, c) + (size_t)k0 * es;
+                    memcpy(o + (((size_t)rb * kblocks + kb) * 64 + l) * LB, src, (size_t)LB);
+                }
+    }
+}
+
+void oracle_preshuffle_w2(int dtype, int E, int H, int I, const void* w2, void* out)
+{
+    int es = dtype == ORACLE_BF16 ? 2 : 1, KE = dtype == ORACLE_BF16 ? 32 : 128;
+    int LB = KE / 4 * es, kblocks = I / KE;
+    size_t per = (size_t)H * I * es;
+    for (int e = 0; e < E; ++e) {
+        const uint8_t* a = (const uint8_t*)w2 + e * per;
+        uint8_t* o = (uint8_t*)out + e * per;
+        for (int rb = 0; rb < H / 16; ++rb)
+            for (int kb = 0; kb < kblocks; ++kb)
+                for (int l = 0; l < 64; ++l) {
+                    int h = rb * 16 + l % 16;
+                    int k0 = kb * KE + (l / 16) * (KE / 4);
+                    const uint8_t* src = a + ((size_t)h * I + k0) * es;
+                    memcpy(o + (((size_t)rb * kblocks + kb) * 64 + l) * LB, src, (size_t)LB);
+                }
+    }
+}
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Array forms of the format conversions (same definitions, element by element). */
+void oracle_f32_to_e4m3fn_n(const float* v, long n, uint8_t* q)
+{
+    for (long i = 0; i < n; ++i)
+        q[i] = oracle_f32_to_e4m3fn(v[i]);
+}
+
+void oracle_e4m3fn_to_f64_n(const uint8_t* q, long n, double* v)
+{
+    for (long i = 0; i < n; ++i)
+        v[i] = oracle_e4m3fn_to_f64(q[i]);
+}
+
+void oracle_f32_to_bf16_n(const float* v, long n, uint16_t* b)
+{
+    for (long i = 0; i < n; ++i)
+        b[i] = oracle_f32_to_bf16(v[i]);
+}
+
+void oracle_bf16_to_f64_n(const uint16_t* b, long n, double* v)
+{
+    for (long i = 0; i < n; ++i)
+        v[i] = oracle_bf16_to_f64(b[i]);
+}

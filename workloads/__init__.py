@@ -1,0 +1,195 @@
+"""Seeded synthetic inputs for the routed top-k MoE layer.
+
+This module only draws random numbers and stores them in the input formats the
+layer consumes (bf16 bit patterns, OCP e4m3fn codes with per-channel fp32
+scales). It holds none of the layer's own arithmetic: no routing, no top-k, no
+GEMM, no SwiGLU, no activation quantisation. Both the CPU oracle and the HIP
+path take their inputs from here, so they see identical bytes.
+
+Shapes and distributions follow the five workloads of the benchmark spec:
+a tiny bf16 layer, and the Mixtral 8x7B expert layer (H=4096, I=14336, E=8,
+top-2) in bf16 decode, fp8 prefill, an fp8 decode sweep and an fp8 layer with
+skewed routing. Mixtral 8x7B in FP8 is the model the first page (the FlyDSL-in-JAX
+talk summary, "Wichtigste Punkte", 5:56-9:14) measures on; the pages use no dataset.
+
+Weight quantisation for the fp8 workloads (one fp32 scale per output channel,
+scale = amax/448, codes by round-to-nearest-even with saturation) is load-time
+input preparation, done here with torch's float8_e4m3fn cast. It is not part of
+the hot path: the library's entry points take the codes and scales as inputs.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+MIXTRAL = dict(H=4096, I=14336, E=8, k=2)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    dtype: str            # "bf16" or "fp8"
+    sigma_x: float
+    sigma_r: float
+    sigma_w: float
+    seed: int
+    skewed: bool = False  # router bias that sends ~40% of slots to expert 0
+    x_seed: tuple = field(default=())  # extra seed words for x only (decode sweep)
+
+    @property
+    def slots(self) -> int:
+        return self.T * self.k
+
+    def flops(self) -> float:
+        """Useful flops of one layer call: 2*3*H*I per token-slot."""
+        return 6.0 * self.H * self.I * self.slots
+
+
+def config(i: int, T: int | None = None) -> Workload:
+    """The i-th workload (0..4). Workload 3 is a sweep; pass T in {1,4,16,64,256}."""
+    m = MIXTRAL
+    if i == 0:
+        return Workload("tiny-bf16-T32", 32, 128, 256, 8, 2, "bf16",
+                        1.0, 1.0 / math.sqrt(128.0), 0.05, 0)
+    if i == 1:
+        return Workload("mixtral-bf16-decode-T16", 16, m["H"], m["I"], m["E"], m["k"], "bf16",
+                        1.0, 1.0 / 64.0, 0.02, 1)
+    if i == 2:
+        return Workload("mixtral-fp8-prefill-T8192", 8192, m["H"], m["I"], m["E"], m["k"], "fp8",
+                        1.0, 1.0 / 64.0, 0.02, 2)
+    if i == 3:
+        T = 16 if T is None else int(T)
+        assert T in DECODE_SWEEP, T
+        return Workload(f"mixtral-fp8-decode-T{T}", T, m["H"], m["I"], m["E"], m["k"], "fp8",
+                        1.0, 1.0 / 64.0, 0.02, 3, x_seed=(T,))
+    if i == 4:
+        return Workload("mixtral-fp8-skewed-T16384", 16384, m["H"], m["I"], m["E"], m["k"], "fp8",
+                        1.0, 1.0 / 64.0, 0.02, 4, skewed=True)
+    raise ValueError(i)
+
+
+DECODE_SWEEP = (1, 4, 16, 64, 256)
+
+
+def scaled(w: Workload, **kw) -> Workload:
+    """A copy of a workload with some fields replaced (used for small parity shapes)."""
+    d = dict(w.__dict__)
+    d.update(kw)
+    return Workload(**d)
+
+
+# ---------------------------------------------------------------------------
+# format helpers (storage only)
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 array -> uint16 bf16 bit patterns (torch's round-to-nearest-even cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def quantize_rows_fp8(a: np.ndarray):
+    """Per-row (output channel) e4m3fn codes and fp32 scales, scale = amax/448.
+
+    Returns (codes uint8 [R, C], scales float32 [R]). A row of zeros gets scale 1.
+    """
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    amax = t.abs().amax(dim=1)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (t / s[:, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy(), s.numpy().astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Inputs:
+    """Host copies of one workload's inputs, in the layer's storage formats."""
+    wl: Workload
+    x: np.ndarray            # uint16 bf16 [T, H]
+    w_router: np.ndarray     # uint16 bf16 [E, H]
+    bias: np.ndarray | None  # float32 [E] or None
+    w1: np.ndarray           # bf16 uint16 or e4m3fn uint8, [E, I, H] (gate)
+    w3: np.ndarray           # same, [E, I, H] (up)
+    w2: np.ndarray           # same, [E, H, I] (down)
+    s1: np.ndarray | None    # float32 [E, I] (fp8 only)
+    s3: np.ndarray | None    # float32 [E, I]
+    s2: np.ndarray | None    # float32 [E, H]
+
+
+def _normal(seed_words, shape, sigma) -> np.ndarray:
+    rng = np.random.default_rng(np.random.SeedSequence(list(seed_words)))
+    a = rng.standard_normal(shape, dtype=np.float32)
+    if sigma != 1.0:
+        a *= np.float32(sigma)
+    return a
+
+
+def skew_bias(E: int) -> np.ndarray:
+    """Router bias of the skewed workload: (beta, 0, ..., 0, -gamma, -gamma).
+
+    beta and gamma were calibrated once by workloads/calibrate_skew.py (which
+    routes with the oracle) and stored in skew_bias.json.
+    """
+    with open(os.path.join(_HERE, "skew_bias.json")) as f:
+        d = json.load(f)
+    b = np.zeros(E, np.float32)
+    b[0] = d["beta"]
+    b[E - 2] = -d["gamma"]
+    b[E - 1] = -d["gamma"]
+    return b
+
+
+def generate(wl: Workload, weights: bool = True, threads: int = 8) -> Inputs:
+    """Draw the inputs of a workload. Tensors are drawn in the fixed order
+    x, W_r, W1, W3, W2 from independent child streams of the workload's seed."""
+    T, H, I, E = wl.T, wl.H, wl.I, wl.E
+    x = to_bf16_bits(_normal((wl.seed, 0) + tuple(wl.x_seed), (T, H), wl.sigma_x))
+    wr = to_bf16_bits(_normal((wl.seed, 1), (E, H), wl.sigma_r))
+    bias = skew_bias(E) if wl.skewed else None
+    if not weights:
+        return Inputs(wl, x, wr, bias, None, None, None, None, None, None)
+
+    # One child stream per (matrix, expert) so experts can be drawn in parallel.
+    jobs = []
+    for m, (rows, cols) in enumerate(((I, H), (I, H), (H, I))):
+        for e in range(E):
+            jobs.append((m, e, rows, cols))
+
+    def draw(job):
+        m, e, rows, cols = job
+        a = _normal((wl.seed, 2 + m, e), (rows, cols), wl.sigma_w)
+        if wl.dtype == "bf16":
+            return job, to_bf16_bits(a), None
+        q, s = quantize_rows_fp8(a)
+        return job, q, s
+
+    wdt = np.uint16 if wl.dtype == "bf16" else np.uint8
+    w1 = np.empty((E, I, H), wdt)
+    w3 = np.empty((E, I, H), wdt)
+    w2 = np.empty((E, H, I), wdt)
+    mats = (w1, w3, w2)
+    fp8 = wl.dtype == "fp8"
+    s1 = np.empty((E, I), np.float32) if fp8 else None
+    s3 = np.empty((E, I), np.float32) if fp8 else None
+    s2 = np.empty((E, H), np.float32) if fp8 else None
+    scales = (s1, s3, s2)
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        for (m, e, _, _), q, s in ex.map(draw, jobs):
+            mats[m][e] = q
+            if fp8:
+                scales[m][e] = s
+    return Inputs(wl, x, wr, bias, w1, w3, w2, s1, s3, s2)
