@@ -1,0 +1,186 @@
+/*
+ * moe.h - C ABI of the routed top-k mixture-of-experts layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer is the one the first page (the FlyDSL-in-JAX talk summary) describes
+ * under "Optimierung gerouteter MoE-GEMMs" (5:56) and "End-to-End-Integration in
+ * MaxText" (8:14): tokens are routed to their top-2 experts, the selected tokens
+ * are gathered, a grouped ("Group") GEMM computes each expert's gate and up
+ * projections with a SwiGLU, a second grouped GEMM computes the down
+ * projection, and the results are scattered back and combined with the routing
+ * weights; expert weights are rearranged once at load time ("einmaliger
+ * Load-Time-Preshuffle"). The same talk summary describes the call boundary it
+ * used ("fly_call", 4:07; the C trampoline that unpacks buffers, scalars and
+ * streams, 5:05): this header is the same kind of boundary, a set of C calls
+ * taking device pointers, sizes and a stream.
+ *
+ * Shapes: x[T,H] tokens, W_r[E,H] router, W1/W3[E,I,H] gate/up, W2[E,H,I] down,
+ * top-k with k <= E. Element types: bf16, or OCP e4m3fn ("FP8", the precision the
+ * talk summary's Mixtral 8x7B kernel runs in, 5:56/7:31) with fp32 scales.
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers owned by the caller, allocated
+ *     with at least the documented size, 16-byte aligned unless noted. The
+ *     library never allocates or frees memory and keeps no state between calls.
+ *   - Calls are asynchronous and ordered on `stream` (hipStream_t, may be 0).
+ *     Nothing is copied back to the host; device-side counts (total_padded)
+ *     stay on the device and later kernels read them there.
+ *   - Arguments are checked on the host before any HIP call; a failed check
+ *     returns an error code and launches nothing. moe_last_error() then holds
+ *     a message naming the argument.
+ *   - T == 0 returns MOE_OK and launches nothing (no output is written).
+ *   - Layout is row-major; bf16 is passed as its 16-bit pattern, e4m3fn as
+ *     its 8-bit code.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* null or misaligned pointer, negative size, k > E ... */
+    MOE_ERR_UNSUPPORTED = 2, /* shape outside the supported set (see each call)     */
+    MOE_ERR_WORKSPACE = 3,   /* workspace smaller than the size query returned      */
+    MOE_ERR_HIP = 4          /* a HIP launch reported an error                      */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3FN = 1 } moe_dtype;
+
+/* Static string for a status code. */
+const char* moe_status_string(int status);
+/* Message of the last failed call on this host thread ("" if none). */
+const char* moe_last_error(void);
+/* Library version string. */
+const char* moe_version(void);
+
+/*
+ * moe_route - router logits, top-k selection, renormalised routing weights,
+ * and (optionally) the per-token FP8 quantisation of x.
+ *
+ * Top-2 routing is the talk summary's Mixtral setting (8:14); small-K TopK is
+ * one of the operators the second page (the PyTorch FlyDSL news item, "Das
+ * Wichtigste in Kürze") lists. Definition:
+ *   l[t,e] = sum_h x[t,h] * W_r[e,h] (+ bias[e]), in fp32, in this fixed order
+ *     so that ids are reproducible bit for bit: the H products go to 64
+ *     partial sums, element h to partial (h/8) mod 64; each partial adds its
+ *     products in ascending h; the partials are then folded pairwise,
+ *     p[l] += p[l+off] for off = 32,16,8,4,2,1; l = p[0]; then one fp32 add
+ *     of bias[e].
+ *   ids[t, 0..k-1]: experts in order of decreasing logit, ties to the lower
+ *     expert index (IEEE compare, -0 == +0).
+ *   w[t,j] = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)  (softmax over the k
+ *     selected logits = full softmax renormalised over the selection), fp32.
+ *   FP8 (when x_q != NULL): s_t = max_h |x[t,h]| / 448 (1 if that is 0), fp32;
+ *     x_q[t,h] = e4m3fn(clamp(x[t,h] / s_t, -448, 448)), fp32 divide,
+ *     round to nearest even.
+ *
+ * x        bf16 [T,H]          w_router bf16 [E,H]       bias fp32 [E] or NULL
+ * topk_ids int32 [T,k] (out)   topk_w   fp32 [T,k] (out)
+ * logits   fp32 [T,E] (out) or NULL
+ * x_q      uint8 [T,H] (out) or NULL; x_scale fp32 [T] (out), required iff x_q
+ * Supported: H % 128 == 0, 1 <= E <= 64, 1 <= k <= min(E, 8).
+ */
+moe_status moe_route(const void* x, const void* w_router, const float* bias, int T, int H,
+                     int E, int k, int32_t* topk_ids, float* topk_w, float* logits, void* x_q,
+                     float* x_scale, hipStream_t stream);
+
+/*
+ * moe_align - groups the T*k token-slots by expert and pads each group to the
+ * M-tile (the "dynamic expert sizes" of the talk summary, 5:56).
+ *
+ * Slot s = t*k + j is token t's j-th choice. For e = 0..E-1 in turn, the
+ * group of e lists every slot with topk_ids[s] == e in ascending s, followed
+ * by the sentinel T*k up to a multiple of block_m.
+ *   expert_count[e]   slots of expert e
+ *   expert_offset[e]  first row of e's group (expert_offset[E] = total)
+ *   total_padded[0]   sum_e ceil(count_e / block_m) * block_m
+ *   sorted_slot[p]    slot in padded row p, for p < total_padded
+ *   tile_expert[i]    expert of rows [i*block_m, (i+1)*block_m), i < total/block_m
+ * Entries past total_padded are not written.
+ *
+ * topk_ids int32 [T*k]; sorted_slot int32 [moe_align_capacity()];
+ * tile_expert int32 [capacity/block_m]; expert_count int32 [E];
+ * expert_offset int32 [E+1]; total_padded int32 [1]. All device memory.
+ * An id outside [0,E) makes total_padded 0 (nothing downstream runs).
+ * Supported: block_m in {16, 32, 64, 128}, 1 <= E <= 64.
+ */
+int64_t moe_align_capacity(int T, int k, int E, int block_m); /* ceil((T*k+E*(bm-1))/bm)*bm */
+moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                     int32_t* sorted_slot, int32_t* tile_expert, int32_t* expert_count,
+                     int32_t* expert_offset, int32_t* total_padded, hipStream_t stream);
+
+/*
+ * moe_preshuffle - one-time, load-time relayout of the expert weights into the
+ * order the matrix-core kernels read them in (talk summary 8:14). A pure byte
+ * permutation: weights are cut into fragments of 16 output rows x KE reduction
+ * columns (KE = 32 for bf16, 128 for e4m3fn, one matrix-core K step), stored
+ * row-block major then K-block; inside a fragment lane l = 0..63 holds row
+ * l mod 16 and the KE/4 consecutive columns starting at (l/16)*KE/4. Gate and
+ * up rows are interleaved in blocks of 16 (W1 block, W3 block, ...), so one
+ * wave holds the gate and up value of the same intermediate column.
+ *
+ * w1, w3   [E,I,H] row-major; w2 [E,H,I] row-major (bf16 or e4m3fn codes)
+ * s1, s3   fp32 [E,I]; s2 fp32 [E,H] per-output-channel scales (FP8 only, else NULL)
+ * w13_out  [moe_preshuffle_bytes(dt,E,H,I,0)] bytes; w2_out [.., 1] bytes
+ * s13_out  fp32 [E,2,I] (gate scales then up scales); s2_out fp32 [E,H]   (FP8 only)
+ * Supported: H % 128 == 0 and I % 128 == 0 (bf16), H % 256 and I % 256 (FP8).
+ */
+int64_t moe_preshuffle_bytes(moe_dtype dt, int E, int H, int I, int which /*0: W1+W3, 1: W2*/);
+moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, const void* w3,
+                          const void* w2, const float* s1, const float* s3, const float* s2,
+                          void* w13_out, void* w2_out, float* s13_out, float* s2_out,
+                          hipStream_t stream);
+
+/*
+ * moe_stage1 - gather + grouped gate/up GEMM + SwiGLU (talk summary 5:56; the
+ * SwiGLU of its glossary). For each padded row p < total_padded with slot
+ * s = sorted_slot[p], token t = s / k, expert e = tile_expert[p / block_m]:
+ *   g = W1[e] x_t, u = W3[e] x_t (fp32 accumulation; FP8: x_t = x_q[t]*x_scale[t],
+ *   W = code * scale), act[p, i] = bf16(silu(g_i) * u_i), silu(z) = z/(1+e^-z).
+ * Pad rows (s == T*k) get act = 0.
+ * FP8 also writes act_amax: per row p, partial maxima of |act[p,:]| over column
+ * blocks, [moe_stage1_amax_floats()/capacity][capacity] floats; stage 2 reduces them.
+ *
+ * x_or_xq  bf16 [T,H] (BF16) or e4m3fn [T,H] (FP8, from moe_route)
+ * x_scale  fp32 [T] (FP8) or NULL; w13, s13 from moe_preshuffle
+ * sorted_slot, tile_expert, total_padded from moe_align with the same block_m
+ * act      bf16 [capacity, I] (out); act_amax as above (FP8) or NULL
+ */
+int64_t moe_stage1_amax_floats(moe_dtype dt, int T, int k, int E, int H, int I, int block_m);
+moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, const void* w13,
+                      const float* s13, const int32_t* sorted_slot, const int32_t* tile_expert,
+                      const int32_t* total_padded, int T, int k, int E, int H, int I,
+                      int block_m, void* act, float* act_amax, hipStream_t stream);
+
+/*
+ * moe_stage2 - grouped down GEMM + weighted scatter-combine (talk summary 5:56,
+ * "Scatter"). For each real row p (slot s, token t = s / k, expert e):
+ *   y = W2[e] act_p   (FP8: act_p requantised per row, scale = max|act_p|/448,
+ *                      code = e4m3fn(act_p / scale); fp32 accumulation)
+ *   out[t, :] = bf16( sum_{j=0..k-1} w[t,j] * y_{t,j} ), summed in ascending j
+ *   in fp32: a fixed order, no floating-point atomics, so results are
+ *   reproducible bit for bit.
+ *
+ * act, act_amax from moe_stage1; w2, s2 from moe_preshuffle; topk_w fp32 [T,k]
+ * out bf16 [T,H] (out); workspace [moe_stage2_workspace_bytes()] bytes (device,
+ * 256-byte aligned): per-slot weighted partials and, for FP8, the requantised
+ * intermediate.
+ */
+int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int I, int block_m);
+moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, const void* w2,
+                      const float* s2, const int32_t* sorted_slot, const int32_t* tile_expert,
+                      const int32_t* total_padded, const float* topk_w, int T, int k, int E,
+                      int H, int I, int block_m, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,281 @@
+// C ABI of libmoe: argument checks (before any HIP call) and kernel launches.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/moe.h"
+#include "moe_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define CHECK(cond, code, ...)                  \
+  do {                                          \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+int64_t capacity(int T, int k, int E, int bm) {
+  int64_t n = (int64_t)T * k + (int64_t)E * (bm - 1);
+  return (n + bm - 1) / bm * bm;
+}
+
+// Checks shared by the two GEMM stages.
+moe_status check_stage(int dt, int T, int k, int E, int H, int I, int bm) {
+  CHECK(dt == MOE_BF16 || dt == MOE_FP8_E4M3FN, MOE_ERR_INVALID_ARG, "dtype %d", dt);
+  CHECK(T >= 0 && k >= 1 && E >= 1 && H > 0 && I > 0, MOE_ERR_INVALID_ARG,
+        "sizes T=%d k=%d E=%d H=%d I=%d", T, k, E, H, I);
+  CHECK(k <= E && k <= 8 && E <= 64, MOE_ERR_UNSUPPORTED, "k=%d E=%d (need k<=min(E,8), E<=64)", k,
+        E);
+  CHECK(valid_bm(bm), MOE_ERR_UNSUPPORTED, "block_m=%d (need 16, 32, 64 or 128)", bm);
+  const int q = dt == MOE_BF16 ? 128 : 256;
+  CHECK(H % q == 0 && I % q == 0, MOE_ERR_UNSUPPORTED, "H=%d I=%d must be multiples of %d", H, I,
+        q);
+  CHECK((int64_t)T * k <= (1 << 30) && capacity(T, k, E, bm) <= (1 << 30), MOE_ERR_UNSUPPORTED,
+        "T*k too large");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_version(void) { return "moe-gfx950 0.1"; }
+
+moe_status moe_route(const void* x, const void* w_router, const float* bias, int T, int H, int E,
+                     int k, int32_t* topk_ids, float* topk_w, float* logits, void* x_q,
+                     float* x_scale, hipStream_t stream) {
+  CHECK(T >= 0 && H > 0, MOE_ERR_INVALID_ARG, "sizes T=%d H=%d", T, H);
+  CHECK(E >= 1 && k >= 1, MOE_ERR_INVALID_ARG, "E=%d k=%d", E, k);
+  CHECK(E <= 64 && k <= E && k <= 8, MOE_ERR_UNSUPPORTED, "E=%d k=%d (need E<=64, k<=min(E,8))",
+        E, k);
+  CHECK(H % 128 == 0, MOE_ERR_UNSUPPORTED, "H=%d must be a multiple of 128", H);
+  CHECK((int64_t)T * H <= ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "T*H too large");
+  if (T == 0) return ok();
+  CHECK(x && w_router && topk_ids && topk_w, MOE_ERR_INVALID_ARG, "null x/w_router/topk_ids/topk_w");
+  CHECK(!x_q || x_scale, MOE_ERR_INVALID_ARG, "x_q given without x_scale");
+  CHECK(aligned(x, 16) && aligned(w_router, 16) && aligned(x_q, 8), MOE_ERR_INVALID_ARG,
+        "x and w_router must be 16-byte aligned, x_q 8-byte aligned");
+  moe::RouteArgs a{(const uint16_t*)x, (const uint16_t*)w_router, bias, T, H, E, k, topk_ids,
+                   topk_w, logits, (uint8_t*)x_q, x_scale};
+  return hip_status(moe::launch_route(a, stream), "moe_route launch");
+}
+
+int64_t moe_align_capacity(int T, int k, int E, int block_m) {
+  if (T < 0 || k < 1 || E < 1 || !valid_bm(block_m)) return -1;
+  return capacity(T, k, E, block_m);
+}
+
+moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                     int32_t* sorted_slot, int32_t* tile_expert, int32_t* expert_count,
+                     int32_t* expert_offset, int32_t* total_padded, hipStream_t stream) {
+  CHECK(T >= 0 && k >= 1 && E >= 1, MOE_ERR_INVALID_ARG, "sizes T=%d k=%d E=%d", T, k, E);
+  CHECK(E <= 64, MOE_ERR_UNSUPPORTED, "E=%d (need E<=64)", E);
+  CHECK(valid_bm(block_m), MOE_ERR_UNSUPPORTED, "block_m=%d (need 16, 32, 64 or 128)", block_m);
+  CHECK((int64_t)T * k <= (1 << 30), MOE_ERR_UNSUPPORTED, "T*k too large");
+  if (T == 0) return ok();
+  CHECK(topk_ids && sorted_slot && tile_expert && expert_count && expert_offset && total_padded,
+        MOE_ERR_INVALID_ARG, "null pointer argument");
+  moe::AlignArgs a{topk_ids, T * k, E, block_m, sorted_slot, tile_expert,
+                   expert_count, expert_offset, total_padded};
+  return hip_status(moe::launch_align(a, stream), "moe_align launch");
+}
+
+int64_t moe_preshuffle_bytes(moe_dtype dt, int E, int H, int I, int which) {
+  if ((dt != MOE_BF16 && dt != MOE_FP8_E4M3FN) || E < 1 || H < 1 || I < 1) return -1;
+  const int64_t es = dt == MOE_BF16 ? 2 : 1;
+  if (which == 0) return 2 * (int64_t)E * I * H * es;
+  if (which == 1) return (int64_t)E * H * I * es;
+  return -1;
+}
+
+moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, const void* w3,
+                          const void* w2, const float* s1, const float* s3, const float* s2,
+                          void* w13_out, void* w2_out, float* s13_out, float* s2_out,
+                          hipStream_t stream) {
+  CHECK(dt == MOE_BF16 || dt == MOE_FP8_E4M3FN, MOE_ERR_INVALID_ARG, "dtype %d", (int)dt);
+  CHECK(E >= 1 && H > 0 && I > 0, MOE_ERR_INVALID_ARG, "sizes E=%d H=%d I=%d", E, H, I);
+  const int q = dt == MOE_BF16 ? 128 : 256;
+  CHECK(H % q == 0 && I % q == 0, MOE_ERR_UNSUPPORTED, "H=%d I=%d must be multiples of %d", H, I,
+        q);
+  CHECK(w1 && w3 && w2 && w13_out && w2_out, MOE_ERR_INVALID_ARG, "null weight pointer");
+  CHECK(aligned(w1, 16) && aligned(w3, 16) && aligned(w2, 16) && aligned(w13_out, 16) &&
+            aligned(w2_out, 16),
+        MOE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  const bool fp8 = dt == MOE_FP8_E4M3FN;
+  if (fp8)
+    CHECK(s1 && s3 && s2 && s13_out && s2_out, MOE_ERR_INVALID_ARG, "FP8 needs all scale pointers");
+  const int es = fp8 ? 1 : 2, KE = fp8 ? 128 : 32;
+  moe::PreshuffleArgs a13{(const uint8_t*)w1, (const uint8_t*)w3, (uint8_t*)w13_out, E, 2 * I, H,
+                          es, KE};
+  hipError_t err = moe::launch_preshuffle(a13, stream);
+  if (err != hipSuccess) return hip_status(err, "preshuffle W1/W3");
+  moe::PreshuffleArgs a2{(const uint8_t*)w2, nullptr, (uint8_t*)w2_out, E, H, I, es, KE};
+  err = moe::launch_preshuffle(a2, stream);
+  if (err != hipSuccess) return hip_status(err, "preshuffle W2");
+  if (fp8) {
+    const size_t row = (size_t)I * 4;
+    err = hipMemcpy2DAsync(s13_out, 2 * row, s1, row, row, E, hipMemcpyDeviceToDevice, stream);
+    if (err == hipSuccess)
+      err = hipMemcpy2DAsync((char*)s13_out + row, 2 * row, s3, row, row, E,
+                             hipMemcpyDeviceToDevice, stream);
+    if (err == hipSuccess)
+      err = hipMemcpyAsync(s2_out, s2, (size_t)E * H * 4, hipMemcpyDeviceToDevice, stream);
+    if (err != hipSuccess) return hip_status(err, "preshuffle scales");
+  }
+  return ok();
+}
+
+int64_t moe_stage1_amax_floats(moe_dtype dt, int T, int k, int E, int H, int I, int block_m) {
+  if (check_stage(dt, T, k, E, H, I, block_m) != MOE_OK) return -1;
+  if (dt != MOE_FP8_E4M3FN) return 0;
+  moe::GemmCfg c = moe::stage1_cfg(dt, T, k, E, H, I, block_m);
+  return capacity(T, k, E, block_m) * (2 * (int64_t)I / c.wg_n);
+}
+
+moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, const void* w13,
+                      const float* s13, const int32_t* sorted_slot, const int32_t* tile_expert,
+                      const int32_t* total_padded, int T, int k, int E, int H, int I, int block_m,
+                      void* act, float* act_amax, hipStream_t stream) {
+  moe_status s = check_stage(dt, T, k, E, H, I, block_m);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  const bool fp8 = dt == MOE_FP8_E4M3FN;
+  CHECK(x_or_xq && w13 && sorted_slot && tile_expert && total_padded && act, MOE_ERR_INVALID_ARG,
+        "null pointer argument");
+  CHECK(!fp8 || (x_scale && s13 && act_amax), MOE_ERR_INVALID_ARG,
+        "FP8 needs x_scale, s13 and act_amax");
+  CHECK(aligned(x_or_xq, 16) && aligned(w13, 16) && aligned(act, 16) && aligned(s13, 16),
+        MOE_ERR_INVALID_ARG, "x, w13, act and s13 must be 16-byte aligned");
+  moe::GemmCfg c = moe::stage1_cfg(dt, T, k, E, H, I, block_m);
+  const int64_t cap = capacity(T, k, E, block_m);
+  moe::GemmArgs a{};
+  a.X = (const uint8_t*)x_or_xq;
+  a.x_scale = x_scale;
+  a.W = (const uint8_t*)w13;
+  a.w_scale = s13;
+  a.sorted_slot = sorted_slot;
+  a.tile_expert = tile_expert;
+  a.total_padded = total_padded;
+  a.out = act;
+  a.amax_part = act_amax;
+  a.T = T;
+  a.k = k;
+  a.K = H;
+  a.N = 2 * I;
+  a.I = I;
+  a.cap = (int)cap;
+  a.n_mtiles = (int)(cap / block_m);
+  a.n_ntiles = 2 * I / c.wg_n;
+  return hip_status(moe::launch_gemm(dt, 1, c, a, stream), "moe_stage1 launch");
+}
+
+int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int I, int block_m) {
+  if (check_stage(dt, T, k, E, H, I, block_m) != MOE_OK) return -1;
+  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  int64_t bytes = up((int64_t)T * k * H * 4);  // weighted per-slot partials
+  if (dt == MOE_FP8_E4M3FN) {
+    const int64_t cap = capacity(T, k, E, block_m);
+    bytes += up(cap * I) + up(cap * 4);  // requantised intermediate + row scales
+  }
+  return bytes;
+}
+
+moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, const void* w2,
+                      const float* s2, const int32_t* sorted_slot, const int32_t* tile_expert,
+                      const int32_t* total_padded, const float* topk_w, int T, int k, int E, int H,
+                      int I, int block_m, void* out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  moe_status s = check_stage(dt, T, k, E, H, I, block_m);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  const bool fp8 = dt == MOE_FP8_E4M3FN;
+  CHECK(act && w2 && sorted_slot && tile_expert && total_padded && topk_w && out && workspace,
+        MOE_ERR_INVALID_ARG, "null pointer argument");
+  CHECK(!fp8 || (act_amax && s2), MOE_ERR_INVALID_ARG, "FP8 needs act_amax and s2");
+  CHECK(aligned(act, 16) && aligned(w2, 16) && aligned(out, 8) && aligned(workspace, 256) &&
+            aligned(s2, 16),
+        MOE_ERR_INVALID_ARG, "act/w2/s2 16-byte, out 8-byte, workspace 256-byte alignment");
+  const int64_t need = moe_stage2_workspace_bytes(dt, T, k, E, H, I, block_m);
+  CHECK((int64_t)workspace_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu bytes < %lld needed",
+        workspace_bytes, (long long)need);
+
+  const int64_t cap = capacity(T, k, E, block_m);
+  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  char* ws = (char*)workspace;
+  float* part = (float*)ws;
+  ws += up((int64_t)T * k * H * 4);
+  const void* x = act;
+  const float* xs = nullptr;
+  hipError_t err;
+  if (fp8) {
+    uint8_t* act_q = (uint8_t*)ws;
+    float* act_scale = (float*)(ws + up(cap * I));
+    moe::GemmCfg c1 = moe::stage1_cfg(dt, T, k, E, H, I, block_m);
+    moe::QuantArgs q{(const uint16_t*)act, act_amax, 2 * I / c1.wg_n, (int)cap, I, total_padded,
+                     act_q, act_scale};
+    err = moe::launch_quant_act(q, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_stage2 requantisation");
+    x = act_q;
+    xs = act_scale;
+  }
+  moe::GemmCfg c = moe::stage2_cfg(dt, T, k, E, H, I, block_m);
+  moe::GemmArgs a{};
+  a.X = (const uint8_t*)x;
+  a.x_scale = xs;
+  a.W = (const uint8_t*)w2;
+  a.w_scale = s2;
+  a.sorted_slot = sorted_slot;
+  a.tile_expert = tile_expert;
+  a.total_padded = total_padded;
+  a.topk_w = topk_w;
+  a.out = part;
+  a.T = T;
+  a.k = k;
+  a.K = I;
+  a.N = H;
+  a.I = I;
+  a.cap = (int)cap;
+  a.n_mtiles = (int)(cap / block_m);
+  a.n_ntiles = H / c.wg_n;
+  err = moe::launch_gemm(dt, 2, c, a, stream);
+  if (err != hipSuccess) return hip_status(err, "moe_stage2 GEMM launch");
+  moe::CombineArgs cb{part, T, k, H, (uint16_t*)out};
+  return hip_status(moe::launch_combine(cb, stream), "moe_stage2 combine launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteArgs {
+  const uint16_t* x;         // bf16 [T,H]
+  const uint16_t* w_router;  // bf16 [E,H]
+  const float* bias;         // [E] or null
+  int T, H, E, k;
+  int32_t* topk_ids;         // [T,k]
+  float* topk_w;             // [T,k]
+  float* logits;             // [T,E] or null
+  uint8_t* x_q;              // [T,H] or null
+  float* x_scale;            // [T]
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+struct AlignArgs {
+  const int32_t* ids;  // [S]
+  int S, E, bm;
+  int32_t* sorted_slot;
+  int32_t* tile_expert;
+  int32_t* count;
+  int32_t* offset;
+  int32_t* total;
+};
+hipError_t launch_align(const AlignArgs& a, hipStream_t st);
+
+// Byte relayout of one row-major [R, K] matrix per expert into fragment order.
+// For the gate/up pair (two sources) composite rows alternate 16-row blocks.
+struct PreshuffleArgs {
+  const uint8_t* src0;  // W1 or W2, [E][rows][K] elements
+  const uint8_t* src1;  // W3, or null for W2
+  uint8_t* dst;
+  int E, R, K;          // R: composite rows per expert (2I or H); K: reduction length
+  int es, KE;           // element size (bytes), elements per fragment column block
+};
+hipError_t launch_preshuffle(const PreshuffleArgs& a, hipStream_t st);
+
+// Kernel configuration of a grouped GEMM stage, chosen on the host from the
+// shapes; the same choice sizes the FP8 amax partials.
+struct GemmCfg {
+  int mt;      // 16-row token blocks per tile (block_m / 16)
+  int ni;      // 16-feature blocks per wave
+  int ksplit;  // waves splitting the reduction inside a workgroup
+  int wg_n;    // features per workgroup = (4 / ksplit) * ni * 16
+};
+GemmCfg stage1_cfg(int dt, int T, int k, int E, int H, int I, int bm);
+GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm);
+
+struct GemmArgs {
+  const uint8_t* X;        // stage 1: x / x_q [T][K] (rows gathered by token); stage 2: act / act_q [cap][K]
+  const float* x_scale;    // FP8: per-token (stage 1) or per-row (stage 2) activation scale
+  const uint8_t* W;        // preshuffled weights
+  const float* w_scale;    // FP8: s13 [E][2][I] (stage 1) or s2 [E][H] (stage 2)
+  const int32_t* sorted_slot;
+  const int32_t* tile_expert;
+  const int32_t* total_padded;
+  const float* topk_w;     // stage 2
+  void* out;               // stage 1: act bf16 [cap][I]; stage 2: part fp32 [T*k][H]
+  float* amax_part;        // stage 1 FP8: [N/wg_n][cap]
+  int T, k, K, N, I, cap;
+  int n_mtiles, n_ntiles;
+};
+hipError_t launch_gemm(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipStream_t st);
+
+// FP8 stage 2 prologue: per-row amax from the partials, scale, requantise.
+struct QuantArgs {
+  const uint16_t* act;     // bf16 [cap][I]
+  const float* amax_part;  // [nparts][cap]
+  int nparts, cap, I;
+  const int32_t* total_padded;
+  uint8_t* act_q;          // [cap][I]
+  float* act_scale;        // [cap]
+};
+hipError_t launch_quant_act(const QuantArgs& a, hipStream_t st);
+
+// out[t,:] = bf16(sum_j part[t*k+j,:]) in ascending j.
+struct CombineArgs {
+  const float* part;  // [T*k][H]
+  int T, k, H;
+  uint16_t* out;      // [T][H]
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,58 @@
+"""GPU parity of moe_align: every output bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routed_top_amd as moe
+import oracle
+from gpu_util import dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def ids_for(T, k, E, seed, skew=None):
+    rng = np.random.default_rng(seed)
+    if skew is None:
+        return np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32).reshape(T, k)
+    p = np.asarray(skew, float)
+    out = np.empty((T, k), np.int32)
+    for t in range(T):
+        out[t] = rng.choice(E, size=k, replace=False, p=p / p.sum())
+    return out
+
+
+def check(ids, E, bm):
+    T, k = ids.shape
+    say(f"align parity T={T} k={k} E={E} bm={bm}")
+    g = moe.align(dev(ids), E, bm)
+    torch.cuda.synchronize()
+    o = oracle.align(ids, E, bm)
+    n = int(host(g.total)[0])
+    assert n == o["total"]
+    assert np.array_equal(host(g.sorted_slot)[:n], o["sorted_slot"])
+    assert np.array_equal(host(g.tile_expert)[: n // bm], o["tile_expert"])
+    assert np.array_equal(host(g.count), o["count"])
+    assert np.array_equal(host(g.offset), o["offset"])
+
+
+@pytest.mark.parametrize("T,k,E,bm", [(32, 2, 8, 16), (1, 2, 8, 16), (16, 2, 8, 16),
+                                      (8192, 2, 8, 128), (16384, 2, 8, 128), (257, 3, 64, 64),
+                                      (1000, 1, 4, 32), (2049, 8, 8, 16), (64, 2, 8, 128)])
+def test_align_uniform(T, k, E, bm):
+    check(ids_for(T, k, E, T + bm), E, bm)
+
+
+def test_align_skewed_and_degenerate():
+    check(ids_for(5000, 2, 8, 1, skew=[40, 10, 10, 10, 10, 10, 1, 1]), 8, 128)
+    one = np.zeros((300, 1), np.int32)  # every slot on expert 0
+    check(one, 8, 16)
+    last = np.full((33, 1), 7, np.int32)
+    check(last, 8, 32)
+
+
+def test_align_rejects_out_of_range_ids_on_device():
+    ids = np.zeros((10, 2), np.int32)
+    ids[3, 1] = 8
+    g = moe.align(dev(ids), 8, 16)
+    torch.cuda.synchronize()
+    assert int(host(g.total)[0]) == 0

@@ -1,0 +1,115 @@
+"""GPU parity of preshuffle, stage 1, stage 2 and the whole layer on small and
+ragged shapes (the oracle finishes in seconds), plus determinism."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routed_top_amd as moe
+import oracle
+import workloads
+from gpu_util import TOL, Uploaded, bf16_to_f64, dev, host, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def make(dtype, T, H, I, E, k, seed=0, bias=None, sigma_w=0.05):
+    wl = workloads.Workload(f"small-{dtype}", T, H, I, E, k, dtype, 1.0, 1.0 / np.sqrt(H),
+                            sigma_w, seed)
+    inp = workloads.generate(wl)
+    if bias is not None:
+        inp.bias = np.asarray(bias, np.float32)
+    return inp
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_preshuffle_bitexact(dtype):
+    inp = make(dtype, 4, 512, 768, 3, 2)
+    say(f"preshuffle {dtype}")
+    pw = moe.preshuffle(dtype, dev(inp.w1), dev(inp.w3), dev(inp.w2), dev(inp.s1), dev(inp.s3),
+                        dev(inp.s2))
+    torch.cuda.synchronize()
+    r13, r2 = oracle.preshuffle(dtype, inp.w1, inp.w3, inp.w2)
+    assert np.array_equal(host(pw.w13).view(np.uint8), r13)
+    assert np.array_equal(host(pw.w2).view(np.uint8), r2)
+    if dtype == "fp8":
+        s13 = host(pw.s13)
+        assert np.array_equal(s13[:, 0], inp.s1) and np.array_equal(s13[:, 1], inp.s3)
+        assert np.array_equal(host(pw.s2), inp.s2)
+
+
+def run_stages(inp, bm):
+    wl = inp.wl
+    fp8 = wl.dtype == "fp8"
+    x = dev(inp.x)
+    ids, w, xq, xs, _ = moe.route(x, dev(inp.w_router), wl.k, dev(inp.bias), fp8=fp8)
+    grp = moe.align(ids, wl.E, bm)
+    pw = moe.preshuffle(wl.dtype, dev(inp.w1), dev(inp.w3), dev(inp.w2), dev(inp.s1),
+                        dev(inp.s3), dev(inp.s2))
+    act, amax = moe.stage1(wl.dtype, xq if fp8 else x, xs, pw, grp)
+    out = moe.stage2(wl.dtype, act, amax, pw, grp, w)
+    torch.cuda.synchronize()
+    return dict(ids=host(ids), w=host(w), grp=grp, act=host(act), out=host(out))
+
+
+@pytest.mark.parametrize("dtype,T,H,I,E,k,bm", [
+    ("bf16", 32, 128, 256, 8, 2, 16),      # the tiny workload's shape
+    ("bf16", 33, 256, 384, 8, 2, 32),      # ragged T, several tiles
+    ("fp8", 40, 512, 768, 8, 2, 16),
+    ("fp8", 200, 256, 512, 8, 2, 64),
+    ("fp8", 300, 512, 512, 8, 2, 128),
+    ("fp8", 17, 256, 256, 4, 1, 16),       # k = 1
+    ("bf16", 9, 256, 256, 1, 1, 16),       # E = 1: a plain SwiGLU MLP
+])
+def test_stages_match_oracle(dtype, T, H, I, E, k, bm):
+    inp = make(dtype, T, H, I, E, k, seed=T)
+    say(f"stages {dtype} T={T} H={H} I={I} E={E} k={k} bm={bm}")
+    r = run_stages(inp, bm)
+    # stage 1: every real row against the oracle's SwiGLU intermediate (bf16 storage)
+    o = oracle.align(r["ids"], E, bm)
+    ss = o["sorted_slot"]
+    real = np.nonzero(ss < T * k)[0]
+    toks = (ss[real] // k).astype(np.int32)
+    exps = r["ids"].ravel()[ss[real]].astype(np.int32)
+    ref = oracle.swiglu(dtype, inp.x, inp.w1, inp.w3, inp.s1, inp.s3, toks, exps)
+    got = bf16_to_f64(r["act"][real])
+    e1 = np.abs(got - ref).max() / np.abs(ref).max()
+    pad = np.nonzero(ss >= T * k)[0]
+    assert np.all(r["act"][pad] == 0)
+    # whole layer
+    _, o64 = oracle.forward(inp)
+    e2 = rel_err(r["out"], o64)
+    say(f"  stage1 rel err {e1:.3e}  layer rel err {e2:.3e}")
+    assert e1 <= 1e-2
+    assert e2 <= TOL[dtype]
+
+
+def test_skew_everything_to_one_pair():
+    inp = make("fp8", 64, 256, 512, 8, 2, bias=[0, 0, 0, 0, 0, 50.0, 0, 60.0])
+    r = run_stages(inp, 16)
+    assert np.all(r["ids"] == [7, 5])
+    _, o64 = oracle.forward(inp)
+    assert rel_err(r["out"], o64) <= TOL["fp8"]
+
+
+def test_layer_is_deterministic_and_token_order_free():
+    inp = make("fp8", 96, 512, 512, 8, 2, seed=3)
+    up = Uploaded(inp, block_m=32)
+    a = up.run()
+    b = up.run()
+    assert np.array_equal(a, b)
+    perm = np.random.default_rng(0).permutation(inp.wl.T)
+    inp2 = make("fp8", 96, 512, 512, 8, 2, seed=3)
+    inp2.x = np.ascontiguousarray(inp.x[perm])
+    c = Uploaded(inp2, block_m=32).run()
+    assert np.array_equal(c, a[perm])
+
+
+def test_two_streams_same_result():
+    inp = make("bf16", 48, 256, 256, 8, 2, seed=5)
+    up = Uploaded(inp, block_m=16)
+    a = up.run()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = up.layer(up.x)
+    s.synchronize()
+    assert np.array_equal(host(out), a)
