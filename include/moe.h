@@ -85,7 +85,7 @@ const char* moe_version(void);
  * topk_ids int32 [T,k] (out)   topk_w   fp32 [T,k] (out)
  * logits   fp32 [T,E] (out) or NULL
  * x_q      uint8 [T,H] (out) or NULL; x_scale fp32 [T] (out), required iff x_q
- * Supported: H % 128 == 0, 1 <= E <= 64, 1 <= k <= min(E, 8).
+ * Supported: H % 128 == 0, H <= 8192, 1 <= E <= 64, 1 <= k <= min(E, 8).
  */
 moe_status moe_route(const void* x, const void* w_router, const float* bias, int T, int H,
                      int E, int k, int32_t* topk_ids, float* topk_w, float* logits, void* x_q,
@@ -109,7 +109,7 @@ moe_status moe_route(const void* x, const void* w_router, const float* bias, int
  * tile_expert int32 [capacity/block_m]; expert_count int32 [E];
  * expert_offset int32 [E+1]; total_padded int32 [1]. All device memory.
  * An id outside [0,E) makes total_padded 0 (nothing downstream runs).
- * Supported: block_m in {16, 32, 64, 128}, 1 <= E <= 64.
+ * Supported: block_m in {32, 64, 128, 256}, 1 <= E <= 64.
  */
 int64_t moe_align_capacity(int T, int k, int E, int block_m); /* ceil((T*k+E*(bm-1))/bm)*bm */
 moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
@@ -119,12 +119,14 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
 /*
  * moe_preshuffle - one-time, load-time relayout of the expert weights into the
  * order the matrix-core kernels read them in (talk summary 8:14). A pure byte
- * permutation: weights are cut into fragments of 16 output rows x KE reduction
- * columns (KE = 32 for bf16, 128 for e4m3fn, one matrix-core K step), stored
- * row-block major then K-block; inside a fragment lane l = 0..63 holds row
- * l mod 16 and the KE/4 consecutive columns starting at (l/16)*KE/4. Gate and
- * up rows are interleaved in blocks of 16 (W1 block, W3 block, ...), so one
- * wave holds the gate and up value of the same intermediate column.
+ * permutation: each expert's matrix (rows = output features, a row = the
+ * reduction) is cut into fragments of 32 rows x 64 bytes (64 e4m3fn or 32 bf16
+ * values, one 32x32 matrix-core step), stored row-block major then reduction
+ * block. A fragment is two 1 KB pieces; in piece pc the 16 bytes at l*16
+ * (lane l = 0..63) are row l mod 32, bytes (l/32)*32 + pc*16 .. +15 of the
+ * fragment's 64. Gate and up rows are interleaved in blocks of 32 (W1 block,
+ * W3 block, ...), so one wave holds the gate and up value of the same
+ * intermediate column.
  *
  * w1, w3   [E,I,H] row-major; w2 [E,H,I] row-major (bf16 or e4m3fn codes)
  * s1, s3   fp32 [E,I]; s2 fp32 [E,H] per-output-channel scales (FP8 only, else NULL)
@@ -146,12 +148,15 @@ moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, con
  *   W = code * scale), act[p, i] = bf16(silu(g_i) * u_i), silu(z) = z/(1+e^-z).
  * Pad rows (s == T*k) get act = 0.
  * FP8 also writes act_amax: per row p, partial maxima of |act[p,:]| over column
- * blocks, [moe_stage1_amax_floats()/capacity][capacity] floats; stage 2 reduces them.
+ * blocks, [capacity][moe_stage1_amax_floats()/capacity] floats (row-major);
+ * stage 2 reduces them.
  *
  * x_or_xq  bf16 [T,H] (BF16) or e4m3fn [T,H] (FP8, from moe_route)
  * x_scale  fp32 [T] (FP8) or NULL; w13, s13 from moe_preshuffle
  * sorted_slot, tile_expert, total_padded from moe_align with the same block_m
  * act      bf16 [capacity, I] (out); act_amax as above (FP8) or NULL
+ * Supported: block_m in {32, 64, 128, 256}; H, I multiples of 128 (bf16) or 256
+ * (FP8); H <= 8192 is not required here; activations below 2 GiB.
  */
 int64_t moe_stage1_amax_floats(moe_dtype dt, int T, int k, int E, int H, int I, int block_m);
 moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, const void* w13,

@@ -40,12 +40,13 @@ def _stream() -> int:
 
 
 def pick_block_m(T: int, k: int, E: int) -> int:
-    """M-tile for a batch: the smallest of 16/32/64/128 covering the mean expert group."""
+    """M-tile for a batch: the smallest of 32/64/128 covering the mean expert group,
+    256 for prefill-sized groups."""
     mean = T * k / max(E, 1)
-    for bm in (16, 32, 64):
+    for bm in (32, 64, 128):
         if mean <= bm:
             return bm
-    return 128
+    return 256
 
 
 def align_capacity(T: int, k: int, E: int, block_m: int) -> int:

@@ -34,7 +34,10 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
     if (!(cond)) return fail(code, __VA_ARGS__); \
   } while (0)
 
-bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+bool valid_bm(int bm) { return bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+
+// M-tiles per scheduling group: about 2048 rows, one expert's share at prefill.
+int group_m(int mt) { return 2048 / (32 * mt); }
 
 int64_t capacity(int T, int k, int E, int bm) {
   int64_t n = (int64_t)T * k + (int64_t)E * (bm - 1);
@@ -48,12 +51,20 @@ moe_status check_stage(int dt, int T, int k, int E, int H, int I, int bm) {
         "sizes T=%d k=%d E=%d H=%d I=%d", T, k, E, H, I);
   CHECK(k <= E && k <= 8 && E <= 64, MOE_ERR_UNSUPPORTED, "k=%d E=%d (need k<=min(E,8), E<=64)", k,
         E);
-  CHECK(valid_bm(bm), MOE_ERR_UNSUPPORTED, "block_m=%d (need 16, 32, 64 or 128)", bm);
+  CHECK(valid_bm(bm), MOE_ERR_UNSUPPORTED, "block_m=%d (need 32, 64, 128 or 256)", bm);
   const int q = dt == MOE_BF16 ? 128 : 256;
   CHECK(H % q == 0 && I % q == 0, MOE_ERR_UNSUPPORTED, "H=%d I=%d must be multiples of %d", H, I,
         q);
   CHECK((int64_t)T * k <= (1 << 30) && capacity(T, k, E, bm) <= (1 << 30), MOE_ERR_UNSUPPORTED,
         "T*k too large");
+  // Activation rows are addressed with 32-bit buffer offsets below 2 GiB.
+  const int64_t es = dt == MOE_BF16 ? 2 : 1;
+  CHECK((int64_t)T * H * es < ((int64_t)1 << 31) &&
+            capacity(T, k, E, bm) * I * es < ((int64_t)1 << 31),
+        MOE_ERR_UNSUPPORTED, "activations beyond 2 GiB (T=%d)", T);
+  CHECK(moe::gemm_cfg_ok(dt, 1, moe::stage1_cfg(dt, T, k, E, H, I, bm), 2 * I, H) &&
+            moe::gemm_cfg_ok(dt, 2, moe::stage2_cfg(dt, T, k, E, H, I, bm), H, I),
+        MOE_ERR_UNSUPPORTED, "no kernel configuration for H=%d I=%d block_m=%d", H, I, bm);
   return ok();
 }
 
@@ -83,7 +94,8 @@ moe_status moe_route(const void* x, const void* w_router, const float* bias, int
   CHECK(E >= 1 && k >= 1, MOE_ERR_INVALID_ARG, "E=%d k=%d", E, k);
   CHECK(E <= 64 && k <= E && k <= 8, MOE_ERR_UNSUPPORTED, "E=%d k=%d (need E<=64, k<=min(E,8))",
         E, k);
-  CHECK(H % 128 == 0, MOE_ERR_UNSUPPORTED, "H=%d must be a multiple of 128", H);
+  CHECK(H % 128 == 0 && H <= 8192, MOE_ERR_UNSUPPORTED,
+        "H=%d must be a multiple of 128, at most 8192", H);
   CHECK((int64_t)T * H <= ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "T*H too large");
   if (T == 0) return ok();
   CHECK(x && w_router && topk_ids && topk_w, MOE_ERR_INVALID_ARG, "null x/w_router/topk_ids/topk_w");
@@ -105,7 +117,7 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
                      int32_t* expert_offset, int32_t* total_padded, hipStream_t stream) {
   CHECK(T >= 0 && k >= 1 && E >= 1, MOE_ERR_INVALID_ARG, "sizes T=%d k=%d E=%d", T, k, E);
   CHECK(E <= 64, MOE_ERR_UNSUPPORTED, "E=%d (need E<=64)", E);
-  CHECK(valid_bm(block_m), MOE_ERR_UNSUPPORTED, "block_m=%d (need 16, 32, 64 or 128)", block_m);
+  CHECK(valid_bm(block_m), MOE_ERR_UNSUPPORTED, "block_m=%d (need 32, 64, 128 or 256)", block_m);
   CHECK((int64_t)T * k <= (1 << 30), MOE_ERR_UNSUPPORTED, "T*k too large");
   if (T == 0) return ok();
   CHECK(topk_ids && sorted_slot && tile_expert && expert_count && expert_offset && total_padded,
@@ -139,12 +151,12 @@ moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, con
   const bool fp8 = dt == MOE_FP8_E4M3FN;
   if (fp8)
     CHECK(s1 && s3 && s2 && s13_out && s2_out, MOE_ERR_INVALID_ARG, "FP8 needs all scale pointers");
-  const int es = fp8 ? 1 : 2, KE = fp8 ? 128 : 32;
-  moe::PreshuffleArgs a13{(const uint8_t*)w1, (const uint8_t*)w3, (uint8_t*)w13_out, E, 2 * I, H,
-                          es, KE};
+  const int64_t es = fp8 ? 1 : 2;
+  moe::PreshuffleArgs a13{(const uint8_t*)w1, (const uint8_t*)w3, (uint8_t*)w13_out, E, 2 * I,
+                          H * es};
   hipError_t err = moe::launch_preshuffle(a13, stream);
   if (err != hipSuccess) return hip_status(err, "preshuffle W1/W3");
-  moe::PreshuffleArgs a2{(const uint8_t*)w2, nullptr, (uint8_t*)w2_out, E, H, I, es, KE};
+  moe::PreshuffleArgs a2{(const uint8_t*)w2, nullptr, (uint8_t*)w2_out, E, H, I * es};
   err = moe::launch_preshuffle(a2, stream);
   if (err != hipSuccess) return hip_status(err, "preshuffle W2");
   if (fp8) {
@@ -195,19 +207,24 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, c
   a.amax_part = act_amax;
   a.T = T;
   a.k = k;
-  a.K = H;
   a.N = 2 * I;
   a.I = I;
   a.cap = (int)cap;
-  a.n_mtiles = (int)(cap / block_m);
+  a.bm = block_m;
+  a.K_bytes = H * (fp8 ? 1 : 2);
+  a.x_bytes = (int64_t)T * a.K_bytes;
+  a.n_mtiles = (int)(cap / (32 * c.mt));
   a.n_ntiles = 2 * I / c.wg_n;
+  a.kg = 1;
+  a.group_m = group_m(c.mt);
   return hip_status(moe::launch_gemm(dt, 1, c, a, stream), "moe_stage1 launch");
 }
 
 int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int I, int block_m) {
   if (check_stage(dt, T, k, E, H, I, block_m) != MOE_OK) return -1;
   auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
-  int64_t bytes = up((int64_t)T * k * H * 4);  // weighted per-slot partials
+  const moe::GemmCfg c = moe::stage2_cfg(dt, T, k, E, H, I, block_m);
+  int64_t bytes = up((int64_t)c.kg * T * k * H * 4);  // weighted per-slot partials per split
   if (dt == MOE_FP8_E4M3FN) {
     const int64_t cap = capacity(T, k, E, block_m);
     bytes += up(cap * I) + up(cap * 4);  // requantised intermediate + row scales
@@ -236,9 +253,10 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
 
   const int64_t cap = capacity(T, k, E, block_m);
   auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  moe::GemmCfg c = moe::stage2_cfg(dt, T, k, E, H, I, block_m);
   char* ws = (char*)workspace;
   float* part = (float*)ws;
-  ws += up((int64_t)T * k * H * 4);
+  ws += up((int64_t)c.kg * T * k * H * 4);
   const void* x = act;
   const float* xs = nullptr;
   hipError_t err;
@@ -253,7 +271,6 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
     x = act_q;
     xs = act_scale;
   }
-  moe::GemmCfg c = moe::stage2_cfg(dt, T, k, E, H, I, block_m);
   moe::GemmArgs a{};
   a.X = (const uint8_t*)x;
   a.x_scale = xs;
@@ -266,15 +283,19 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
   a.out = part;
   a.T = T;
   a.k = k;
-  a.K = I;
   a.N = H;
   a.I = I;
   a.cap = (int)cap;
-  a.n_mtiles = (int)(cap / block_m);
+  a.bm = block_m;
+  a.K_bytes = I * (fp8 ? 1 : 2);
+  a.x_bytes = cap * a.K_bytes;
+  a.n_mtiles = (int)(cap / (32 * c.mt));
   a.n_ntiles = H / c.wg_n;
+  a.kg = c.kg;
+  a.group_m = group_m(c.mt);
   err = moe::launch_gemm(dt, 2, c, a, stream);
   if (err != hipSuccess) return hip_status(err, "moe_stage2 GEMM launch");
-  moe::CombineArgs cb{part, T, k, H, (uint16_t*)out};
+  moe::CombineArgs cb{part, T, k, H, c.kg, (uint16_t*)out};
   return hip_status(moe::launch_combine(cb, stream), "moe_stage2 combine launch");
 }
 

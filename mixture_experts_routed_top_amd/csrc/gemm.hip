@@ -5,226 +5,308 @@
 // the routed MoE GEMM of the FlyDSL-in-JAX talk summary (5:56); the tiling
 // here is this library's own.
 //
-// Roles: the matrix-core A operand is a 16-row block of (preshuffled) expert
-// weights, the B operand a 16-token block of activations, so each lane's four
-// accumulators are four consecutive output features of one token:
-//   acc[feature 4*(lane/16) + r][token lane%16], r = 0..3.
-// A workgroup is 4 waves. Waves split the tile's features (and, for decode
-// shapes, the reduction); all waves share the token tile, which is staged
-// through LDS in 256-byte-per-row chunks (double buffered; the gather of
-// token rows happens in that load). Weight fragments go straight from HBM to
-// registers: the preshuffle made each wave's fragment one contiguous block.
+// Matrix-core roles. The A operand of v_mfma_f32_32x32x64_f8f6f4 (FP8) or of
+// two v_mfma_f32_32x32x16_bf16 (BF16) is a fragment of 32 expert-weight rows
+// (output features) by 64 reduction bytes; the B operand is the same shape cut
+// from 32 token rows. Lane l supplies row l%32 and the 32 reduction bytes
+// starting at (l/32)*32, held as two 16-byte pieces; accumulator register i of
+// lane l is then output feature 8*(i/4) + 4*(l/32) + i%4 of token l%32.
+//
+// Workgroup = 4 waves. Each wave owns two weight fragments along the features
+// (64 rows: for stage 1 one gate block and the matching up block, so the SwiGLU
+// pairs sit in the same lane) and all MT token fragments of the tile; KSPLIT
+// waves may split the reduction instead of the features (decode shapes), and a
+// launch may split the reduction over KG workgroups (stage 2 decode).
+// Weights stream from HBM straight into registers, NB-1 pipeline stages ahead
+// (the preshuffle made each piece of a fragment one contiguous 1 KB block);
+// tokens are gathered by row (sorted_slot) into registers one stage ahead and
+// written to LDS in fragment order, double buffered, so the matrix-core reads
+// are contiguous 16-byte-per-lane blocks with no bank conflicts.
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace moe {
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPiece = 1024;  // one fragment piece: 64 lanes x 16 B
+constexpr int kFrag = 2048;   // one fragment: 32 rows x 64 reduction bytes
+
 template <int DT>
-struct Frag;
+struct Mma;
 template <>
-struct Frag<0> {  // bf16, v_mfma_f32_16x16x32_bf16: 8 values (16 B) per lane
-  static constexpr int ES = 2, KE = 32, WV = 1;
-  static __device__ __forceinline__ f32x4 mma(const uint4* w, const uint4* x, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[0]),
-                                                   __builtin_bit_cast(bf16x8, x[0]), c, 0, 0, 0);
-  }
-};
-template <>
-struct Frag<1> {  // e4m3fn, v_mfma_f32_16x16x128_f8f6f4 (both formats fp8): 32 B per lane
-  static constexpr int ES = 1, KE = 128, WV = 2;
-  static __device__ __forceinline__ f32x4 mma(const uint4* w, const uint4* x, f32x4 c) {
+struct Mma<1> {  // e4m3fn x e4m3fn, 32x32x64, unscaled form
+  static __device__ __forceinline__ f32x16 run(const uint4 (&w)[2], const uint4 (&x)[2],
+                                               f32x16 c) {
     i32x8 a = {(int)w[0].x, (int)w[0].y, (int)w[0].z, (int)w[0].w,
                (int)w[1].x, (int)w[1].y, (int)w[1].z, (int)w[1].w};
     i32x8 b = {(int)x[0].x, (int)x[0].y, (int)x[0].z, (int)x[0].w,
                (int)x[1].x, (int)x[1].y, (int)x[1].z, (int)x[1].w};
-    // format codes 0/0 = e4m3 for A and B; scale operands 0 select the unscaled form.
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<0> {  // bf16: one 32x32x16 per piece
+  static __device__ __forceinline__ f32x16 run(const uint4 (&w)[2], const uint4 (&x)[2],
+                                               f32x16 c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[0]),
+                                                __builtin_bit_cast(bf16x8, x[0]), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[1]),
+                                                   __builtin_bit_cast(bf16x8, x[1]), c, 0, 0, 0);
   }
 };
 
-constexpr int kChunk = 256;           // bytes of reduction per row per LDS stage
-constexpr int kRowBytes = kChunk + 16;  // padded LDS row: conflict-free 16-B reads
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
-template <int DT, int MT, int KSPLIT>
+// Buffer offset of a pad row: past the end of any activation buffer (those are
+// limited to 2 GiB), so a raw buffer load from it returns zeros.
+constexpr uint32_t kPadOffset = 0x80000000u;
+
+// LDS slot swizzle of the token tile. The 16-byte column c (0..3) of a row's
+// 64-byte window goes to piece c&1, slot s = row + 32*(c>>1), stored at slot
+// s ^ lds_swz(c). The four columns of a row (written by four adjacent lanes)
+// then land in different bank groups, for both 8- and 16-lane LDS passes:
+// over 2 rows x 4 columns the slots differ mod 8, over 4 rows x 4 columns
+// mod 16. Readers apply the same permutation (it keeps bit 5 of the slot, so
+// it is a bijection inside each piece).
+__device__ __forceinline__ int lds_swz(int c) { return 4 * (c & 1) + 10 * (c >> 1); }
+
+template <int MT, int KSPLIT, int CK>
 constexpr int gemm_lds_bytes() {
-  return 2 * KSPLIT * 16 * MT * kRowBytes;
+  return 2 * KSPLIT * (CK / 64) * MT * kFrag;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-template <int DT, int STAGE, int MT, int NI, int KSPLIT>
+template <int DT, int STAGE, int MT, int KSPLIT, int NB, int CK>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
-  using F = Frag<DT>;
-  constexpr int ES = F::ES, KE = F::KE, WV = F::WV;
-  constexpr int KB = KE * ES;          // bytes per row per k-step (64 / 128)
-  constexpr int LB = KB / 4;           // bytes per lane per operand (16 / 32)
-  constexpr int KS = kChunk / KB;      // k-steps per chunk (4 / 2)
-  constexpr int CE = kChunk / ES;      // elements per chunk (128 / 256)
-  constexpr int BM = 16 * MT;
-  constexpr int WN = 4 / KSPLIT;       // waves along features
-  constexpr int WGN = WN * NI * 16;    // features per workgroup
-  constexpr int PIECES = KSPLIT * BM * 16;
-  constexpr int PPT = PIECES / 256;    // 16-byte activation pieces per thread per chunk
-  constexpr int LDS = gemm_lds_bytes<DT, MT, KSPLIT>();
-  static_assert(PIECES % 256 == 0, "tile too small for the staging layout");
-  static_assert(STAGE == 2 || (NI % 2 == 0 && KSPLIT == 1), "stage 1 pairs gate/up blocks");
-  static_assert(KSPLIT == 1 || (KSPLIT - 1) * WN * MT * NI * 4 * 64 * 4 <= LDS, "reduction space");
-  static_assert(STAGE == 2 || DT == 0 || WN * BM * 4 <= LDS, "amax space");
+  constexpr int kSub = CK / 64;          // fragments along the reduction per stage
+  constexpr int kChunk = CK;             // reduction bytes per pipeline stage
+  constexpr int WN = 4 / KSPLIT;         // waves along the features
+  constexpr int WGN = WN * 64;           // composite rows (features) per workgroup
+  constexpr int BMT = 32 * MT;           // token rows per tile
+  constexpr int PPT = KSPLIT * kSub * MT / 2;  // 16-byte token pieces per thread per stage
+  constexpr int LDS = gemm_lds_bytes<MT, KSPLIT, CK>();
+  static_assert(PPT >= 1 && KSPLIT * kSub * MT % 2 == 0, "staging layout");
+  constexpr int NACC = MT * 2 * 16;      // accumulator floats per lane
+  static_assert(KSPLIT == 1 || (KSPLIT - 1) * WN * NACC * 64 * 4 <= LDS, "reduction space");
+  static_assert(WN * BMT * 4 <= LDS, "amax space");
+  static_assert(NB >= 2 && NB <= 3, "weight pipeline depth");
 
   __shared__ __align__(16) uint8_t lds[LDS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wk = wave / WN;
 
-  const int ntiles = a.n_mtiles * a.n_ntiles;
-  const int logical = xcd_remap(blockIdx.x, ntiles);
-  const int mtile = logical % a.n_mtiles, ntile = logical / a.n_mtiles;
-  const int total = *a.total_padded;
-  const int row0 = mtile * BM;
-  if (row0 >= total) return;
-  const int e = a.tile_expert[mtile];
-  const int S = a.T * a.k;
-  const int Kw = a.K / KSPLIT;  // reduction elements per wave
-  const int nchunks = Kw / CE;
+  // Tile order: XCD-contiguous runs of logical tiles; inside a run, groups of
+  // gm M-tiles sweep the N-tiles so that co-resident workgroups of one XCD
+  // share weight slabs and token rows in its L2.
+  const int n_mn = a.n_mtiles * a.n_ntiles;
+  const int logical = xcd_remap(blockIdx.x, n_mn * a.kg);
+  const int kg = logical % a.kg;
+  const int mn = logical / a.kg;
+  const int per_group = a.group_m * a.n_ntiles;
+  const int grp = mn / per_group, rem = mn % per_group;
+  const int gm = min(a.group_m, a.n_mtiles - grp * a.group_m);
+  const int mtile = grp * a.group_m + rem % gm, ntile = rem / gm;
 
-  // Activation pieces this thread stages each chunk (row gather happens here).
-  const uint8_t* src[PPT];
+  const int total = *a.total_padded;
+  const int row0 = mtile * BMT;
+  if (row0 >= total) return;
+  const int e = a.tile_expert[row0 / a.bm];
+  const int S = a.T * a.k;
+  const int Kb = a.K_bytes;                    // reduction bytes of a full row
+  const int Kw = Kb / (KSPLIT * a.kg);         // reduction bytes per wave
+  const int nchunks = Kw / kChunk;
+  const int kbase = (kg * KSPLIT) * Kw;        // first reduction byte of this workgroup
+
+  // Token pieces this thread stages each stage. Piece q (thread tid, slot j):
+  // 16-byte column c = q%4 of the 64-byte window, row r = (q/4)%32 of fragment
+  // m = (q/128)%MT, reduction sub-block s = (q/(128*MT))%kSub, wave split ks.
+  // Rows are read through a raw buffer descriptor: a pad row gets an offset
+  // past the end of the buffer, which the hardware returns as zeros, so the
+  // load needs no branch.
+  const __amdgpu_buffer_rsrc_t xrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, (int)a.x_bytes, 0x00020000);
+  uint32_t xoff[PPT];
   int loff[PPT];
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
     const int q = tid + 256 * j;
-    const int ks = q / (BM * 16), r = (q / 16) % BM, c16 = q % 16;
-    const int p = row0 + r;
-    const uint8_t* rowp;
+    const int c = q & 3, r = (q >> 2) & 31, m = (q >> 7) % MT;
+    const int s = (q / (128 * MT)) % kSub, ks = q / (128 * MT * kSub);
+    const int p = row0 + m * 32 + r;
+    uint32_t rowbase;
     if constexpr (STAGE == 1) {
       const int slot = a.sorted_slot[p];
-      rowp = slot < S ? a.X + (size_t)(slot / a.k) * a.K * ES : nullptr;
+      rowbase = slot < S ? (uint32_t)(slot / a.k) * (uint32_t)Kb : kPadOffset;
     } else {
-      rowp = a.X + (size_t)p * a.K * ES;
+      rowbase = (uint32_t)p * (uint32_t)Kb;
     }
-    src[j] = rowp ? rowp + (size_t)ks * Kw * ES + c16 * 16 : nullptr;
-    loff[j] = (ks * BM + r) * kRowBytes + c16 * 16;
+    xoff[j] = rowbase + (uint32_t)(kbase + ks * Kw + s * 64 + c * 16);
+    loff[j] = ((ks * kSub + s) * MT + m) * kFrag + (c & 1) * kPiece +
+              ((r + 32 * (c >> 1)) ^ lds_swz(c)) * 16;
   }
 
-  // This wave's weight fragments: feature blocks rb0 .. rb0+NI-1, K blocks of its split.
-  const size_t kblocks = (size_t)a.K / KE;
-  const int rb0 = (ntile * WGN + wn * NI * 16) / 16;
-  const uint8_t* wbase = a.W + (size_t)e * a.N * a.K * ES +
-                         ((size_t)rb0 * kblocks + (size_t)wk * (Kw / KE)) * 64 * LB + lane * LB;
+  // This wave's weight fragments: composite row blocks rb0, rb0+1; reduction
+  // blocks from this wave's split on.
+  const int64_t RB = a.N / 32, KB = Kb / 64;
+  const int rb0 = ntile * (WGN / 32) + wn * 2;
+  const uint8_t* wbase = a.W + (((int64_t)e * RB + rb0) * KB + (kbase + wk * Kw) / 64) * kFrag +
+                         lane * 16;
+  const int64_t wfrag_stride = KB * kFrag;  // next row block
 
-  f32x4 acc[MT][NI];
+  f32x16 acc[MT][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int n = 0; n < NI; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][f][i] = 0.0f;
 
-  uint4 xr[PPT];
-  uint4 wc[KS][NI][WV], wx[KS][NI][WV];
+  uint4 xr[2][PPT];             // token prefetch, by chunk parity
+  uint4 wbuf[NB][kSub][2][2];   // weight prefetch: [stage][sub-block][fragment][piece]
 
-  auto load_x = [&](int c) {
+  auto load_x = [&](int c, uint4 (&x)[PPT]) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j)
-      xr[j] = src[j] ? *reinterpret_cast<const uint4*>(src[j] + (size_t)c * kChunk)
-                     : make_uint4(0, 0, 0, 0);
+      x[j] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff[j] + (uint32_t)c * kChunk, 0, 0));
   };
-  auto store_x = [&](int buf) {
+  auto store_x = [&](int buf, const uint4 (&x)[PPT]) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j)
-      *reinterpret_cast<uint4*>(lds + buf * (LDS / 2) + loff[j]) = xr[j];
+      *reinterpret_cast<uint4*>(lds + buf * (LDS / 2) + loff[j]) = x[j];
   };
-  auto load_w = [&](int c, uint4 (&w)[KS][NI][WV]) {
+  auto load_w = [&](int c, uint4 (&w)[kSub][2][2]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int s = 0; s < kSub; ++s)
 #pragma unroll
-      for (int n = 0; n < NI; ++n)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int v = 0; v < WV; ++v)
-          w[ks][n][v] = *reinterpret_cast<const uint4*>(
-              wbase + ((size_t)n * kblocks + (size_t)c * KS + ks) * 64 * LB + v * 16);
+        for (int pc = 0; pc < 2; ++pc)
+          w[s][f][pc] = *reinterpret_cast<const uint4*>(
+              wbase + f * wfrag_stride + ((int64_t)c * kSub + s) * kFrag + pc * kPiece);
   };
-  auto compute = [&](int buf, uint4 (&w)[KS][NI][WV]) {
-    const uint8_t* xl = lds + buf * (LDS / 2) + wk * BM * kRowBytes;
+  // Matrix-core work of one stage; the token fragment for the next step is
+  // read from LDS before the current step's two MFMAs are issued.
+  const int rd0 = (lane ^ lds_swz(2 * (lane >> 5))) * 16;           // piece 0 slot of this lane
+  const int rd1 = kPiece + (lane ^ lds_swz(1 + 2 * (lane >> 5))) * 16;  // piece 1
+  auto compute = [&](int buf, const uint4 (&w)[kSub][2][2]) {
+    const uint8_t* xl = lds + buf * (LDS / 2) + wk * kSub * MT * kFrag;
+    constexpr int NSTEP = kSub * MT;
+    uint4 xf[2][2];
+    xf[0][0] = *reinterpret_cast<const uint4*>(xl + rd0);
+    xf[0][1] = *reinterpret_cast<const uint4*>(xl + rd1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        uint4 xf[WV];
-        const uint8_t* pp = xl + (m * 16 + (lane & 15)) * kRowBytes + ks * KB + (lane >> 4) * LB;
-#pragma unroll
-        for (int v = 0; v < WV; ++v) xf[v] = *reinterpret_cast<const uint4*>(pp + 16 * v);
-#pragma unroll
-        for (int n = 0; n < NI; ++n) acc[m][n] = F::mma(w[ks][n], xf, acc[m][n]);
+    for (int t = 0; t < NSTEP; ++t) {
+      if (t + 1 < NSTEP) {
+        const uint8_t* pp = xl + (t + 1) * kFrag;
+        xf[(t + 1) & 1][0] = *reinterpret_cast<const uint4*>(pp + rd0);
+        xf[(t + 1) & 1][1] = *reinterpret_cast<const uint4*>(pp + rd1);
       }
+      const int s = t / MT, m = t % MT;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) acc[m][f] = Mma<DT>::run(w[s][f], xf[t & 1], acc[m][f]);
+      __builtin_amdgcn_sched_barrier(0);  // keep "read next, multiply current" in this order
     }
   };
-
-  load_x(0);
-  load_w(0, wc);
-  store_x(0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      load_x(c + 1);
-      load_w(c + 1, wx);
-    }
-    compute(c & 1, wc);
-    if (more) store_x((c + 1) & 1);
+  // One pipeline stage for chunk c (u = c mod the unroll period): prefetch the
+  // tokens of chunk c+2 and the weights of chunk c+NB-1 (indices clamped at
+  // the last chunk, so the steady state has no branches and the load counters
+  // stay exact), multiply chunk c, publish the tokens of chunk c+1 (loaded one
+  // stage ago) in the other LDS buffer.
+  auto step = [&](int c, auto u_const) {
+    constexpr int u = decltype(u_const)::value;
+    const int last = nchunks - 1;
+    load_x(min(c + 2, last), xr[u & 1]);
+    load_w(min(c + NB - 1, last), wbuf[(u + NB - 1) % NB]);
+    __builtin_amdgcn_sched_barrier(0);  // prefetches are issued before the matrix work
+    compute(c & 1, wbuf[u % NB]);
+    store_x((c + 1) & 1, xr[(u + 1) & 1]);
     __syncthreads();
-    if (more) {
+  };
+
+  // Prologue: weights for stages 0..NB-2, tokens of chunk 0 in LDS, tokens of
+  // chunk 1 in registers.
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int n = 0; n < NI; ++n)
-#pragma unroll
-          for (int v = 0; v < WV; ++v) wc[ks][n][v] = wx[ks][n][v];
-    }
+  for (int u = 0; u < NB - 1; ++u) load_w(min(u, nchunks - 1), wbuf[u]);
+  load_x(0, xr[0]);
+  load_x(min(1, nchunks - 1), xr[1]);
+  store_x(0, xr[0]);
+  __syncthreads();
+
+  // Steady state, unrolled by the period P = lcm(2, NB) so that every buffer
+  // index is static; then at most P-1 guarded tail stages.
+  constexpr int P = NB % 2 ? 2 * NB : NB;
+  int c0 = 0;
+  for (; c0 + P <= nchunks; c0 += P) {
+    step(c0 + 0, IntC<0>{});
+    step(c0 + 1, IntC<1>{});
+    if constexpr (P > 2) step(c0 + 2, IntC<2>{});
+    if constexpr (P > 3) step(c0 + 3, IntC<3>{});
+    if constexpr (P > 4) step(c0 + 4, IntC<4>{});
+    if constexpr (P > 5) step(c0 + 5, IntC<5>{});
   }
+  if (c0 + 0 < nchunks) step(c0 + 0, IntC<0>{});
+  if (c0 + 1 < nchunks) step(c0 + 1, IntC<1>{});
+  if constexpr (P > 2)
+    if (c0 + 2 < nchunks) step(c0 + 2, IntC<2>{});
+  if constexpr (P > 3)
+    if (c0 + 3 < nchunks) step(c0 + 3, IntC<3>{});
+  if constexpr (P > 4)
+    if (c0 + 4 < nchunks) step(c0 + 4, IntC<4>{});
 
   if constexpr (KSPLIT > 1) {
-    // Fixed-order reduction of the reduction splits: wave 0's sum, + split 1, + split 2, ...
+    // Fixed-order reduction of the wave splits: split 0 + split 1 + split 2 + ...
     float* red = reinterpret_cast<float*>(lds);
-    constexpr int NV = MT * NI * 4;
     if (wk > 0) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int n = 0; n < NI; ++n)
+        for (int f = 0; f < 2; ++f)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            red[(((wk - 1) * WN + wn) * NV + (m * NI + n) * 4 + r) * 64 + lane] = acc[m][n][r];
+          for (int i = 0; i < 16; ++i)
+            red[(((wk - 1) * WN + wn) * NACC + (m * 2 + f) * 16 + i) * 64 + lane] = acc[m][f][i];
     }
     __syncthreads();
-    if (wk > 0) return;
+    if (wk == 0) {
 #pragma unroll
-    for (int s = 1; s < KSPLIT; ++s)
+      for (int sp = 1; sp < KSPLIT; ++sp)
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int n = 0; n < NI; ++n)
+          for (int f = 0; f < 2; ++f)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[m][n][r] += red[(((s - 1) * WN + wn) * NV + (m * NI + n) * 4 + r) * 64 + lane];
+            for (int i = 0; i < 16; ++i)
+              acc[m][f][i] += red[(((sp - 1) * WN + wn) * NACC + (m * 2 + f) * 16 + i) * 64 + lane];
+    }
+    __syncthreads();  // the amax step below reuses the same LDS
   }
 
-  const int tok = lane & 15, fq = (lane >> 4) * 4;
+  const int tok = lane & 31, fq = (lane >> 5) * 4;
   if constexpr (STAGE == 1) {
-    // SwiGLU epilogue: gate block 2j and up block 2j+1 hold the same act columns.
+    // SwiGLU epilogue: fragment 0 is gate block ib, fragment 1 the up block ib.
     uint16_t* act = reinterpret_cast<uint16_t*>(a.out);
+    const int ib = rb0 / 2;
     const float* sg = DT == 1 ? a.w_scale + (size_t)e * 2 * a.I : nullptr;
     float amax[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int p = row0 + m * 16 + tok;
+      amax[m] = 0.0f;
+      if (wk != 0) continue;
+      const int p = row0 + m * 32 + tok;
       float xs = 1.0f;
       if constexpr (DT == 1) {
         const int slot = a.sorted_slot[p];
         xs = slot < S ? a.x_scale[slot / a.k] : 0.0f;
       }
-      amax[m] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < NI / 2; ++j) {
-        const int i0 = (ntile * WGN + wn * NI * 16) / 2 + j * 16 + fq;
+      for (int g = 0; g < 4; ++g) {
+        const int i0 = ib * 32 + 8 * g + fq;
         float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
         if constexpr (DT == 1) {
           float4 g4 = *reinterpret_cast<const float4*>(sg + i0);
@@ -235,9 +317,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         uint32_t b[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float g = acc[m][2 * j][r] * gs[r];
-          const float u = acc[m][2 * j + 1][r] * us[r];
-          b[r] = f32_to_bf16_bits(silu(g) * u);
+          const float gv = acc[m][0][4 * g + r] * gs[r];
+          const float uv = acc[m][1][4 * g + r] * us[r];
+          b[r] = f32_to_bf16_bits(silu(gv) * uv);
           amax[m] = fmaxf(amax[m], fabsf(bf16_bits_to_f32(b[r])));
         }
         *reinterpret_cast<uint2*>(act + (size_t)p * a.I + i0) =
@@ -245,49 +327,50 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       }
     }
     if constexpr (DT == 1) {
-      // Partial row maxima of this workgroup's columns: lanes, then waves.
+      // Partial row maxima over this workgroup's columns: lane halves, then waves.
       float* wmax = reinterpret_cast<float*>(lds);
-      __syncthreads();  // LDS reuse after the main loop's last reads
+      if constexpr (KSPLIT == 1) __syncthreads();  // LDS reuse after the main loop's last reads
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        float v = amax[m];
-        v = fmaxf(v, __shfl_xor(v, 16, 64));
-        v = fmaxf(v, __shfl_xor(v, 32, 64));
-        if (lane < 16) wmax[wn * BM + m * 16 + lane] = v;
+        const float v = fmaxf(amax[m], __shfl_xor(amax[m], 32, 64));
+        if (wk == 0 && lane < 32) wmax[wn * BMT + m * 32 + lane] = v;
       }
       __syncthreads();
-      if (tid < BM) {
-        float v = wmax[tid];
+      for (int r = tid; r < BMT; r += 256) {
+        float v = wmax[r];
 #pragma unroll
-        for (int w = 1; w < WN; ++w) v = fmaxf(v, wmax[w * BM + tid]);
-        a.amax_part[(size_t)(row0 + tid) * a.n_ntiles + ntile] = v;
+        for (int w = 1; w < WN; ++w) v = fmaxf(v, wmax[w * BMT + r]);
+        a.amax_part[(size_t)(row0 + r) * a.n_ntiles + ntile] = v;
       }
     }
   } else {
     // Down-projection epilogue: weighted per-slot partials, one writer per element.
-    float* part = reinterpret_cast<float*>(a.out);
+    if (wk != 0) return;
+    float* part = reinterpret_cast<float*>(a.out) + (size_t)kg * S * a.N;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int p = row0 + m * 16 + tok;
+      const int p = row0 + m * 32 + tok;
       const int slot = a.sorted_slot[p];
       if (slot >= S) continue;
       float sc = a.topk_w[slot];
       if constexpr (DT == 1) sc *= a.x_scale[p];
 #pragma unroll
-      for (int n = 0; n < NI; ++n) {
-        const int h0 = ntile * WGN + wn * NI * 16 + n * 16 + fq;
-        float ws[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (DT == 1) {
-          float4 w4 = *reinterpret_cast<const float4*>(a.w_scale + (size_t)e * a.N + h0);
-          ws[0] = w4.x; ws[1] = w4.y; ws[2] = w4.z; ws[3] = w4.w;
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int h0 = (rb0 + f) * 32 + 8 * g + fq;
+          float ws[4] = {1.f, 1.f, 1.f, 1.f};
+          if constexpr (DT == 1) {
+            float4 w4 = *reinterpret_cast<const float4*>(a.w_scale + (size_t)e * a.N + h0);
+            ws[0] = w4.x; ws[1] = w4.y; ws[2] = w4.z; ws[3] = w4.w;
+          }
+          float4 o;
+          o.x = acc[m][f][4 * g + 0] * ws[0] * sc;
+          o.y = acc[m][f][4 * g + 1] * ws[1] * sc;
+          o.z = acc[m][f][4 * g + 2] * ws[2] * sc;
+          o.w = acc[m][f][4 * g + 3] * ws[3] * sc;
+          *reinterpret_cast<float4*>(part + (size_t)slot * a.N + h0) = o;
         }
-        float4 o;
-        o.x = acc[m][n][0] * ws[0] * sc;
-        o.y = acc[m][n][1] * ws[1] * sc;
-        o.z = acc[m][n][2] * ws[2] * sc;
-        o.w = acc[m][n][3] * ws[3] * sc;
-        *reinterpret_cast<float4*>(part + (size_t)slot * a.N + h0) = o;
-      }
     }
   }
 }
@@ -325,18 +408,27 @@ __global__ __launch_bounds__(256) void quant_act_kernel(QuantArgs a) {
   }
 }
 
+// out[t,:] = bf16( sum_j sum_g part[g][t*k+j][:] ), j ascending, then split g ascending.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t n4 = (int64_t)a.T * a.H / 4;
+  const size_t split = (size_t)a.T * a.k * a.H;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i * 4 / a.H, h = i * 4 % a.H;
-    float4 s = *reinterpret_cast<const float4*>(a.part + ((size_t)t * a.k) * a.H + h);
-    for (int j = 1; j < a.k; ++j) {
-      float4 v = *reinterpret_cast<const float4*>(a.part + ((size_t)t * a.k + j) * a.H + h);
-      s.x = s.x + v.x;
-      s.y = s.y + v.y;
-      s.z = s.z + v.z;
-      s.w = s.w + v.w;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < a.k; ++j) {
+      for (int g = 0; g < a.kg; ++g) {
+        const float4 v = *reinterpret_cast<const float4*>(a.part + g * split +
+                                                          ((size_t)t * a.k + j) * a.H + h);
+        if (j == 0 && g == 0) {
+          s = v;
+        } else {
+          s.x = s.x + v.x;
+          s.y = s.y + v.y;
+          s.z = s.z + v.z;
+          s.w = s.w + v.w;
+        }
+      }
     }
     *reinterpret_cast<uint2*>(a.out + (size_t)t * a.H + h) =
         make_uint2(f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16),
@@ -345,71 +437,115 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Host side: configuration choice and dispatch.
+
+namespace {
+
+// Expected live row tiles of a grouping: every expert with slots needs
+// ceil(count/tile) tiles; bounded by the slots and by the experts.
+int64_t live_mtiles(int T, int k, int E, int tile_rows) {
+  const int64_t S = (int64_t)T * k;
+  int64_t by_slots = (S + tile_rows - 1) / tile_rows;
+  return by_slots + (S < E ? S : E);
+}
+
+// Pipeline shape of a (mt, ksplit) pair: stage bytes and weight stages.
+void set_pipeline(GemmCfg& c) {
+  if (c.ksplit == 1 && c.mt >= 4) {
+    c.ck = 64;   // 256- and 128-row tiles: short stages keep the registers in budget
+    c.nb = 3;
+  } else if (c.ksplit == 4) {
+    c.ck = 128;  // decode: deep weight prefetch, small accumulators
+    c.nb = 3;
+  } else {
+    c.ck = 128;
+    c.nb = 2;
+  }
+  c.wg_n = (4 / c.ksplit) * 64;
+}
+
+}  // namespace
 
 GemmCfg stage1_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
-  (void)dt; (void)T; (void)k; (void)E; (void)H; (void)I;
+  (void)T; (void)k; (void)E; (void)I;
   GemmCfg c;
-  c.mt = bm / 16;
-  c.ni = 4;
+  c.mt = (bm >= 256 ? 256 : bm) / 32;
   c.ksplit = 1;
-  c.wg_n = 4 * c.ni * 16;
+  c.kg = 1;
+  // Decode shapes (one 32-row fragment per tile): split the reduction over the
+  // waves so that a workgroup covers 64 features and the launch fills the chip.
+  if (c.mt == 1 && (H * (dt == 0 ? 2 : 1)) % (4 * 128) == 0) c.ksplit = 4;
+  set_pipeline(c);
   return c;
 }
 
 GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
-  (void)T; (void)k; (void)E;
-  const int ce = dt == 0 ? 128 : 256;
   GemmCfg c;
-  c.mt = bm / 16;
-  if (c.mt == 1 && (I / ce) % 4 == 0 && H % 64 == 0) {
-    c.ksplit = 4;
-    c.ni = 4;
-  } else {
-    c.ksplit = 1;
-    c.ni = H % 256 == 0 ? 4 : 2;
+  c.mt = (bm >= 256 ? 256 : bm) / 32;
+  c.ksplit = 1;
+  c.kg = 1;
+  const int kbytes = I * (dt == 0 ? 2 : 1);
+  if (H % 256 != 0) {
+    c.ksplit = 2;  // 128 features per workgroup
+    if (c.mt > 2) c.mt = 2;
   }
-  c.wg_n = (4 / c.ksplit) * c.ni * 16;
+  if (c.mt == 1 && kbytes % (4 * 128) == 0) {
+    c.ksplit = 4;
+    // Split the reduction over workgroups too until the launch has about
+    // 1024 live workgroups (each split g adds a partial, summed in order).
+    const int chunks = kbytes / (4 * 128);
+    const int64_t base = live_mtiles(T, k, E, 32) * (H / 64);
+    for (int cand = 2; cand <= 16; ++cand) {
+      if (chunks % cand) continue;
+      if (base * c.kg >= 1024) break;
+      c.kg = cand;
+    }
+  }
+  set_pipeline(c);
   return c;
 }
 
-template <int DT, int STAGE, int MT, int NI, int KSPLIT>
-static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
-  const int blocks = a.n_mtiles * a.n_ntiles;
-  hipLaunchKernelGGL((gemm_kernel<DT, STAGE, MT, NI, KSPLIT>), dim3(blocks), dim3(256), 0, st, a);
+bool gemm_cfg_ok(int dt, int stage, const GemmCfg& c, int N, int K) {
+  const int64_t kbytes = (int64_t)K * (dt == 0 ? 2 : 1);
+  if (c.mt != 1 && c.mt != 2 && c.mt != 4 && c.mt != 8) return false;
+  if (N % c.wg_n) return false;
+  if (kbytes % ((int64_t)c.ksplit * c.kg * c.ck)) return false;
+  if (stage == 1 && c.kg != 1) return false;
+  if (c.ksplit == 4) return c.mt == 1 && c.ck == 128 && c.nb == 3;
+  if (c.ksplit == 2) return c.mt <= 2 && c.ck == 128 && c.nb == 2;
+  if (c.ksplit == 1 && c.mt >= 4) return c.ck == 64 && c.nb == 3;
+  return c.ksplit == 1 && c.ck == 128 && c.nb == 2;
+}
+
+namespace {
+
+template <int DT, int STAGE, int MT, int KSPLIT, int NB, int CK>
+hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
+  const int64_t blocks = (int64_t)a.n_mtiles * a.n_ntiles * a.kg;
+  hipLaunchKernelGGL((gemm_kernel<DT, STAGE, MT, KSPLIT, NB, CK>), dim3((unsigned)blocks),
+                     dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <int DT, int STAGE>
-static hipError_t launch_dt_stage(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
-  if (STAGE == 1) {
-    switch (c.mt) {
-      case 1: return launch_one<DT, STAGE, 1, 4, 1>(a, st);
-      case 2: return launch_one<DT, STAGE, 2, 4, 1>(a, st);
-      case 4: return launch_one<DT, STAGE, 4, 4, 1>(a, st);
-      case 8: return launch_one<DT, STAGE, 8, 4, 1>(a, st);
-    }
-    return hipErrorInvalidValue;
-  }
-  if (c.ksplit == 4) return launch_one<DT, 2, 1, 4, 4>(a, st);
-  if (c.ni == 4) {
-    switch (c.mt) {
-      case 1: return launch_one<DT, 2, 1, 4, 1>(a, st);
-      case 2: return launch_one<DT, 2, 2, 4, 1>(a, st);
-      case 4: return launch_one<DT, 2, 4, 4, 1>(a, st);
-      case 8: return launch_one<DT, 2, 8, 4, 1>(a, st);
-    }
-  } else {
-    switch (c.mt) {
-      case 1: return launch_one<DT, 2, 1, 2, 1>(a, st);
-      case 2: return launch_one<DT, 2, 2, 2, 1>(a, st);
-      case 4: return launch_one<DT, 2, 4, 2, 1>(a, st);
-      case 8: return launch_one<DT, 2, 8, 2, 1>(a, st);
-    }
+hipError_t launch_dt_stage(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
+  if (c.ksplit == 4) return launch_one<DT, STAGE, 1, 4, 3, 128>(a, st);
+  if (c.ksplit == 2)
+    return c.mt == 1 ? launch_one<DT, STAGE, 1, 2, 2, 128>(a, st)
+                     : launch_one<DT, STAGE, 2, 2, 2, 128>(a, st);
+  switch (c.mt) {
+    case 1: return launch_one<DT, STAGE, 1, 1, 2, 128>(a, st);
+    case 2: return launch_one<DT, STAGE, 2, 1, 2, 128>(a, st);
+    case 4: return launch_one<DT, STAGE, 4, 1, 3, 64>(a, st);
+    case 8: return launch_one<DT, STAGE, 8, 1, 3, 64>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
+}  // namespace
+
 hipError_t launch_gemm(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
+  if (!gemm_cfg_ok(dt, stage, c, a.N, a.K_bytes / (dt == 0 ? 2 : 1))) return hipErrorInvalidValue;
   if (dt == 0) return stage == 1 ? launch_dt_stage<0, 1>(c, a, st) : launch_dt_stage<0, 2>(c, a, st);
   return stage == 1 ? launch_dt_stage<1, 1>(c, a, st) : launch_dt_stage<1, 2>(c, a, st);
 }

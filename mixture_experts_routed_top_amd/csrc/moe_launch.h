@@ -31,26 +31,30 @@ struct AlignArgs {
 hipError_t launch_align(const AlignArgs& a, hipStream_t st);
 
 // Byte relayout of one row-major [R, K] matrix per expert into fragment order.
-// For the gate/up pair (two sources) composite rows alternate 16-row blocks.
+// For the gate/up pair (two sources) composite rows alternate 32-row blocks.
 struct PreshuffleArgs {
   const uint8_t* src0;  // W1 or W2, [E][rows][K] elements
   const uint8_t* src1;  // W3, or null for W2
   uint8_t* dst;
-  int E, R, K;          // R: composite rows per expert (2I or H); K: reduction length
-  int es, KE;           // element size (bytes), elements per fragment column block
+  int E, R;             // R: composite rows per expert (2I or H)
+  int64_t K_bytes;      // reduction length in bytes (multiple of 64)
 };
 hipError_t launch_preshuffle(const PreshuffleArgs& a, hipStream_t st);
 
 // Kernel configuration of a grouped GEMM stage, chosen on the host from the
 // shapes; the same choice sizes the FP8 amax partials.
 struct GemmCfg {
-  int mt;      // 16-row token blocks per tile (block_m / 16)
-  int ni;      // 16-feature blocks per wave
-  int ksplit;  // waves splitting the reduction inside a workgroup
-  int wg_n;    // features per workgroup = (4 / ksplit) * ni * 16
+  int mt;      // 32-row token fragments per tile (tile rows = 32 * mt, dividing block_m)
+  int ksplit;  // waves splitting the reduction inside a workgroup (1 or 4)
+  int kg;      // workgroups splitting the reduction (stage 2 only; partials summed in order)
+  int nb;      // weight pipeline depth (register stages)
+  int ck;      // reduction bytes per pipeline stage (64 or 128)
+  int wg_n;    // features (composite rows) per workgroup = (4 / ksplit) * 64
 };
 GemmCfg stage1_cfg(int dt, int T, int k, int E, int H, int I, int bm);
 GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm);
+// Whether a configuration can run a stage with N output features and reduction length K.
+bool gemm_cfg_ok(int dt, int stage, const GemmCfg& c, int N, int K);
 
 struct GemmArgs {
   const uint8_t* X;        // stage 1: x / x_q [T][K] (rows gathered by token); stage 2: act / act_q [cap][K]
@@ -61,10 +65,13 @@ struct GemmArgs {
   const int32_t* tile_expert;
   const int32_t* total_padded;
   const float* topk_w;     // stage 2
-  void* out;               // stage 1: act bf16 [cap][I]; stage 2: part fp32 [T*k][H]
-  float* amax_part;        // stage 1 FP8: [N/wg_n][cap]
-  int T, k, K, N, I, cap;
-  int n_mtiles, n_ntiles;
+  void* out;               // stage 1: act bf16 [cap][I]; stage 2: part fp32 [kg][T*k][H]
+  float* amax_part;        // stage 1 FP8: [cap][N/wg_n]
+  int T, k, N, I, cap, bm;
+  int K_bytes;             // reduction bytes of one row (H or I times the element size)
+  int64_t x_bytes;         // size of X in bytes (< 2 GiB): loads past it read zeros
+  int n_mtiles, n_ntiles;  // row tiles (32*mt rows) and feature tiles (wg_n rows)
+  int kg, group_m;         // reduction split over workgroups; M-tiles per schedule group
 };
 hipError_t launch_gemm(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipStream_t st);
 
@@ -79,10 +86,10 @@ struct QuantArgs {
 };
 hipError_t launch_quant_act(const QuantArgs& a, hipStream_t st);
 
-// out[t,:] = bf16(sum_j part[t*k+j,:]) in ascending j.
+// out[t,:] = bf16(sum_j sum_g part[g][t*k+j,:]), j ascending, then g ascending.
 struct CombineArgs {
-  const float* part;  // [T*k][H]
-  int T, k, H;
+  const float* part;  // [kg][T*k][H]
+  int T, k, H, kg;
   uint16_t* out;      // [T][H]
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);

@@ -2,22 +2,30 @@
 // quantisation of x (the top-2 routing of the Mixtral layer in the FlyDSL-in-JAX
 // talk summary, 8:14).
 //
-// One wavefront per token. Lane l owns the 8-element chunks c = l, l+64, ...
-// of the row, which is exactly the partial-sum assignment of the layer's
-// fixed logit order (element h -> partial (h/8) mod 64), so each lane's
-// running sum is that partial; the 64 partials are folded with shuffles at
-// offsets 32..1. Chunks are 16-byte loads: one wave reads 1 KB contiguous.
+// Fixed logit order (part of the layer's contract, so that ids can be compared
+// bit for bit): element h goes to partial (h/8) mod 64; each partial adds its
+// products in ascending h; the 64 partials are folded with p[l] += p[l+off]
+// for off = 32..1. Lane l of a wave owns the 8-element chunks c = l, l+64, ...,
+// which is exactly partial l, so each lane's running sum is that partial and
+// the fold is a shuffle tree. A lane keeps its chunks of the token row in
+// registers (16-byte loads, at most kMaxChunks per lane: H <= 64*8*kMaxChunks).
+//
+// Two launch shapes:
+//  - small batches: one workgroup per token; its four waves split the experts
+//    (expert e on wave e%4) so that all loads of the token are in flight at
+//    once, then wave 0 selects the top-k and quantises the row;
+//  - large batches (E <= 16): one wave per token, W_r staged once per
+//    workgroup in LDS (batched 16-byte copies), several tokens per workgroup.
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace moe {
 
-// W_r staged in LDS when it fits (Mixtral: 8 x 4096 x 2 B = 64 KB).
-constexpr int kRouteLdsBytes = 64 * 1024;
+constexpr int kRouteLdsBytes = 64 * 1024;  // W_r staged in LDS when it fits
+constexpr int kMaxChunks = 16;             // 8-element chunks per lane (H <= 8192)
 
-__device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
-  uint4 q = *reinterpret_cast<const uint4*>(p);
-  uint32_t w[4] = {q.x, q.y, q.z, q.w};
+__device__ __forceinline__ void unpack8(uint4 q, float v[8]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
@@ -30,137 +38,240 @@ __device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
-template <int MAXE, bool LDS_W>
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-  extern __shared__ __align__(16) uint16_t wr_lds[];
-  const int lane = threadIdx.x & 63;
-  const int H = a.H, E = a.E, k = a.k;
-  const int nchunk = H / 8;
+// This lane's partial of one logit: its chunks in ascending order, products
+// added one by one (a bf16 x bf16 product is exact in fp32).
+template <int NCH>
+__device__ __forceinline__ float lane_partial(const uint4 (&xv)[NCH], const uint16_t* wrow,
+                                              int lane, int nchunk) {
+  uint4 wv[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+    if (lane + 64 * i < nchunk)
+      wv[i] = *reinterpret_cast<const uint4*>(wrow + (size_t)(lane + 64 * i) * 8);
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (lane + 64 * i < nchunk) {
+      float xf[8], wf[8];
+      unpack8(xv[i], xf);
+      unpack8(wv[i], wf);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s = s + xf[j] * wf[j];
+    }
+  }
+  return s;
+}
 
-  if constexpr (LDS_W) {
-    const int n16 = E * H / 8;  // 16-byte pieces of W_r
-    for (int i = threadIdx.x; i < n16; i += blockDim.x)
-      reinterpret_cast<uint4*>(wr_lds)[i] = reinterpret_cast<const uint4*>(a.w_router)[i];
+__device__ __forceinline__ float fold64(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_down(v, off, 64);
+  return __shfl(v, 0, 64);
+}
+
+// Top-k over the logits held by lanes e < E (lane e holds logit e), weights,
+// outputs (lane 0 writes).
+__device__ __forceinline__ void select_topk(const RouteArgs& a, int t, int lane, float mine) {
+  const int E = a.E, k = a.k;
+  if (a.logits && lane < E) a.logits[(size_t)t * E + lane] = mine;
+  bool taken = lane >= E;
+  float top_l[8];
+  int top_i[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    float bv = taken ? -__builtin_inff() : mine;
+    int bi = taken ? 1 << 20 : lane;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    top_l[j] = bv;
+    top_i[j] = bi;
+    if (lane == bi) taken = true;
+  }
+  if (lane == 0) {
+    float num[8], den = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) break;
+      num[j] = expf(top_l[j] - top_l[0]);
+      den += num[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) break;
+      a.topk_ids[(size_t)t * k + j] = top_i[j];
+      a.topk_w[(size_t)t * k + j] = num[j] / den;
+    }
+  }
+}
+
+// Per-token FP8 quantisation from the row chunks held in registers:
+// s = amax/448 (1 if zero), code = e4m3fn(clamp(x/s)), fp32 divide.
+template <int NCH>
+__device__ __forceinline__ void quantise_row(const RouteArgs& a, int t, int lane, int nchunk,
+                                             const uint4 (&xv)[NCH]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (lane + 64 * i < nchunk) {
+      float xf[8];
+      unpack8(xv[i], xf);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(xf[j]));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  if (lane == 0) a.x_scale[t] = s;
+  uint8_t* qr = a.x_q + (size_t)t * a.H;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nchunk) {
+      float xf[8];
+      unpack8(xv[i], xf);
+      const uint32_t lo = f32x4_to_e4m3(clamp448(xf[0] / s), clamp448(xf[1] / s),
+                                        clamp448(xf[2] / s), clamp448(xf[3] / s));
+      const uint32_t hi = f32x4_to_e4m3(clamp448(xf[4] / s), clamp448(xf[5] / s),
+                                        clamp448(xf[6] / s), clamp448(xf[7] / s));
+      *reinterpret_cast<uint2*>(qr + (size_t)c * 8) = make_uint2(lo, hi);
+    }
+  }
+}
+
+template <int NCH>
+__device__ __forceinline__ void load_row(const uint16_t* xr, int lane, int nchunk,
+                                         uint4 (&xv)[NCH]) {
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+    xv[i] = lane + 64 * i < nchunk
+                ? *reinterpret_cast<const uint4*>(xr + (size_t)(lane + 64 * i) * 8)
+                : make_uint4(0, 0, 0, 0);
+}
+
+// One workgroup per token; wave w computes the logits of experts w, w+4, ...
+template <int NCH>
+__global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
+  __shared__ float logit[64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nchunk = a.H / 8;
+  for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
+    uint4 xv[NCH];
+    load_row<NCH>(a.x + (size_t)t * a.H, lane, nchunk, xv);
+    for (int e = wave; e < a.E; e += 4) {
+      float l = fold64(lane_partial<NCH>(xv, a.w_router + (size_t)e * a.H, lane, nchunk));
+      if (a.bias) l = l + a.bias[e];
+      if (lane == 0) logit[e] = l;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      select_topk(a, t, lane, lane < a.E ? logit[lane] : -__builtin_inff());
+      if (a.x_q) quantise_row<NCH>(a, t, lane, nchunk, xv);
+    }
     __syncthreads();
   }
-  const uint16_t* wr = LDS_W ? wr_lds : a.w_router;
+}
 
+// One wave per token; W_r in LDS. All experts accumulate together (chunk by
+// chunk, each expert's sum still in ascending h), so the LDS reads and FMAs of
+// different experts overlap.
+template <int NCH, int MAXE>
+__global__ __launch_bounds__(256) void route_wave_kernel(RouteArgs a) {
+  extern __shared__ __align__(16) uint16_t wr_lds[];
+  const int lane = threadIdx.x & 63;
+  const int nchunk = a.H / 8;
+  {
+    // Stage W_r: 16 independent 16-byte loads per thread in flight per batch.
+    const int n16 = a.E * a.H / 8;
+    const uint4* src = reinterpret_cast<const uint4*>(a.w_router);
+    uint4* dst = reinterpret_cast<uint4*>(wr_lds);
+    for (int b = 0; b < n16; b += 256 * 16) {
+      uint4 tmp[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmp[i] = src[min(b + (int)threadIdx.x + 256 * i, n16 - 1)];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int idx = b + threadIdx.x + 256 * i;
+        if (idx < n16) dst[idx] = tmp[i];
+      }
+    }
+    __syncthreads();
+  }
   const int waves_total = gridDim.x * (blockDim.x / 64);
   for (int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); t < a.T; t += waves_total) {
-    const uint16_t* xr = a.x + (size_t)t * H;
+    uint4 xv[NCH];
+    load_row<NCH>(a.x + (size_t)t * a.H, lane, nchunk, xv);
     float acc[MAXE];
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) acc[e] = 0.0f;
-    float amax = 0.0f;
-
-    for (int c = lane; c < nchunk; c += 64) {
-      float xv[8];
-      load8(xr + c * 8, xv);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(xv[i]));
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunk) {
+        float xf[8];
+        unpack8(xv[i], xf);
 #pragma unroll
-      for (int e = 0; e < MAXE; ++e) {
-        if (e < E) {
-          float wv[8];
-          load8(wr + (size_t)e * H + c * 8, wv);
-          float s = acc[e];
+        for (int e = 0; e < MAXE; ++e) {
+          if (e < a.E) {
+            float wf[8];
+            unpack8(*reinterpret_cast<const uint4*>(wr_lds + (size_t)e * a.H + (size_t)c * 8), wf);
+            float s = acc[e];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) s = s + xv[i] * wv[i];  // product exact in fp32
-          acc[e] = s;
+            for (int j = 0; j < 8; ++j) s = s + xf[j] * wf[j];
+            acc[e] = s;
+          }
         }
       }
     }
-
-    // Fold the 64 partials: p[l] += p[l+off], off = 32..1; lane 0 ends with the logit.
     float mine = -__builtin_inff();
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) {
-      if (e < E) {
-        float v = acc[e];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_down(v, off, 64);
-        float l = __shfl(v, 0, 64);
+      if (e < a.E) {
+        float l = fold64(acc[e]);
         if (a.bias) l = l + a.bias[e];
         if (lane == e) mine = l;
       }
     }
-    if (a.logits && lane < E) a.logits[(size_t)t * E + lane] = mine;
-
-    // k rounds of a wave-wide argmax over the lanes e < E not yet taken.
-    bool taken = lane >= E;
-    float top_l[8];
-    int top_i[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= k) break;
-      float bv = taken ? -__builtin_inff() : mine;
-      int bi = taken ? 1 << 20 : lane;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        float ov = __shfl_xor(bv, off, 64);
-        int oi = __shfl_xor(bi, off, 64);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      top_l[j] = bv;
-      top_i[j] = bi;
-      if (lane == bi) taken = true;
-    }
-    if (lane == 0) {
-      float num[8], den = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= k) break;
-        num[j] = expf(top_l[j] - top_l[0]);
-        den += num[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= k) break;
-        a.topk_ids[(size_t)t * k + j] = top_i[j];
-        a.topk_w[(size_t)t * k + j] = num[j] / den;
-      }
-    }
-
-    if (a.x_q) {
-      // amax over the row (exact, order free), scale, then the fp32 divide.
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-      const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-      if (lane == 0) a.x_scale[t] = s;
-      uint8_t* qr = a.x_q + (size_t)t * H;
-      for (int c = lane; c < nchunk; c += 64) {
-        float xv[8];
-        load8(xr + c * 8, xv);
-        uint32_t lo = f32x4_to_e4m3(clamp448(xv[0] / s), clamp448(xv[1] / s),
-                                    clamp448(xv[2] / s), clamp448(xv[3] / s));
-        uint32_t hi = f32x4_to_e4m3(clamp448(xv[4] / s), clamp448(xv[5] / s),
-                                    clamp448(xv[6] / s), clamp448(xv[7] / s));
-        *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(lo, hi);
-      }
-    }
+    select_topk(a, t, lane, mine);
+    if (a.x_q) quantise_row<NCH>(a, t, lane, nchunk, xv);
   }
 }
 
-template <int MAXE>
-static hipError_t launch_route_e(const RouteArgs& a, hipStream_t st) {
+namespace {
+
+template <int NCH>
+hipError_t launch_nch(const RouteArgs& a, hipStream_t st) {
   const size_t wbytes = (size_t)a.E * a.H * 2;
-  const int blocks_needed = (a.T + 3) / 4;
-  if (wbytes <= (size_t)kRouteLdsBytes) {
-    // Enough tokens per workgroup to amortise staging W_r in LDS.
-    int blocks = blocks_needed < 1024 ? blocks_needed : 1024;
-    hipLaunchKernelGGL((route_kernel<MAXE, true>), dim3(blocks), dim3(256), wbytes, st, a);
+  if (a.T >= 1024 && a.E <= 16 && wbytes <= (size_t)kRouteLdsBytes) {
+    // W_r fits in LDS: about 4 tokens per wave, so staging it is amortised.
+    int blocks = (a.T + 15) / 16;
+    if (blocks > 2048) blocks = 2048;
+    if (a.E <= 8)
+      hipLaunchKernelGGL((route_wave_kernel<NCH, 8>), dim3(blocks), dim3(256), wbytes, st, a);
+    else
+      hipLaunchKernelGGL((route_wave_kernel<NCH, 16>), dim3(blocks), dim3(256), wbytes, st, a);
   } else {
-    int blocks = blocks_needed < 4096 ? blocks_needed : 4096;
-    hipLaunchKernelGGL((route_kernel<MAXE, false>), dim3(blocks), dim3(256), 0, st, a);
+    const int blocks = a.T < 4096 ? a.T : 4096;
+    hipLaunchKernelGGL((route_block_kernel<NCH>), dim3(blocks), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
 
+}  // namespace
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
-  if (a.E <= 8) return launch_route_e<8>(a, st);
-  if (a.E <= 16) return launch_route_e<16>(a, st);
-  if (a.E <= 32) return launch_route_e<32>(a, st);
-  return launch_route_e<64>(a, st);
+  const int nch = (a.H / 8 + 63) / 64;  // chunks per lane
+  if (nch <= 4) return launch_nch<4>(a, st);
+  if (nch <= 8) return launch_nch<8>(a, st);
+  if (nch <= kMaxChunks) return launch_nch<kMaxChunks>(a, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -418,59 +418,55 @@ void oracle_store_intermediate(int dtype, double* act, int n, int I)
 /* One-time weight preshuffle into MFMA operand order                        */
 
 /* The layout the GPU library stores expert weights in (load time only, not
- * arithmetic). A weight matrix with R rows (output features) and K columns
- * (the reduction) is cut into fragments of 16 rows x KE columns, KE = 32 for
- * bf16 and 128 for e4m3fn (one matrix-core K step). Fragments are stored
- * row-block major, then K-block; inside a fragment, lane l = 0..63 holds row
- * l mod 16 and the KE/4 consecutive columns starting at (l / 16) * KE/4,
- * lane after lane. For the gate/up pair the rows of one expert are taken in
- * blocks of 16 alternating W1, W3: composite row c is W1 row (c/32)*16 + c%16
- * when (c/16) is even, W3 row of the same index when it is odd. */
-/* Source row c of the composite gate/up matrix of one expert. */
-static const uint8_t* w13_row(const uint8_t* w1, const uint8_t* w3, size_t rowbytes, int c)
+ * arithmetic). A weight matrix with R rows (output features) and a reduction
+ * of K_bytes bytes per row is cut into fragments of 32 rows x 64 bytes (64
+ * e4m3fn or 32 bf16 values), stored row-block major, then reduction block.
+ * A fragment is two 1 KB pieces; in piece pc, the 16 bytes of lane l = 0..63
+ * (at l*16) are row l mod 32, bytes (l / 32)*32 + pc*16 .. +15 of the 64.
+ * For the gate/up pair, the rows of one expert are taken in blocks of 32
+ * alternating W1, W3: composite row c is W1 row (c/64)*32 + c%32 when (c/32)
+ * is even, W3 row of the same index when it is odd. */
+static void shuffle_matrix(const uint8_t* const* rows, int R, size_t K_bytes, uint8_t* out)
 {
-    int i = (c / 32) * 16 + c % 16;
-    return (((c / 16) % 2 == 0) ? w1 : w3) + (size_t)i * rowbytes;
+    size_t kblocks = K_bytes / 64;
+    for (int rb = 0; rb < R / 32; ++rb)
+        for (size_t kb = 0; kb < kblocks; ++kb)
+            for (int pc = 0; pc < 2; ++pc)
+                for (int l = 0; l < 64; ++l) {
+                    const uint8_t* src = rows[rb * 32 + l % 32] + kb * 64 + (size_t)(l / 32) * 32 +
+                                         (size_t)pc * 16;
+                    uint8_t* dst = out + (((size_t)rb * kblocks + kb) * 2 + pc) * 1024 + l * 16;
+                    memcpy(dst, src, 16);
+                }
 }
 
 void oracle_preshuffle_w13(int dtype, int E, int H, int I, const void* w1, const void* w3,
                            void* out)
 {
-    int es = dtype == ORACLE_BF16 ? 2 : 1, KE = dtype == ORACLE_BF16 ? 32 : 128;
-    int LB = KE / 4 * es, kblocks = H / KE;
-    size_t per = (size_t)I * H * es;
+    size_t es = dtype == ORACLE_BF16 ? 2 : 1;
+    size_t rowbytes = (size_t)H * es, per = (size_t)I * rowbytes;
+    const uint8_t** rows = (const uint8_t**)malloc(sizeof(uint8_t*) * 2 * (size_t)I);
     for (int e = 0; e < E; ++e) {
-        const uint8_t* a = (const uint8_t*)w1 + e * per;
-        const uint8_t* b = (const uint8_t*)w3 + e * per;
-        uint8_t* o = (uint8_t*)out + 2 * e * per;
-        for (int rb = 0; rb < 2 * I / 16; ++rb)
-            for (int kb = 0; kb < kblocks; ++kb)
-                for (int l = 0; l < 64; ++l) {
-                    int c = rb * 16 + l % 16;
-                    int k0 = kb * KE + (l / 16) * (KE / 4);
-                    const uint8_t* src = w13_row(a, b, (size_t)H * es, c) + (size_t)k0 * es;
-                    memcpy(o + (((size_t)rb * kblocks + kb) * 64 + l) * LB, src, (size_t)LB);
-                }
+        for (int c = 0; c < 2 * I; ++c) {
+            const uint8_t* base = (const uint8_t*)(((c / 32) % 2 == 0) ? w1 : w3) + e * per;
+            rows[c] = base + (size_t)((c / 64) * 32 + c % 32) * rowbytes;
+        }
+        shuffle_matrix(rows, 2 * I, rowbytes, (uint8_t*)out + 2 * e * per);
     }
+    free(rows);
 }
 
 void oracle_preshuffle_w2(int dtype, int E, int H, int I, const void* w2, void* out)
 {
-    int es = dtype == ORACLE_BF16 ? 2 : 1, KE = dtype == ORACLE_BF16 ? 32 : 128;
-    int LB = KE / 4 * es, kblocks = I / KE;
-    size_t per = (size_t)H * I * es;
+    size_t es = dtype == ORACLE_BF16 ? 2 : 1;
+    size_t rowbytes = (size_t)I * es, per = (size_t)H * rowbytes;
+    const uint8_t** rows = (const uint8_t**)malloc(sizeof(uint8_t*) * (size_t)H);
     for (int e = 0; e < E; ++e) {
-        const uint8_t* a = (const uint8_t*)w2 + e * per;
-        uint8_t* o = (uint8_t*)out + e * per;
-        for (int rb = 0; rb < H / 16; ++rb)
-            for (int kb = 0; kb < kblocks; ++kb)
-                for (int l = 0; l < 64; ++l) {
-                    int h = rb * 16 + l % 16;
-                    int k0 = kb * KE + (l / 16) * (KE / 4);
-                    const uint8_t* src = a + ((size_t)h * I + k0) * es;
-                    memcpy(o + (((size_t)rb * kblocks + kb) * 64 + l) * LB, src, (size_t)LB);
-                }
+        for (int h = 0; h < H; ++h)
+            rows[h] = (const uint8_t*)w2 + e * per + (size_t)h * rowbytes;
+        shuffle_matrix(rows, H, rowbytes, (uint8_t*)out + e * per);
     }
+    free(rows);
 }
 
 int oracle_threads(void)

@@ -43,16 +43,18 @@ def test_status_strings():
 
 def test_size_queries():
     L = _lib.lib()
-    assert L.moe_align_capacity(32, 2, 8, 16) == 64 + 8 * 15 + 8  # ceil(184/16)*16 = 192
+    assert L.moe_align_capacity(32, 2, 8, 32) == 320  # ceil((64 + 8*31)/32)*32
+    assert L.moe_align_capacity(32, 2, 8, 16) == -1   # block_m below one 32-row fragment
     assert L.moe_align_capacity(8192, 2, 8, 128) == (16384 + 8 * 127 + 127) // 128 * 128
+    assert L.moe_align_capacity(8192, 2, 8, 256) == (16384 + 8 * 255 + 255) // 256 * 256
     assert L.moe_align_capacity(1, 2, 8, 48) == -1
     assert L.moe_preshuffle_bytes(1, 8, 4096, 14336, 0) == 2 * 8 * 4096 * 14336
     assert L.moe_preshuffle_bytes(0, 8, 4096, 14336, 1) == 2 * 8 * 4096 * 14336
-    assert L.moe_stage1_amax_floats(0, 16, 2, 8, 4096, 14336, 16) == 0
+    assert L.moe_stage1_amax_floats(0, 16, 2, 8, 4096, 14336, 32) == 0
     cap = L.moe_align_capacity(8192, 2, 8, 128)
     assert L.moe_stage1_amax_floats(1, 8192, 2, 8, 4096, 14336, 128) == cap * (2 * 14336 // 256)
-    assert L.moe_stage2_workspace_bytes(0, 32, 2, 8, 128, 256, 16) == 64 * 128 * 4
-    assert L.moe_stage2_workspace_bytes(1, 3, 2, 8, 128, 256, 16) == -1  # FP8 needs H % 256
+    assert L.moe_stage2_workspace_bytes(0, 32, 2, 8, 128, 256, 64) == 64 * 128 * 4
+    assert L.moe_stage2_workspace_bytes(1, 3, 2, 8, 128, 256, 32) == -1  # FP8 needs H % 256
 
 
 def status(fn, *args):
@@ -81,7 +83,7 @@ def test_route_argument_checks():
 
 
 def test_align_argument_checks():
-    base = [FAKE, 16, 2, 8, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    base = [FAKE, 16, 2, 8, 32, FAKE, FAKE, FAKE, FAKE, FAKE, None]
     a = list(base); a[4] = 24
     assert status("moe_align", *a) == _lib.ERR_UNSUPPORTED
     assert b"block_m" in _lib.lib().moe_last_error()
@@ -106,20 +108,21 @@ def test_preshuffle_argument_checks():
 
 
 def stage2_args(ws_bytes, T=16):
-    return [1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, 2, 8, 4096, 14336, 16, FAKE,
+    return [1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, 2, 8, 4096, 14336, 32, FAKE,
             FAKE, ws_bytes, None]
 
 
 def test_stage_argument_checks():
-    s1 = [1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 8, 4096, 14336, 16, FAKE, FAKE, None]
-    a = list(s1); a[13] = 256
-    assert status("moe_stage1", *a) == _lib.ERR_UNSUPPORTED         # block_m
+    s1 = [1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 8, 4096, 14336, 32, FAKE, FAKE, None]
+    for bad_bm in (16, 48, 512):
+        a = list(s1); a[13] = bad_bm
+        assert status("moe_stage1", *a) == _lib.ERR_UNSUPPORTED     # block_m
     a = list(s1); a[15] = None
     assert status("moe_stage1", *a) == _lib.ERR_INVALID_ARG         # FP8 without act_amax
     a = list(s1); a[9] = 9
     assert status("moe_stage1", *a) == _lib.ERR_UNSUPPORTED         # k > 8
-    need = _lib.lib().moe_stage2_workspace_bytes(1, 16, 2, 8, 4096, 14336, 16)
-    assert need > 0
+    need = _lib.lib().moe_stage2_workspace_bytes(1, 16, 2, 8, 4096, 14336, 32)
+    assert need >= 16 * 2 * 4096 * 4
     assert status("moe_stage2", *stage2_args(need - 1)) == _lib.ERR_WORKSPACE
     a = stage2_args(need); a[16] = FAKE + 16
     assert status("moe_stage2", *a) == _lib.ERR_INVALID_ARG         # workspace alignment

@@ -35,17 +35,18 @@ def check(ids, E, bm):
     assert np.array_equal(host(g.offset), o["offset"])
 
 
-@pytest.mark.parametrize("T,k,E,bm", [(32, 2, 8, 16), (1, 2, 8, 16), (16, 2, 8, 16),
-                                      (8192, 2, 8, 128), (16384, 2, 8, 128), (257, 3, 64, 64),
-                                      (1000, 1, 4, 32), (2049, 8, 8, 16), (64, 2, 8, 128)])
+@pytest.mark.parametrize("T,k,E,bm", [(32, 2, 8, 32), (1, 2, 8, 32), (16, 2, 8, 32),
+                                      (8192, 2, 8, 128), (8192, 2, 8, 256), (16384, 2, 8, 256),
+                                      (257, 3, 64, 64), (1000, 1, 4, 32), (2049, 8, 8, 32),
+                                      (64, 2, 8, 128)])
 def test_align_uniform(T, k, E, bm):
     check(ids_for(T, k, E, T + bm), E, bm)
 
 
 def test_align_skewed_and_degenerate():
-    check(ids_for(5000, 2, 8, 1, skew=[40, 10, 10, 10, 10, 10, 1, 1]), 8, 128)
+    check(ids_for(5000, 2, 8, 1, skew=[40, 10, 10, 10, 10, 10, 1, 1]), 8, 256)
     one = np.zeros((300, 1), np.int32)  # every slot on expert 0
-    check(one, 8, 16)
+    check(one, 8, 32)
     last = np.full((33, 1), 7, np.int32)
     check(last, 8, 32)
 
@@ -53,6 +54,6 @@ def test_align_skewed_and_degenerate():
 def test_align_rejects_out_of_range_ids_on_device():
     ids = np.zeros((10, 2), np.int32)
     ids[3, 1] = 8
-    g = moe.align(dev(ids), 8, 16)
+    g = moe.align(dev(ids), 8, 32)
     torch.cuda.synchronize()
     assert int(host(g.total)[0]) == 0

@@ -52,13 +52,17 @@ def run_stages(inp, bm):
 
 
 @pytest.mark.parametrize("dtype,T,H,I,E,k,bm", [
-    ("bf16", 32, 128, 256, 8, 2, 16),      # the tiny workload's shape
+    ("bf16", 32, 128, 256, 8, 2, 32),      # the tiny workload's shape
     ("bf16", 33, 256, 384, 8, 2, 32),      # ragged T, several tiles
-    ("fp8", 40, 512, 768, 8, 2, 16),
+    ("bf16", 70, 128, 256, 8, 2, 64),      # H = 128: stage 2 on 128-feature workgroups
+    ("bf16", 300, 256, 512, 8, 2, 256),    # 256-row tiles in bf16
+    ("fp8", 40, 512, 768, 8, 2, 32),
     ("fp8", 200, 256, 512, 8, 2, 64),
     ("fp8", 300, 512, 512, 8, 2, 128),
-    ("fp8", 17, 256, 256, 4, 1, 16),       # k = 1
-    ("bf16", 9, 256, 256, 1, 1, 16),       # E = 1: a plain SwiGLU MLP
+    ("fp8", 700, 512, 768, 8, 2, 256),     # 256-row tiles, several per expert
+    ("fp8", 17, 256, 256, 4, 1, 32),       # k = 1
+    ("fp8", 5, 1024, 1024, 8, 2, 32),      # decode: reduction split over waves and workgroups
+    ("bf16", 9, 256, 256, 1, 1, 32),       # E = 1: a plain SwiGLU MLP
 ])
 def test_stages_match_oracle(dtype, T, H, I, E, k, bm):
     inp = make(dtype, T, H, I, E, k, seed=T)
@@ -85,7 +89,7 @@ def test_stages_match_oracle(dtype, T, H, I, E, k, bm):
 
 def test_skew_everything_to_one_pair():
     inp = make("fp8", 64, 256, 512, 8, 2, bias=[0, 0, 0, 0, 0, 50.0, 0, 60.0])
-    r = run_stages(inp, 16)
+    r = run_stages(inp, 32)
     assert np.all(r["ids"] == [7, 5])
     _, o64 = oracle.forward(inp)
     assert rel_err(r["out"], o64) <= TOL["fp8"]
@@ -106,7 +110,7 @@ def test_layer_is_deterministic_and_token_order_free():
 
 def test_two_streams_same_result():
     inp = make("bf16", 48, 256, 256, 8, 2, seed=5)
-    up = Uploaded(inp, block_m=16)
+    up = Uploaded(inp, block_m=32)
     a = up.run()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):

@@ -1,23 +1,25 @@
 """Pins of the oracle's preshuffle layout: it is a bijection, and it agrees with
-the same layout written as numpy reshapes/transposes (fragments of 16 rows x KE
-columns; inside a fragment lane l = 16*q + r holds row r and the q-th quarter
-of the KE columns)."""
+the same layout written as numpy reshapes/transposes (fragments of 32 rows x 64
+bytes; a fragment is two 1 KB pieces, and in piece pc lane l = 32*h + r holds
+row r, bytes 32*h + 16*pc .. +15)."""
 import numpy as np
 import pytest
 
 import oracle
 
 
-def numpy_layout(w, KE):
-    """[R, K] array of elements -> fragment order, via reshape/transpose."""
-    R, K = w.shape
-    a = w.reshape(R // 16, 16, K // KE, 4, KE // 4)   # rb, r, kb, q, c
-    a = a.transpose(0, 2, 3, 1, 4)                    # rb, kb, q, r, c  (lane = 16q + r)
+def numpy_layout(w):
+    """[R, K] array of elements -> fragment order, via reshape/transpose of its bytes."""
+    R = w.shape[0]
+    b = np.ascontiguousarray(w).view(np.uint8).reshape(R, -1)
+    Kb = b.shape[1]
+    a = b.reshape(R // 32, 32, Kb // 64, 2, 2, 16)    # rb, r, kb, h, pc, byte
+    a = a.transpose(0, 2, 4, 3, 1, 5)                 # rb, kb, pc, h, r, byte (lane = 32h + r)
     return np.ascontiguousarray(a).reshape(-1)
 
 
-@pytest.mark.parametrize("dtype,esize,KE", [("bf16", 2, 32), ("fp8", 1, 128)])
-def test_preshuffle_matches_numpy_layout(dtype, esize, KE):
+@pytest.mark.parametrize("dtype,esize", [("bf16", 2), ("fp8", 1)])
+def test_preshuffle_matches_numpy_layout(dtype, esize):
     E, H, I = 3, 256, 384
     rng = np.random.default_rng(2)
     edt = np.uint16 if esize == 2 else np.uint8
@@ -27,12 +29,12 @@ def test_preshuffle_matches_numpy_layout(dtype, esize, KE):
     p13, p2 = oracle.preshuffle(dtype, w1, w3, w2)
     ref13, ref2 = [], []
     for e in range(E):
-        # composite gate/up rows: blocks of 16 alternating W1, W3
-        comp = np.stack([w1[e].reshape(I // 16, 16, H), w3[e].reshape(I // 16, 16, H)], 1)
-        ref13.append(numpy_layout(comp.reshape(2 * I, H), KE))
-        ref2.append(numpy_layout(w2[e], KE))
-    assert np.array_equal(p13.view(edt), np.concatenate(ref13))
-    assert np.array_equal(p2.view(edt), np.concatenate(ref2))
+        # composite gate/up rows: blocks of 32 alternating W1, W3
+        comp = np.stack([w1[e].reshape(I // 32, 32, H), w3[e].reshape(I // 32, 32, H)], 1)
+        ref13.append(numpy_layout(comp.reshape(2 * I, H)))
+        ref2.append(numpy_layout(w2[e]))
+    assert np.array_equal(p13, np.concatenate(ref13))
+    assert np.array_equal(p2, np.concatenate(ref2))
 
 
 def test_preshuffle_is_a_bijection():
