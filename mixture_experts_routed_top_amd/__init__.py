@@ -40,13 +40,13 @@ def _stream() -> int:
 
 
 def pick_block_m(T: int, k: int, E: int) -> int:
-    """M-tile for a batch: the smallest of 32/64/128 covering the mean expert group,
-    256 for prefill-sized groups."""
+    """M-tile for a batch: the smallest of 32/64/128 covering the mean expert group
+    (the kernels' largest row tile is 128, so larger groups also use 128)."""
     mean = T * k / max(E, 1)
-    for bm in (32, 64, 128):
+    for bm in (32, 64):
         if mean <= bm:
             return bm
-    return 256
+    return 128
 
 
 def align_capacity(T: int, k: int, E: int, block_m: int) -> int:

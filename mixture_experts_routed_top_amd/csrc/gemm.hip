@@ -81,17 +81,18 @@ constexpr int gemm_lds_bytes() {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-template <int DT, int STAGE, int MT, int KSPLIT, int NB, int CK>
+template <int DT, int STAGE, int MT, int NF, int KSPLIT, int NB, int CK>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int kSub = CK / 64;          // fragments along the reduction per stage
   constexpr int kChunk = CK;             // reduction bytes per pipeline stage
   constexpr int WN = 4 / KSPLIT;         // waves along the features
-  constexpr int WGN = WN * 64;           // composite rows (features) per workgroup
+  constexpr int WGN = WN * NF * 32;      // composite rows (features) per workgroup
   constexpr int BMT = 32 * MT;           // token rows per tile
   constexpr int PPT = KSPLIT * kSub * MT / 2;  // 16-byte token pieces per thread per stage
   constexpr int LDS = gemm_lds_bytes<MT, KSPLIT, CK>();
   static_assert(PPT >= 1 && KSPLIT * kSub * MT % 2 == 0, "staging layout");
-  constexpr int NACC = MT * 2 * 16;      // accumulator floats per lane
+  constexpr int NACC = MT * NF * 16;     // accumulator floats per lane
+  static_assert(NF == 2 || NF == 4, "weight fragments per wave (gate/up pairs)");
   static_assert(KSPLIT == 1 || (KSPLIT - 1) * WN * NACC * 64 * 4 <= LDS, "reduction space");
   static_assert(WN * BMT * 4 <= LDS, "amax space");
   static_assert(NB >= 2 && NB <= 3, "weight pipeline depth");
@@ -151,24 +152,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
               ((r + 32 * (c >> 1)) ^ lds_swz(c)) * 16;
   }
 
-  // This wave's weight fragments: composite row blocks rb0, rb0+1; reduction
-  // blocks from this wave's split on.
+  // This wave's weight fragments: composite row blocks rb0 .. rb0+NF-1;
+  // reduction blocks from this wave's split on.
   const int64_t RB = a.N / 32, KB = Kb / 64;
-  const int rb0 = ntile * (WGN / 32) + wn * 2;
+  const int rb0 = ntile * (WGN / 32) + wn * NF;
   const uint8_t* wbase = a.W + (((int64_t)e * RB + rb0) * KB + (kbase + wk * Kw) / 64) * kFrag +
                          lane * 16;
   const int64_t wfrag_stride = KB * kFrag;  // next row block
 
-  f32x16 acc[MT][2];
+  f32x16 acc[MT][NF];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][f][i] = 0.0f;
 
   uint4 xr[2][PPT];             // token prefetch, by chunk parity
-  uint4 wbuf[NB][kSub][2][2];   // weight prefetch: [stage][sub-block][fragment][piece]
+  uint4 wbuf[NB][kSub][NF][2];  // weight prefetch: [stage][sub-block][fragment][piece]
 
   auto load_x = [&](int c, uint4 (&x)[PPT]) {
 #pragma unroll
@@ -181,11 +182,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     for (int j = 0; j < PPT; ++j)
       *reinterpret_cast<uint4*>(lds + buf * (LDS / 2) + loff[j]) = x[j];
   };
-  auto load_w = [&](int c, uint4 (&w)[kSub][2][2]) {
+  auto load_w = [&](int c, uint4 (&w)[kSub][NF][2]) {
 #pragma unroll
     for (int s = 0; s < kSub; ++s)
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int pc = 0; pc < 2; ++pc)
           w[s][f][pc] = *reinterpret_cast<const uint4*>(
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // read from LDS before the current step's two MFMAs are issued.
   const int rd0 = (lane ^ lds_swz(2 * (lane >> 5))) * 16;           // piece 0 slot of this lane
   const int rd1 = kPiece + (lane ^ lds_swz(1 + 2 * (lane >> 5))) * 16;  // piece 1
-  auto compute = [&](int buf, const uint4 (&w)[kSub][2][2]) {
+  auto compute = [&](int buf, const uint4 (&w)[kSub][NF][2]) {
     const uint8_t* xl = lds + buf * (LDS / 2) + wk * kSub * MT * kFrag;
     constexpr int NSTEP = kSub * MT;
     uint4 xf[2][2];
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       }
       const int s = t / MT, m = t % MT;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) acc[m][f] = Mma<DT>::run(w[s][f], xf[t & 1], acc[m][f]);
+      for (int f = 0; f < NF; ++f) acc[m][f] = Mma<DT>::run(w[s][f], xf[t & 1], acc[m][f]);
       __builtin_amdgcn_sched_barrier(0);  // keep "read next, multiply current" in this order
     }
   };
@@ -267,10 +268,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < NF; ++f)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            red[(((wk - 1) * WN + wn) * NACC + (m * 2 + f) * 16 + i) * 64 + lane] = acc[m][f][i];
+            red[(((wk - 1) * WN + wn) * NACC + (m * NF + f) * 16 + i) * 64 + lane] = acc[m][f][i];
     }
     __syncthreads();
     if (wk == 0) {
@@ -279,19 +280,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
+          for (int f = 0; f < NF; ++f)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              acc[m][f][i] += red[(((sp - 1) * WN + wn) * NACC + (m * 2 + f) * 16 + i) * 64 + lane];
+              acc[m][f][i] += red[(((sp - 1) * WN + wn) * NACC + (m * NF + f) * 16 + i) * 64 + lane];
     }
     __syncthreads();  // the amax step below reuses the same LDS
   }
 
   const int tok = lane & 31, fq = (lane >> 5) * 4;
   if constexpr (STAGE == 1) {
-    // SwiGLU epilogue: fragment 0 is gate block ib, fragment 1 the up block ib.
+    // SwiGLU epilogue: fragment 2q is gate block ib0+q, fragment 2q+1 the
+    // matching up block.
     uint16_t* act = reinterpret_cast<uint16_t*>(a.out);
-    const int ib = rb0 / 2;
+    const int ib0 = rb0 / 2;
     const float* sg = DT == 1 ? a.w_scale + (size_t)e * 2 * a.I : nullptr;
     float amax[MT];
 #pragma unroll
@@ -305,8 +307,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         xs = slot < S ? a.x_scale[slot / a.k] : 0.0f;
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int i0 = ib * 32 + 8 * g + fq;
+      for (int qg = 0; qg < NF / 2 * 4; ++qg) {
+        const int q = qg / 4, g = qg % 4;
+        const int i0 = (ib0 + q) * 32 + 8 * g + fq;
         float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
         if constexpr (DT == 1) {
           float4 g4 = *reinterpret_cast<const float4*>(sg + i0);
@@ -317,8 +320,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         uint32_t b[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float gv = acc[m][0][4 * g + r] * gs[r];
-          const float uv = acc[m][1][4 * g + r] * us[r];
+          const float gv = acc[m][2 * q][4 * g + r] * gs[r];
+          const float uv = acc[m][2 * q + 1][4 * g + r] * us[r];
           b[r] = f32_to_bf16_bits(silu(gv) * uv);
           amax[m] = fmaxf(amax[m], fabsf(bf16_bits_to_f32(b[r])));
         }
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       float sc = a.topk_w[slot];
       if constexpr (DT == 1) sc *= a.x_scale[p];
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int h0 = (rb0 + f) * 32 + 8 * g + fq;
@@ -449,10 +452,10 @@ int64_t live_mtiles(int T, int k, int E, int tile_rows) {
   return by_slots + (S < E ? S : E);
 }
 
-// Pipeline shape of a (mt, ksplit) pair: stage bytes and weight stages.
+// Pipeline shape of a (mt, nf, ksplit) triple: stage bytes and weight stages.
 void set_pipeline(GemmCfg& c) {
-  if (c.ksplit == 1 && c.mt >= 4) {
-    c.ck = 64;   // 256- and 128-row tiles: short stages keep the registers in budget
+  if (c.ksplit == 1 && c.mt * c.nf >= 16) {
+    c.ck = 64;   // prefill tiles: short stages keep the registers in budget
     c.nb = 3;
   } else if (c.ksplit == 4) {
     c.ck = 128;  // decode: deep weight prefetch, small accumulators
@@ -461,15 +464,16 @@ void set_pipeline(GemmCfg& c) {
     c.ck = 128;
     c.nb = 2;
   }
-  c.wg_n = (4 / c.ksplit) * 64;
+  c.wg_n = (4 / c.ksplit) * c.nf * 32;
 }
 
 }  // namespace
 
 GemmCfg stage1_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
-  (void)T; (void)k; (void)E; (void)I;
+  (void)T; (void)k; (void)E;
   GemmCfg c;
-  c.mt = (bm >= 256 ? 256 : bm) / 32;
+  c.mt = (bm >= 128 ? 128 : bm) / 32;
+  c.nf = c.mt == 4 && (2 * I) % 512 == 0 ? 4 : 2;  // prefill: 128 x 128 per wave
   c.ksplit = 1;
   c.kg = 1;
   // Decode shapes (one 32-row fragment per tile): split the reduction over the
@@ -481,12 +485,14 @@ GemmCfg stage1_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
 
 GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
   GemmCfg c;
-  c.mt = (bm >= 256 ? 256 : bm) / 32;
+  c.mt = (bm >= 128 ? 128 : bm) / 32;
+  c.nf = c.mt == 4 && H % 512 == 0 ? 4 : 2;
   c.ksplit = 1;
   c.kg = 1;
   const int kbytes = I * (dt == 0 ? 2 : 1);
   if (H % 256 != 0) {
     c.ksplit = 2;  // 128 features per workgroup
+    c.nf = 2;
     if (c.mt > 2) c.mt = 2;
   }
   if (c.mt == 1 && kbytes % (4 * 128) == 0) {
@@ -507,37 +513,38 @@ GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
 
 bool gemm_cfg_ok(int dt, int stage, const GemmCfg& c, int N, int K) {
   const int64_t kbytes = (int64_t)K * (dt == 0 ? 2 : 1);
-  if (c.mt != 1 && c.mt != 2 && c.mt != 4 && c.mt != 8) return false;
+  if (c.mt != 1 && c.mt != 2 && c.mt != 4) return false;
+  if (c.nf != 2 && !(c.nf == 4 && c.mt == 4 && c.ksplit == 1)) return false;
   if (N % c.wg_n) return false;
   if (kbytes % ((int64_t)c.ksplit * c.kg * c.ck)) return false;
   if (stage == 1 && c.kg != 1) return false;
   if (c.ksplit == 4) return c.mt == 1 && c.ck == 128 && c.nb == 3;
   if (c.ksplit == 2) return c.mt <= 2 && c.ck == 128 && c.nb == 2;
-  if (c.ksplit == 1 && c.mt >= 4) return c.ck == 64 && c.nb == 3;
+  if (c.ksplit == 1 && c.mt * c.nf >= 16) return c.ck == 64 && c.nb == 3;
   return c.ksplit == 1 && c.ck == 128 && c.nb == 2;
 }
 
 namespace {
 
-template <int DT, int STAGE, int MT, int KSPLIT, int NB, int CK>
+template <int DT, int STAGE, int MT, int NF, int KSPLIT, int NB, int CK>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int64_t blocks = (int64_t)a.n_mtiles * a.n_ntiles * a.kg;
-  hipLaunchKernelGGL((gemm_kernel<DT, STAGE, MT, KSPLIT, NB, CK>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((gemm_kernel<DT, STAGE, MT, NF, KSPLIT, NB, CK>), dim3((unsigned)blocks),
                      dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <int DT, int STAGE>
 hipError_t launch_dt_stage(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
-  if (c.ksplit == 4) return launch_one<DT, STAGE, 1, 4, 3, 128>(a, st);
+  if (c.ksplit == 4) return launch_one<DT, STAGE, 1, 2, 4, 3, 128>(a, st);
   if (c.ksplit == 2)
-    return c.mt == 1 ? launch_one<DT, STAGE, 1, 2, 2, 128>(a, st)
-                     : launch_one<DT, STAGE, 2, 2, 2, 128>(a, st);
+    return c.mt == 1 ? launch_one<DT, STAGE, 1, 2, 2, 2, 128>(a, st)
+                     : launch_one<DT, STAGE, 2, 2, 2, 2, 128>(a, st);
+  if (c.nf == 4) return launch_one<DT, STAGE, 4, 4, 1, 3, 64>(a, st);
   switch (c.mt) {
-    case 1: return launch_one<DT, STAGE, 1, 1, 2, 128>(a, st);
-    case 2: return launch_one<DT, STAGE, 2, 1, 2, 128>(a, st);
-    case 4: return launch_one<DT, STAGE, 4, 1, 3, 64>(a, st);
-    case 8: return launch_one<DT, STAGE, 8, 1, 3, 64>(a, st);
+    case 1: return launch_one<DT, STAGE, 1, 2, 1, 2, 128>(a, st);
+    case 2: return launch_one<DT, STAGE, 2, 2, 1, 2, 128>(a, st);
+    case 4: return launch_one<DT, STAGE, 4, 2, 1, 3, 64>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -45,11 +45,12 @@ hipError_t launch_preshuffle(const PreshuffleArgs& a, hipStream_t st);
 // shapes; the same choice sizes the FP8 amax partials.
 struct GemmCfg {
   int mt;      // 32-row token fragments per tile (tile rows = 32 * mt, dividing block_m)
+  int nf;      // 32-row weight fragments per wave (2 or 4: gate/up pairs in stage 1)
   int ksplit;  // waves splitting the reduction inside a workgroup (1 or 4)
   int kg;      // workgroups splitting the reduction (stage 2 only; partials summed in order)
   int nb;      // weight pipeline depth (register stages)
   int ck;      // reduction bytes per pipeline stage (64 or 128)
-  int wg_n;    // features (composite rows) per workgroup = (4 / ksplit) * 64
+  int wg_n;    // features (composite rows) per workgroup = (4 / ksplit) * nf * 32
 };
 GemmCfg stage1_cfg(int dt, int T, int k, int E, int H, int I, int bm);
 GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm);

@@ -52,7 +52,11 @@ def test_size_queries():
     assert L.moe_preshuffle_bytes(0, 8, 4096, 14336, 1) == 2 * 8 * 4096 * 14336
     assert L.moe_stage1_amax_floats(0, 16, 2, 8, 4096, 14336, 32) == 0
     cap = L.moe_align_capacity(8192, 2, 8, 128)
-    assert L.moe_stage1_amax_floats(1, 8192, 2, 8, 4096, 14336, 128) == cap * (2 * 14336 // 256)
+    # one partial maximum per row and per stage-1 workgroup column block (512 composite rows)
+    assert L.moe_stage1_amax_floats(1, 8192, 2, 8, 4096, 14336, 128) == cap * (2 * 14336 // 512)
+    # decode tiles (32 rows) use 64-row column blocks
+    cap32 = L.moe_align_capacity(16, 2, 8, 32)
+    assert L.moe_stage1_amax_floats(1, 16, 2, 8, 4096, 14336, 32) == cap32 * (2 * 14336 // 64)
     assert L.moe_stage2_workspace_bytes(0, 32, 2, 8, 128, 256, 64) == 64 * 128 * 4
     assert L.moe_stage2_workspace_bytes(1, 3, 2, 8, 128, 256, 32) == -1  # FP8 needs H % 256
 

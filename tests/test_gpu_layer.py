@@ -59,7 +59,9 @@ def run_stages(inp, bm):
     ("fp8", 40, 512, 768, 8, 2, 32),
     ("fp8", 200, 256, 512, 8, 2, 64),
     ("fp8", 300, 512, 512, 8, 2, 128),
-    ("fp8", 700, 512, 768, 8, 2, 256),     # 256-row tiles, several per expert
+    ("fp8", 700, 512, 768, 8, 2, 256),     # 128-row tiles, block_m 256, several per expert
+    ("fp8", 150, 768, 512, 8, 2, 128),     # H % 512 != 0: stage 2 on 2 fragments per wave
+    ("bf16", 200, 256, 384, 8, 2, 128),    # 2I % 512 != 0: stage 1 on 2 fragments per wave
     ("fp8", 17, 256, 256, 4, 1, 32),       # k = 1
     ("fp8", 5, 1024, 1024, 8, 2, 32),      # decode: reduction split over waves and workgroups
     ("bf16", 9, 256, 256, 1, 1, 32),       # E = 1: a plain SwiGLU MLP
