@@ -3,14 +3,28 @@
 One step = one whole layer call (route + FP8 token quantisation, align, stage 1,
 stage 2 with requantisation and combine) on the Mixtral 8x7B expert shape in
 FP8 e4m3fn at T=8192 tokens (H=4096, I=14336, E=8, top-2), inputs resident in
-HBM, weights preshuffled once before timing. Prints one JSON line.
+HBM, weights preshuffled once before timing. Prints one JSON line whose value
+is the effective TFLOP/s of the whole layer (6*H*I flops per token-slot).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload prefill|decode16]
-                    [--no-cpu-baseline] [--cpu-tokens 24]
+The same line carries:
+  roofline      stage-1 kernel (gather + gate/up GEMM + SwiGLU, the dominant
+                kernel) against the FP8 matrix-core peak, its launch time taken
+                with HIP events on the stream it runs on; traffic = HBM bytes
+                per launch from the committed counter summary (null if the
+                kernel source changed since);
+  decode_sweep  the FP8 decode batches T = 1, 4, 16, 64, 256: latency,
+                tokens/s, and weight-read bandwidth over the active experts'
+                weight bytes against 8 TB/s;
+  cpu_baseline  the CPU oracle on the first tokens of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-sweep]
+                    [--no-cpu-baseline] [--cpu-tokens 64] [--copy-calibration]
+    python bench.py --traffic-from FETCH.db WRITE.db   (writes the traffic summary)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -21,25 +35,44 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"fp8": 5000.0, "bf16": 2500.0}  # dense MFMA TFLOP/s, MI355X published
-HBM_PEAK = 8000.0                       # GB/s
+PEAK = {"fp8": 5000.0, "bf16": 2500.0}  # dense matrix-core TFLOP/s, MI355X published
+HBM_PEAK = 8000.0                       # GB/s, MI355X published
+TRAFFIC = os.path.join(ROOT, "profiles", "stage1_traffic.json")
+METRIC = "MoE layer effective TFLOP/s + tokens/s, Mixtral 8x7B shape, FP8, T=16..8192"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def pick_workload(name):
-    import workloads
-    if name == "prefill":
-        return workloads.config(2)
-    if name == "decode16":
-        return workloads.config(3, 16)
-    if name == "bf16-decode":
-        return workloads.config(1)
-    if name == "skewed":
-        return workloads.config(4)
-    raise SystemExit(f"unknown workload {name}")
+def kernel_sha() -> str:
+    """Hash of the HIP sources: a traffic figure is only valid for the code it was taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_routed_top_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def dev(a):
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def make_layer(inp, block_m=None):
+    import mixture_experts_routed_top_amd as moe
+    wl = inp.wl
+    w1, w3, w2 = dev(inp.w1), dev(inp.w3), dev(inp.w2)
+    layer = moe.Layer(wl.dtype, dev(inp.w_router), w1, w3, w2, dev(inp.s1), dev(inp.s3),
+                      dev(inp.s2), dev(inp.bias), wl.k, wl.T, block_m)
+    del w1, w3, w2  # only the preshuffled copies stay resident
+    return layer
 
 
 def cpu_baseline(inp, n_tokens):
@@ -51,11 +84,76 @@ def cpu_baseline(inp, n_tokens):
     oracle.forward(inp, toks)
     dt = time.perf_counter() - t0
     flops = 6.0 * wl.H * wl.I * wl.k * toks.size
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle",
             "sample": f"whole layer (route, quantise, {wl.k} experts, combine) for the first "
-                      f"{toks.size} tokens of {wl.name}: {dt:.1f} s wall, effective flops "
-                      f"6*H*I per token-slot"}
+                      f"{toks.size} of {wl.T} tokens of {wl.name}: {dt:.1f} s wall; effective "
+                      f"flops 6*H*I per token-slot"}
+
+
+def decode_sweep(steps):
+    """FP8 decode batches: per-T latency of the whole layer, tokens/s, weight GB/s."""
+    import torch
+    import workloads
+    base = workloads.generate(workloads.config(3, workloads.DECODE_SWEEP[0]), threads=16)
+    layer = make_layer(base)
+    torch.cuda.synchronize()
+    out = []
+    for T in workloads.DECODE_SWEEP:
+        wl = workloads.config(3, T)
+        x = dev(workloads.generate(wl, weights=False).x)
+        for _ in range(5):
+            layer(x)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            layer(x)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        active = int(torch.unique(layer.ids).numel())
+        wbytes = active * 3 * wl.H * wl.I  # e4m3fn weights of the experts that get a slot
+        gbps = wbytes / (ms * 1e-3) / 1e9
+        out.append({"T": T, "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                    "active_experts": active, "weight_gbps": round(gbps, 1),
+                    "frac_hbm": round(gbps / HBM_PEAK, 4),
+                    "tflops": round(wl.flops() / (ms * 1e-3) / 1e12, 2)})
+        log(f"[bench] decode T={T}: {ms * 1e3:.1f} us, {gbps:.0f} GB/s over {active} experts")
+    del layer
+    torch.cuda.empty_cache()
+    return out
+
+
+def traffic_from(fetch_db, write_db):
+    """Stage-1 HBM bytes per launch from two rocprofv3 --pmc databases (FETCH_SIZE,
+    WRITE_SIZE, in KiB per dispatch), each scaled by the same counter's reading for the
+    1 GiB device copy that --copy-calibration runs in the same program."""
+    import sqlite3
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, value from counters_collection "
+                           "where counter_name=?", (counter,)).fetchall()
+        s1 = [v for n, v in rows if "gemm_kernel<1, 1," in n]
+        copy = [v for n, v in rows if "copyBuffer" in n and v > 500000]
+        if not s1 or not copy:
+            raise SystemExit(f"{db}: no stage-1 or calibration-copy dispatch with {counter}")
+        return float(np.mean(s1)), float(max(copy))
+
+    f_s1, f_copy = per_kernel(fetch_db, "FETCH_SIZE")
+    w_s1, w_copy = per_kernel(write_db, "WRITE_SIZE")
+    kib = float(1 << 20)  # the calibration copy reads and writes 1 GiB = 2^20 KiB
+    f_scale, w_scale = kib / f_copy, kib / w_copy
+    rec = {"workload": "mixtral-fp8-prefill-T8192", "kernel": "stage 1 (gemm_kernel<1, 1, ...>)",
+           "kernel_source_sha": kernel_sha(),
+           "fetch_kib_raw": round(f_s1, 1), "write_kib_raw": round(w_s1, 1),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "bytes_per_launch": int((f_s1 * f_scale + w_s1 * w_scale) * 1024)}
+    with open(TRAFFIC, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def main():
@@ -63,38 +161,38 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=24)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this layer is built and timed on a single "
+        print(f"bench.py measures one GPU only: the layer is built and timed on a single "
               f"MI355X (got --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         raise SystemExit(2)
 
     import torch
     import workloads
-    import mixture_experts_routed_top_amd as moe
 
-    wl = pick_workload(args.workload)
+    wl = workloads.config(2)
     log(f"[bench] generating {wl.name}")
     inp = workloads.generate(wl, threads=16)
-    dev = lambda a: None if a is None else torch.from_numpy(
-        np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else np.ascontiguousarray(a)
-    ).to("cuda")
-    x, wr, bias = dev(inp.x), dev(inp.w_router), dev(inp.bias)
-    w1, w3, w2 = dev(inp.w1), dev(inp.w3), dev(inp.w2)
-    layer = moe.Layer(wl.dtype, wr, w1, w3, w2, dev(inp.s1), dev(inp.s3), dev(inp.s2), bias,
-                      wl.k, wl.T)
-    del w1, w3, w2
+    layer = make_layer(inp, args.block_m)
+    x = dev(inp.x)
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     log(f"[bench] block_m={layer.bm}; warmup {args.warmup}")
-
     for _ in range(args.warmup):
         layer(x)
     torch.cuda.synchronize()
 
+    # Timed region: K whole-layer steps; stage 1 bracketed by events on the same stream.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
@@ -109,21 +207,28 @@ def main():
     s1_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     log(f"[bench] {ms:.3f} ms/step, stage-1 kernel {s1_ms:.3f} ms")
 
-    flops = wl.flops()
-    tflops = flops / (ms * 1e-3) / 1e12
-    s1_flops = 4.0 * wl.H * wl.I * wl.slots  # gate + up GEMMs: 2 * 2*H*I per slot
+    tflops = wl.flops() / (ms * 1e-3) / 1e12
+    s1_flops = 4.0 * wl.H * wl.I * wl.slots  # gate + up GEMMs: 2 * 2*H*I per token-slot
     s1_tf = s1_flops / (s1_ms * 1e-3) / 1e12
     peak = PEAK[wl.dtype]
-    traffic_path = os.path.join(ROOT, "profiles", "stage1_traffic.json")
     traffic = None
-    if os.path.exists(traffic_path):
-        with open(traffic_path) as f:
+    if os.path.exists(TRAFFIC):
+        with open(TRAFFIC) as f:
             t = json.load(f)
-        if t.get("workload") == wl.name and t.get("kernel_source_sha") == _kernel_sha():
+        if t.get("workload") == wl.name and t.get("kernel_source_sha") == kernel_sha():
             traffic = t.get("bytes_per_launch")
 
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    del layer
+    torch.cuda.empty_cache()
+
     rec = {
-        "metric": "MoE layer effective TFLOP/s + tokens/s, Mixtral 8x7B shape, FP8, T=16..8192",
+        "metric": METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -134,29 +239,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3fn (fp32 accumulate, bf16 out)" if wl.dtype == "fp8" else "bf16",
+        "dtype": "fp8_e4m3fn",
         "data": "synthetic (seeded normals, Mixtral 8x7B expert shapes; no trained weights)",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
-                   "block_m": layer.bm, "frac_of_fp8_peak_whole_layer": round(tflops / peak, 4)},
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel stage 1 (gate/up + SwiGLU)",
+                   "block_m": args.block_m or __import__(
+                       "mixture_experts_routed_top_amd").pick_block_m(wl.T, wl.k, wl.E),
+                   "accumulate": "fp32", "output": "bf16",
+                   "frac_of_fp8_peak_whole_layer": round(tflops / peak, 4)},
+        "roofline": {"bound": "mfma", "kernel": "stage 1: gather + gate/up FP8 GEMM + SwiGLU",
                      "achieved": round(s1_tf, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(s1_tf / peak, 4), "traffic": traffic,
                      "avg_launch_ms": round(s1_ms, 4)},
     }
+    if not args.no_sweep:
+        rec["decode_sweep"] = decode_sweep(max(10, args.steps))
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
     print(json.dumps(rec), flush=True)
-
-
-def _kernel_sha():
-    import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "mixture_experts_routed_top_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

@@ -61,6 +61,15 @@ struct IntC {
   static constexpr int value = V;
 };
 
+// f(IntC<0>), ..., f(IntC<N-1>), unrolled at compile time.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 // Buffer offset of a pad row: past the end of any activation buffer (those are
 // limited to 2 GiB), so a raw buffer load from it returns zeros.
 constexpr uint32_t kPadOffset = 0x80000000u;
@@ -76,7 +85,7 @@ __device__ __forceinline__ int lds_swz(int c) { return 4 * (c & 1) + 10 * (c >> 
 
 template <int MT, int KSPLIT, int CK>
 constexpr int gemm_lds_bytes() {
-  return 2 * KSPLIT * (CK / 64) * MT * kFrag;
+  return 3 * KSPLIT * (CK / 64) * MT * kFrag;  // three token buffers
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
@@ -90,14 +99,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int BMT = 32 * MT;           // token rows per tile
   constexpr int PPT = KSPLIT * kSub * MT / 2;  // 16-byte token pieces per thread per stage
   constexpr int LDS = gemm_lds_bytes<MT, KSPLIT, CK>();
+  constexpr int BUF = LDS / 3;           // one token buffer
+  constexpr int NSTEP = kSub * MT;       // token fragments per wave per stage
+  static_assert(NSTEP % 2 == 0, "the stage barrier sits between two halves");
   static_assert(PPT >= 1 && KSPLIT * kSub * MT % 2 == 0, "staging layout");
   constexpr int NACC = MT * NF * 16;     // accumulator floats per lane
   static_assert(NF == 2 || NF == 4, "weight fragments per wave (gate/up pairs)");
   static_assert(KSPLIT == 1 || (KSPLIT - 1) * WN * NACC * 64 * 4 <= LDS, "reduction space");
   static_assert(WN * BMT * 4 <= LDS, "amax space");
-  static_assert(NB >= 2 && NB <= 3, "weight pipeline depth");
+  static_assert(NB == 3, "weight pipeline depth (the unroll period assumes 3)");
 
-  __shared__ __align__(16) uint8_t lds[LDS];
+  // Token buffers (reused by the epilogue), then the column scales of this
+  // workgroup's features (FP8), staged once so that the epilogue reads LDS.
+  constexpr int SCL = DT == 1 ? WGN : 0;
+  __shared__ __align__(16) uint8_t lds[LDS + SCL * 4];
+  float* const scl = reinterpret_cast<float*>(lds + LDS);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wk = wave / WN;
@@ -180,7 +196,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   auto store_x = [&](int buf, const uint4 (&x)[PPT]) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j)
-      *reinterpret_cast<uint4*>(lds + buf * (LDS / 2) + loff[j]) = x[j];
+      *reinterpret_cast<uint4*>(lds + buf * BUF + loff[j]) = x[j];
+  };
+  auto load_w1 = [&](int c, int s, int f, int pc, uint4& w) {
+    w = *reinterpret_cast<const uint4*>(wbase + f * wfrag_stride +
+                                        ((int64_t)c * kSub + s) * kFrag + pc * kPiece);
   };
   auto load_w = [&](int c, uint4 (&w)[kSub][NF][2]) {
 #pragma unroll
@@ -188,78 +208,131 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int pc = 0; pc < 2; ++pc)
-          w[s][f][pc] = *reinterpret_cast<const uint4*>(
-              wbase + f * wfrag_stride + ((int64_t)c * kSub + s) * kFrag + pc * kPiece);
+        for (int pc = 0; pc < 2; ++pc) load_w1(c, s, f, pc, w[s][f][pc]);
   };
-  // Matrix-core work of one stage; the token fragment for the next step is
-  // read from LDS before the current step's two MFMAs are issued.
   const int rd0 = (lane ^ lds_swz(2 * (lane >> 5))) * 16;           // piece 0 slot of this lane
   const int rd1 = kPiece + (lane ^ lds_swz(1 + 2 * (lane >> 5))) * 16;  // piece 1
-  auto compute = [&](int buf, const uint4 (&w)[kSub][NF][2]) {
-    const uint8_t* xl = lds + buf * (LDS / 2) + wk * kSub * MT * kFrag;
-    constexpr int NSTEP = kSub * MT;
-    uint4 xf[2][2];
-    xf[0][0] = *reinterpret_cast<const uint4*>(xl + rd0);
-    xf[0][1] = *reinterpret_cast<const uint4*>(xl + rd1);
-#pragma unroll
-    for (int t = 0; t < NSTEP; ++t) {
-      if (t + 1 < NSTEP) {
-        const uint8_t* pp = xl + (t + 1) * kFrag;
-        xf[(t + 1) & 1][0] = *reinterpret_cast<const uint4*>(pp + rd0);
-        xf[(t + 1) & 1][1] = *reinterpret_cast<const uint4*>(pp + rd1);
-      }
-      const int s = t / MT, m = t % MT;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) acc[m][f] = Mma<DT>::run(w[s][f], xf[t & 1], acc[m][f]);
-      __builtin_amdgcn_sched_barrier(0);  // keep "read next, multiply current" in this order
-    }
+  auto read_frag = [&](int buf, int t, uint4 (&x)[2]) {
+    const uint8_t* pp = lds + buf * BUF + (wk * NSTEP + t) * kFrag;
+    x[0] = *reinterpret_cast<const uint4*>(pp + rd0);
+    x[1] = *reinterpret_cast<const uint4*>(pp + rd1);
   };
-  // One pipeline stage for chunk c (u = c mod the unroll period): prefetch the
-  // tokens of chunk c+2 and the weights of chunk c+NB-1 (indices clamped at
-  // the last chunk, so the steady state has no branches and the load counters
-  // stay exact), multiply chunk c, publish the tokens of chunk c+1 (loaded one
-  // stage ago) in the other LDS buffer.
+
+  // One pipeline stage for chunk c (u = c mod the unroll period). Its token
+  // fragments sit in LDS buffer c%3, fragment 0 already in registers. In
+  // order: the MFMAs of each fragment, each preceded by the LDS read of the
+  // next one (the last step reads fragment 0 of chunk c+1 from buffer
+  // (c+1)%3); the global prefetches (tokens of chunk c+3, weights of chunk
+  // c+NB-1; indices clamped at the last chunk, so there are no branches and
+  // the load counters stay exact) spread one by one between the MFMAs; and,
+  // halfway, the workgroup barrier followed by the LDS write of the tokens of
+  // chunk c+2 into buffer (c+2)%3. The barrier sits behind queued MFMAs and
+  // orders: every wave's reads of buffer (c+2)%3 (chunk c-1) before its
+  // overwrite, and every wave's writes of buffer (c+1)%3 (made in stage c-1)
+  // before the first read of chunk c+1.
+  uint4 xf[2][2];
   auto step = [&](int c, auto u_const) {
     constexpr int u = decltype(u_const)::value;
+    constexpr int NLOAD = PPT + kSub * NF * 2;
+    constexpr int NM = NSTEP * NF;
     const int last = nchunks - 1;
-    load_x(min(c + 2, last), xr[u & 1]);
-    load_w(min(c + NB - 1, last), wbuf[(u + NB - 1) % NB]);
-    __builtin_amdgcn_sched_barrier(0);  // prefetches are issued before the matrix work
-    compute(c & 1, wbuf[u % NB]);
-    store_x((c + 1) & 1, xr[(u + 1) & 1]);
-    __syncthreads();
+    const int cx = min(c + 3, last), cw = min(c + NB - 1, last);
+    auto issue = [&](auto j_const) {
+      constexpr int j = decltype(j_const)::value;
+      if constexpr (j < PPT) {
+        xr[(u + 1) & 1][j] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff[j] + (uint32_t)cx * kChunk,
+                                                         0, 0));
+      } else {
+        constexpr int q = j - PPT, s = q / (NF * 2), f = (q / 2) % NF, pc = q % 2;
+        load_w1(cw, s, f, pc, wbuf[(u + NB - 1) % NB][s][f][pc]);
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t) {
+      if (t + 1 < NSTEP)
+        read_frag(u % 3, t + 1, xf[(t + 1) & 1]);
+      else
+        read_frag((u + 1) % 3, 0, xf[(t + 1) & 1]);
+      const int s = t / MT, m = t % MT;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        acc[m][f] = Mma<DT>::run(wbuf[u % NB][s][f], xf[t & 1], acc[m][f]);
+        const int mi = t * NF + f;
+        static_for<NLOAD>([&](auto j_const) {
+          constexpr int j = decltype(j_const)::value;
+          if (j * NM / NLOAD == mi) issue(j_const);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (t == NSTEP / 2 - 1) {
+        __syncthreads();
+        store_x((u + 2) % 3, xr[u & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
 
-  // Prologue: weights for stages 0..NB-2, tokens of chunk 0 in LDS, tokens of
-  // chunk 1 in registers.
+  // Epilogue inputs, fetched now so that their latency hides behind the main
+  // loop: per output row of this lane (token tok of each fragment m) its
+  // scale factor, and the workgroup's column scales into LDS.
+  const int tok = lane & 31, fq = (lane >> 5) * 4;
+  float rsc[MT];   // stage 1: token scale (0 for pad rows); stage 2: routing weight x row scale
+  int rslot[MT];   // stage 2: destination slot (S for pad rows)
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u) load_w(min(u, nchunks - 1), wbuf[u]);
-  load_x(0, xr[0]);
-  load_x(min(1, nchunks - 1), xr[1]);
-  store_x(0, xr[0]);
-  __syncthreads();
+  for (int m = 0; m < MT; ++m) {
+    const int p = row0 + m * 32 + tok;
+    const int slot = a.sorted_slot[p];
+    rslot[m] = slot;
+    if constexpr (STAGE == 1)
+      rsc[m] = DT == 1 ? (slot < S ? a.x_scale[slot / a.k] : 0.0f) : 1.0f;
+    else
+      rsc[m] = slot < S ? a.topk_w[slot] * (DT == 1 ? a.x_scale[p] : 1.0f) : 0.0f;
+  }
+  if constexpr (DT == 1) {
+    for (int i = tid; i < WGN; i += 256) {
+      if constexpr (STAGE == 1) {
+        const int half = WGN / 2;  // intermediate columns of this workgroup
+        scl[i] = a.w_scale[(size_t)e * 2 * a.I + (i / half) * a.I + ntile * half + i % half];
+      } else {
+        scl[i] = a.w_scale[(size_t)e * a.N + ntile * WGN + i];
+      }
+    }
+  }
 
-  // Steady state, unrolled by the period P = lcm(2, NB) so that every buffer
-  // index is static; then at most P-1 guarded tail stages.
-  constexpr int P = NB % 2 ? 2 * NB : NB;
+  // Prologue: weights of chunks 0..NB-2; tokens of chunks 0 and 1 in LDS
+  // buffers 0 and 1, chunk 2 in registers; fragment 0 of chunk 0 read.
+  {
+    const int last = nchunks - 1;
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u) load_w(min(u, last), wbuf[u]);
+    load_x(0, xr[0]);
+    load_x(min(1, last), xr[1]);
+    store_x(0, xr[0]);
+    store_x(1, xr[1]);
+    load_x(min(2, last), xr[0]);
+    __syncthreads();
+    read_frag(0, 0, xf[0]);
+  }
+
+  // Steady state, unrolled by the period P = 6 (token registers alternate
+  // by 2, LDS buffers and weight stages cycle by 3) so that every buffer
+  // index is static; then at most 5 guarded tail stages.
   int c0 = 0;
-  for (; c0 + P <= nchunks; c0 += P) {
+  for (; c0 + 6 <= nchunks; c0 += 6) {
     step(c0 + 0, IntC<0>{});
     step(c0 + 1, IntC<1>{});
-    if constexpr (P > 2) step(c0 + 2, IntC<2>{});
-    if constexpr (P > 3) step(c0 + 3, IntC<3>{});
-    if constexpr (P > 4) step(c0 + 4, IntC<4>{});
-    if constexpr (P > 5) step(c0 + 5, IntC<5>{});
+    step(c0 + 2, IntC<2>{});
+    step(c0 + 3, IntC<3>{});
+    step(c0 + 4, IntC<4>{});
+    step(c0 + 5, IntC<5>{});
   }
   if (c0 + 0 < nchunks) step(c0 + 0, IntC<0>{});
   if (c0 + 1 < nchunks) step(c0 + 1, IntC<1>{});
-  if constexpr (P > 2)
-    if (c0 + 2 < nchunks) step(c0 + 2, IntC<2>{});
-  if constexpr (P > 3)
-    if (c0 + 3 < nchunks) step(c0 + 3, IntC<3>{});
-  if constexpr (P > 4)
-    if (c0 + 4 < nchunks) step(c0 + 4, IntC<4>{});
+  if (c0 + 2 < nchunks) step(c0 + 2, IntC<2>{});
+  if (c0 + 3 < nchunks) step(c0 + 3, IntC<3>{});
+  if (c0 + 4 < nchunks) step(c0 + 4, IntC<4>{});
+  __syncthreads();  // all LDS reads done before the epilogue reuses the space
 
   if constexpr (KSPLIT > 1) {
     // Fixed-order reduction of the wave splits: split 0 + split 1 + split 2 + ...
@@ -288,34 +361,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     __syncthreads();  // the amax step below reuses the same LDS
   }
 
-  const int tok = lane & 31, fq = (lane >> 5) * 4;
   if constexpr (STAGE == 1) {
     // SwiGLU epilogue: fragment 2q is gate block ib0+q, fragment 2q+1 the
     // matching up block.
     uint16_t* act = reinterpret_cast<uint16_t*>(a.out);
     const int ib0 = rb0 / 2;
-    const float* sg = DT == 1 ? a.w_scale + (size_t)e * 2 * a.I : nullptr;
+    const int col0 = ntile * (WGN / 2);  // first intermediate column of this workgroup
     float amax[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       amax[m] = 0.0f;
       if (wk != 0) continue;
       const int p = row0 + m * 32 + tok;
-      float xs = 1.0f;
-      if constexpr (DT == 1) {
-        const int slot = a.sorted_slot[p];
-        xs = slot < S ? a.x_scale[slot / a.k] : 0.0f;
-      }
+      const float xs = rsc[m];
 #pragma unroll
       for (int qg = 0; qg < NF / 2 * 4; ++qg) {
         const int q = qg / 4, g = qg % 4;
         const int i0 = (ib0 + q) * 32 + 8 * g + fq;
-        float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
+        float gs[4] = {xs, xs, xs, xs}, us[4] = {xs, xs, xs, xs};
         if constexpr (DT == 1) {
-          float4 g4 = *reinterpret_cast<const float4*>(sg + i0);
-          float4 u4 = *reinterpret_cast<const float4*>(sg + a.I + i0);
-          gs[0] = g4.x * xs; gs[1] = g4.y * xs; gs[2] = g4.z * xs; gs[3] = g4.w * xs;
-          us[0] = u4.x * xs; us[1] = u4.y * xs; us[2] = u4.z * xs; us[3] = u4.w * xs;
+          const float4 g4 = *reinterpret_cast<const float4*>(scl + (i0 - col0));
+          const float4 u4 = *reinterpret_cast<const float4*>(scl + WGN / 2 + (i0 - col0));
+          gs[0] *= g4.x; gs[1] *= g4.y; gs[2] *= g4.z; gs[3] *= g4.w;
+          us[0] *= u4.x; us[1] *= u4.y; us[2] *= u4.z; us[3] *= u4.w;
         }
         uint32_t b[4];
 #pragma unroll
@@ -352,11 +420,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     float* part = reinterpret_cast<float*>(a.out) + (size_t)kg * S * a.N;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int p = row0 + m * 32 + tok;
-      const int slot = a.sorted_slot[p];
+      const int slot = rslot[m];
       if (slot >= S) continue;
-      float sc = a.topk_w[slot];
-      if constexpr (DT == 1) sc *= a.x_scale[p];
+      const float sc = rsc[m];
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -364,7 +430,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
           const int h0 = (rb0 + f) * 32 + 8 * g + fq;
           float ws[4] = {1.f, 1.f, 1.f, 1.f};
           if constexpr (DT == 1) {
-            float4 w4 = *reinterpret_cast<const float4*>(a.w_scale + (size_t)e * a.N + h0);
+            const float4 w4 = *reinterpret_cast<const float4*>(scl + (h0 - ntile * WGN));
             ws[0] = w4.x; ws[1] = w4.y; ws[2] = w4.z; ws[3] = w4.w;
           }
           float4 o;
@@ -452,18 +518,14 @@ int64_t live_mtiles(int T, int k, int E, int tile_rows) {
   return by_slots + (S < E ? S : E);
 }
 
-// Pipeline shape of a (mt, nf, ksplit) triple: stage bytes and weight stages.
+// Pipeline shape of a (mt, nf, ksplit) triple: stage bytes (the weight
+// pipeline is always three stages deep).
 void set_pipeline(GemmCfg& c) {
-  if (c.ksplit == 1 && c.mt * c.nf >= 16) {
-    c.ck = 64;   // prefill tiles: short stages keep the registers in budget
-    c.nb = 3;
-  } else if (c.ksplit == 4) {
-    c.ck = 128;  // decode: deep weight prefetch, small accumulators
-    c.nb = 3;
-  } else {
-    c.ck = 128;
-    c.nb = 2;
-  }
+  // Prefill tiles use 64-byte stages to keep the registers in budget; the
+  // others use 128-byte stages so that every stage has an even number of
+  // token fragments per wave.
+  c.ck = c.ksplit == 1 && c.mt * c.nf >= 16 ? 64 : 128;
+  c.nb = 3;
   c.wg_n = (4 / c.ksplit) * c.nf * 32;
 }
 
@@ -518,10 +580,11 @@ bool gemm_cfg_ok(int dt, int stage, const GemmCfg& c, int N, int K) {
   if (N % c.wg_n) return false;
   if (kbytes % ((int64_t)c.ksplit * c.kg * c.ck)) return false;
   if (stage == 1 && c.kg != 1) return false;
-  if (c.ksplit == 4) return c.mt == 1 && c.ck == 128 && c.nb == 3;
-  if (c.ksplit == 2) return c.mt <= 2 && c.ck == 128 && c.nb == 2;
-  if (c.ksplit == 1 && c.mt * c.nf >= 16) return c.ck == 64 && c.nb == 3;
-  return c.ksplit == 1 && c.ck == 128 && c.nb == 2;
+  if (c.nb != 3) return false;
+  if (c.ksplit == 4) return c.mt == 1 && c.ck == 128;
+  if (c.ksplit == 2) return c.mt <= 2 && c.ck == 128;
+  if (c.ksplit == 1 && c.mt * c.nf >= 16) return c.ck == 64;
+  return c.ksplit == 1 && c.ck == 128;
 }
 
 namespace {
@@ -538,12 +601,12 @@ template <int DT, int STAGE>
 hipError_t launch_dt_stage(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
   if (c.ksplit == 4) return launch_one<DT, STAGE, 1, 2, 4, 3, 128>(a, st);
   if (c.ksplit == 2)
-    return c.mt == 1 ? launch_one<DT, STAGE, 1, 2, 2, 2, 128>(a, st)
-                     : launch_one<DT, STAGE, 2, 2, 2, 2, 128>(a, st);
+    return c.mt == 1 ? launch_one<DT, STAGE, 1, 2, 2, 3, 128>(a, st)
+                     : launch_one<DT, STAGE, 2, 2, 2, 3, 128>(a, st);
   if (c.nf == 4) return launch_one<DT, STAGE, 4, 4, 1, 3, 64>(a, st);
   switch (c.mt) {
-    case 1: return launch_one<DT, STAGE, 1, 2, 1, 2, 128>(a, st);
-    case 2: return launch_one<DT, STAGE, 2, 2, 1, 2, 128>(a, st);
+    case 1: return launch_one<DT, STAGE, 1, 2, 1, 3, 128>(a, st);
+    case 2: return launch_one<DT, STAGE, 2, 2, 1, 3, 128>(a, st);
     case 4: return launch_one<DT, STAGE, 4, 2, 1, 3, 64>(a, st);
   }
   return hipErrorInvalidValue;
