@@ -36,6 +36,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool valid_bm(int bm) { return bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
+// ceil(2^35 / k): the kernels divide slot numbers (< 2^30) by k with a multiply.
+uint64_t k_magic(int k) { return (((uint64_t)1 << 35) + k - 1) / k; }
+
 // M-tiles per scheduling group: about 2048 rows, one expert's share at prefill.
 int group_m(int mt) { return 2048 / (32 * mt); }
 
@@ -217,6 +220,7 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, c
   a.n_ntiles = 2 * I / c.wg_n;
   a.kg = 1;
   a.group_m = group_m(c.mt);
+  a.k_magic = k_magic(k);
   return hip_status(moe::launch_gemm(dt, 1, c, a, stream), "moe_stage1 launch");
 }
 
@@ -293,6 +297,7 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
   a.n_ntiles = H / c.wg_n;
   a.kg = c.kg;
   a.group_m = group_m(c.mt);
+  a.k_magic = k_magic(k);
   err = moe::launch_gemm(dt, 2, c, a, stream);
   if (err != hipSuccess) return hip_status(err, "moe_stage2 GEMM launch");
   moe::CombineArgs cb{part, T, k, H, c.kg, (uint16_t*)out};

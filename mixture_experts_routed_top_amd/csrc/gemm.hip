@@ -83,12 +83,25 @@ constexpr uint32_t kPadOffset = 0x80000000u;
 // it is a bijection inside each piece).
 __device__ __forceinline__ int lds_swz(int c) { return 4 * (c & 1) + 10 * (c >> 1); }
 
+// n / k for 0 <= n < 2^30 and 1 <= k <= 32 with magic = ceil(2^35 / k):
+// n*magic / 2^35 = n/k + n*(magic*k - 2^35)/(k*2^35), and the added term is
+// below (k-1)/(32k), too small to carry the fraction of n/k (at most
+// (k-1)/k) past the next integer, so the quotient is exact. A multiply
+// instead of a division keeps the compiler from branching around it.
+__device__ __forceinline__ uint32_t div_k(int n, uint64_t magic) {
+  return (uint32_t)(((uint64_t)(uint32_t)n * magic) >> 35);
+}
+
 template <int MT, int KSPLIT, int CK>
 constexpr int gemm_lds_bytes() {
   return 3 * KSPLIT * (CK / 64) * MT * kFrag;  // three token buffers
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp; the
+// product is rounded to bf16 or requantised right after).
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 template <int DT, int STAGE, int MT, int NF, int KSPLIT, int NB, int CK>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
@@ -107,7 +120,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   static_assert(NF == 2 || NF == 4, "weight fragments per wave (gate/up pairs)");
   static_assert(KSPLIT == 1 || (KSPLIT - 1) * WN * NACC * 64 * 4 <= LDS, "reduction space");
   static_assert(WN * BMT * 4 <= LDS, "amax space");
-  static_assert(NB == 3, "weight pipeline depth (the unroll period assumes 3)");
+  static_assert(NB == 3 || NB == 4, "weight pipeline depth");
 
   // Token buffers (reused by the epilogue), then the column scales of this
   // workgroup's features (FP8), staged once so that the epilogue reads LDS.
@@ -130,10 +143,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const int gm = min(a.group_m, a.n_mtiles - grp * a.group_m);
   const int mtile = grp * a.group_m + rem % gm, ntile = rem / gm;
 
-  const int total = *a.total_padded;
+  // The grouping's size and this tile's expert are read together (the
+  // expert index is in bounds for any tile of the launch), then the tile
+  // exits if it lies past the padded total.
   const int row0 = mtile * BMT;
+  const int total = *a.total_padded;
+  const int e_raw = a.tile_expert[row0 / a.bm];
   if (row0 >= total) return;
-  const int e = a.tile_expert[row0 / a.bm];
+  const int e = e_raw;
   const int S = a.T * a.k;
   const int Kb = a.K_bytes;                    // reduction bytes of a full row
   const int Kw = Kb / (KSPLIT * a.kg);         // reduction bytes per wave
@@ -156,13 +173,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const int c = q & 3, r = (q >> 2) & 31, m = (q >> 7) % MT;
     const int s = (q / (128 * MT)) % kSub, ks = q / (128 * MT * kSub);
     const int p = row0 + m * 32 + r;
-    uint32_t rowbase;
-    if constexpr (STAGE == 1) {
-      const int slot = a.sorted_slot[p];
-      rowbase = slot < S ? (uint32_t)(slot / a.k) * (uint32_t)Kb : kPadOffset;
-    } else {
-      rowbase = (uint32_t)p * (uint32_t)Kb;
-    }
+    // Stage 1 gathers token rows; stage 2 reads intermediate rows in place.
+    // Pad rows (sentinel slot) are not read at all.
+    const int slot = a.sorted_slot[p];
+    const uint32_t row = STAGE == 1 ? div_k(min(slot, S - 1), a.k_magic) : (uint32_t)p;
+    const uint32_t rowbase = slot < S ? row * (uint32_t)Kb : kPadOffset;  // select, no branch
     xoff[j] = rowbase + (uint32_t)(kbase + ks * Kw + s * 64 + c * 16);
     loff[j] = ((ks * kSub + s) * MT + m) * kFrag + (c & 1) * kPiece +
               ((r + 32 * (c >> 1)) ^ lds_swz(c)) * 16;
@@ -275,30 +290,39 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 
   // Epilogue inputs, fetched now so that their latency hides behind the main
   // loop: per output row of this lane (token tok of each fragment m) its
-  // scale factor, and the workgroup's column scales into LDS.
+  // scale factor, and the workgroup's column scales into LDS. The loads are
+  // unconditional (pad rows read a clamped index and are masked in the
+  // epilogue), so nothing here waits for memory.
   const int tok = lane & 31, fq = (lane >> 5) * 4;
-  float rsc[MT];   // stage 1: token scale (0 for pad rows); stage 2: routing weight x row scale
-  int rslot[MT];   // stage 2: destination slot (S for pad rows)
+  float rsc[MT];   // stage 1: token scale; stage 2: routing weight x row scale
+  int rslot[MT];   // slot of the row (S for pad rows)
+#pragma unroll
+  for (int m = 0; m < MT; ++m) rslot[m] = a.sorted_slot[row0 + m * 32 + tok];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int p = row0 + m * 32 + tok;
-    const int slot = a.sorted_slot[p];
-    rslot[m] = slot;
+    const int sc = min(rslot[m], S - 1);
     if constexpr (STAGE == 1)
-      rsc[m] = DT == 1 ? (slot < S ? a.x_scale[slot / a.k] : 0.0f) : 1.0f;
+      rsc[m] = DT == 1 ? a.x_scale[div_k(sc, a.k_magic)] : 1.0f;
     else
-      rsc[m] = slot < S ? a.topk_w[slot] * (DT == 1 ? a.x_scale[p] : 1.0f) : 0.0f;
+      rsc[m] = a.topk_w[sc] * (DT == 1 ? a.x_scale[row0 + m * 32 + tok] : 1.0f);
   }
-  if constexpr (DT == 1) {
-    for (int i = tid; i < WGN; i += 256) {
+  // Column scales of this workgroup's features (FP8): loaded after the
+  // pipeline's first loads, kept in registers through the main loop and
+  // written to LDS after it, so no wait is spent on them.
+  constexpr int NSC = DT == 1 ? (WGN + 255) / 256 : 1;
+  float colsc[NSC];
+  auto load_colsc = [&]() {
+#pragma unroll
+    for (int u = 0; u < NSC; ++u) {
+      const int i = min(tid + 256 * u, WGN - 1);
       if constexpr (STAGE == 1) {
         const int half = WGN / 2;  // intermediate columns of this workgroup
-        scl[i] = a.w_scale[(size_t)e * 2 * a.I + (i / half) * a.I + ntile * half + i % half];
+        colsc[u] = a.w_scale[(size_t)e * 2 * a.I + (i / half) * a.I + ntile * half + i % half];
       } else {
-        scl[i] = a.w_scale[(size_t)e * a.N + ntile * WGN + i];
+        colsc[u] = a.w_scale[(size_t)e * a.N + ntile * WGN + i];
       }
     }
-  }
+  };
 
   // Prologue: weights of chunks 0..NB-2; tokens of chunks 0 and 1 in LDS
   // buffers 0 and 1, chunk 2 in registers; fragment 0 of chunk 0 read.
@@ -308,6 +332,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     for (int u = 0; u < NB - 1; ++u) load_w(min(u, last), wbuf[u]);
     load_x(0, xr[0]);
     load_x(min(1, last), xr[1]);
+    if constexpr (DT == 1) load_colsc();
     store_x(0, xr[0]);
     store_x(1, xr[1]);
     load_x(min(2, last), xr[0]);
@@ -315,24 +340,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     read_frag(0, 0, xf[0]);
   }
 
-  // Steady state, unrolled by the period P = 6 (token registers alternate
-  // by 2, LDS buffers and weight stages cycle by 3) so that every buffer
-  // index is static; then at most 5 guarded tail stages.
+  // Steady state, unrolled by the period P = lcm(2, 3, NB) (token registers
+  // alternate by 2, LDS buffers cycle by 3, weight stages by NB) so that every
+  // buffer index is static; then at most P-1 guarded tail stages.
+  constexpr int P = NB == 4 ? 12 : 6;
   int c0 = 0;
-  for (; c0 + 6 <= nchunks; c0 += 6) {
-    step(c0 + 0, IntC<0>{});
-    step(c0 + 1, IntC<1>{});
-    step(c0 + 2, IntC<2>{});
-    step(c0 + 3, IntC<3>{});
-    step(c0 + 4, IntC<4>{});
-    step(c0 + 5, IntC<5>{});
+  for (; c0 + P <= nchunks; c0 += P) static_for<P>([&](auto u) { step(c0 + decltype(u)::value, u); });
+  static_for<P - 1>([&](auto u) {
+    if (c0 + decltype(u)::value < nchunks) step(c0 + decltype(u)::value, u);
+  });
+  if constexpr (DT == 1) {
+#pragma unroll
+    for (int u = 0; u < NSC; ++u)
+      if (WGN % 256 == 0 || tid + 256 * u < WGN) scl[tid + 256 * u] = colsc[u];
   }
-  if (c0 + 0 < nchunks) step(c0 + 0, IntC<0>{});
-  if (c0 + 1 < nchunks) step(c0 + 1, IntC<1>{});
-  if (c0 + 2 < nchunks) step(c0 + 2, IntC<2>{});
-  if (c0 + 3 < nchunks) step(c0 + 3, IntC<3>{});
-  if (c0 + 4 < nchunks) step(c0 + 4, IntC<4>{});
-  __syncthreads();  // all LDS reads done before the epilogue reuses the space
+  __syncthreads();  // all LDS reads done before the epilogue reuses the space; scales visible
 
   if constexpr (KSPLIT > 1) {
     // Fixed-order reduction of the wave splits: split 0 + split 1 + split 2 + ...
@@ -373,7 +395,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       amax[m] = 0.0f;
       if (wk != 0) continue;
       const int p = row0 + m * 32 + tok;
-      const float xs = rsc[m];
+      const float xs = rslot[m] < S ? rsc[m] : 0.0f;  // pad rows: act = 0
 #pragma unroll
       for (int qg = 0; qg < NF / 2 * 4; ++qg) {
         const int q = qg / 4, g = qg % 4;
@@ -385,16 +407,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
           gs[0] *= g4.x; gs[1] *= g4.y; gs[2] *= g4.z; gs[3] *= g4.w;
           us[0] *= u4.x; us[1] *= u4.y; us[2] *= u4.z; us[3] *= u4.w;
         }
-        uint32_t b[4];
+        float h[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float gv = acc[m][2 * q][4 * g + r] * gs[r];
           const float uv = acc[m][2 * q + 1][4 * g + r] * us[r];
-          b[r] = f32_to_bf16_bits(silu(gv) * uv);
-          amax[m] = fmaxf(amax[m], fabsf(bf16_bits_to_f32(b[r])));
+          h[r] = silu(gv) * uv;
         }
-        *reinterpret_cast<uint2*>(act + (size_t)p * a.I + i0) =
-            make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+        const uint32_t lo = f32x2_to_bf16x2(h[0], h[1]), hi = f32x2_to_bf16x2(h[2], h[3]);
+        // row maximum of the stored (bf16) values: |x| of a bf16 is exact in fp32
+        amax[m] = fmaxf(amax[m], fmaxf(fmaxf(fabsf(__uint_as_float(lo << 16)),
+                                             fabsf(__uint_as_float(lo & 0xffff0000u))),
+                                       fmaxf(fabsf(__uint_as_float(hi << 16)),
+                                             fabsf(__uint_as_float(hi & 0xffff0000u)))));
+        *reinterpret_cast<uint2*>(act + (size_t)p * a.I + i0) = make_uint2(lo, hi);
       }
     }
     if constexpr (DT == 1) {
@@ -500,8 +526,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       }
     }
     *reinterpret_cast<uint2*>(a.out + (size_t)t * a.H + h) =
-        make_uint2(f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16),
-                   f32_to_bf16_bits(s.z) | (f32_to_bf16_bits(s.w) << 16));
+        make_uint2(f32x2_to_bf16x2(s.x, s.y), f32x2_to_bf16x2(s.z, s.w));
   }
 }
 

@@ -18,11 +18,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
 
-// fp32 -> bf16 bit pattern, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 packed little-endian (a in the low half), round to
+// nearest even: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Two fp32 -> two OCP e4m3fn codes in the low 16 bits (round to nearest even).

@@ -73,6 +73,7 @@ struct GemmArgs {
   int64_t x_bytes;         // size of X in bytes (< 2 GiB): loads past it read zeros
   int n_mtiles, n_ntiles;  // row tiles (32*mt rows) and feature tiles (wg_n rows)
   int kg, group_m;         // reduction split over workgroups; M-tiles per schedule group
+  uint64_t k_magic;        // ceil(2^35 / k): slot / k as a multiply
 };
 hipError_t launch_gemm(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipStream_t st);
 
