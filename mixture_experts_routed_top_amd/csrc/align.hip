@@ -2,19 +2,24 @@
 // sort (the "dynamic expert sizes" of the routed MoE GEMM in the FlyDSL-in-JAX
 // talk summary, 5:56).
 //
-// One workgroup of 1024 threads. Pass 1 counts slots per expert with LDS
-// integer atomics (order free). One thread scans the padded counts. Pass 2
-// walks the slots in 1024-slot chunks in ascending order; inside a chunk a
-// slot's rank among equal experts comes from a wave ballot (lanes are in
-// ascending slot order) plus the counts of the lower waves, so the result is
-// exactly the stable order. Integer work only: bit-exact by construction.
+// One workgroup of 1024 threads (16 waves). Every thread first loads its ids
+// for all 1024-slot chunks (thread t holds slot c*1024 + t of chunk c), so the
+// loads are in flight together. Pass 1 counts slots per expert with wave
+// ballots, one LDS integer atomic per wave and expert (order free). One
+// thread turns the padded counts into
+// offsets. Pass 2 walks the chunks in ascending order: inside a chunk a slot's
+// rank among equal experts is a wave ballot (lanes are in ascending slot
+// order) plus the counts of the lower waves, which one lane per (expert, wave)
+// pair obtains with a 16-lane shuffle scan; so the result is exactly the
+// stable order. Integer work only: bit-exact by construction.
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace moe {
 
 constexpr int kAlignThreads = 1024;
-constexpr int kAlignWaves = kAlignThreads / 64;
+constexpr int kAlignWaves = kAlignThreads / 64;  // 16
+constexpr int kIdsInRegs = 32;                   // chunks held in registers (S <= 32768)
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a) {
   __shared__ int cnt[64];
@@ -24,17 +29,40 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a) {
   __shared__ int bad;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, E = a.E, bm = a.bm;
+  const int nchunks = (S + kAlignThreads - 1) / kAlignThreads;
+
+  int idv[kIdsInRegs];
+#pragma unroll
+  for (int i = 0; i < kIdsInRegs; ++i) {
+    const int s = i * kAlignThreads + tid;  // clamped load, then select: no branches
+    const int v = a.ids[min(s, S - 1)];
+    idv[i] = s < S ? v : -1;
+  }
+  auto id_of = [&](int i) {  // id of slot i*1024 + tid (-1 past the end)
+    const int s = i * kAlignThreads + tid;
+    return s < S ? a.ids[s] : -1;
+  };
 
   if (tid < 64) cnt[tid] = 0;
   if (tid == 0) bad = 0;
   __syncthreads();
-  for (int s = tid; s < S; s += kAlignThreads) {
-    int e = a.ids[s];
-    if (e < 0 || e >= E)
-      bad = 1;
-    else
-      atomicAdd(&cnt[e], 1);
-  }
+  // Per-wave counts from ballots: one LDS atomic per wave and expert instead
+  // of one per slot on a few hot counters.
+  int mine = 0;  // this lane's count for expert `lane` (lanes e < E)
+  bool anybad = false;
+  auto count = [&](int i, int e) {
+    anybad |= i * kAlignThreads + tid < S && (e < 0 || e >= E);
+    for (int ee = 0; ee < E; ++ee) {
+      const int c = __popcll(__ballot(e == ee));
+      if (lane == ee) mine += c;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kIdsInRegs; ++i)
+    if (i < nchunks) count(i, idv[i]);
+  for (int i = kIdsInRegs; i < nchunks; ++i) count(i, id_of(i));
+  if (anybad) bad = 1;
+  if (lane < E && mine) atomicAdd(&cnt[lane], mine);
   __syncthreads();
   if (bad) {  // invalid ids: publish an empty grouping so nothing downstream runs
     if (tid == 0) *a.total = 0;
@@ -57,44 +85,59 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a) {
   }
   if (tid == 0) a.offset[E] = off[E];
 
-  // Tile experts and pad sentinels.
-  const int total = off[E];
-  for (int i = tid; i < total / bm; i += kAlignThreads) {
-    int e = 0;
-    while (off[e + 1] <= i * bm) ++e;
-    a.tile_expert[i] = e;
-  }
-  for (int p = tid; p < total; p += kAlignThreads) {
-    int e = 0;
-    while (off[e + 1] <= p) ++e;
-    if (p - off[e] >= cnt[e]) a.sorted_slot[p] = S;
-  }
-  __syncthreads();
-
-  // Stable scatter.
+  // Stable scatter, one chunk at a time. Destinations are kept in registers
+  // and every global store is issued after the chunk loop: on this
+  // architecture stores and loads share one completion counter, so a store
+  // inside the loop would make later waits wait for it too.
   const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int c0 = 0; c0 < S; c0 += kAlignThreads) {
-    const int s = c0 + tid;
-    const int e = s < S ? a.ids[s] : -1;
+  const int se = tid >> 4, sw = tid & 15;  // scan lane: expert se, wave sw
+  auto rank_of = [&](int e) {  // destination row of this thread's slot (or -1)
     int rank = 0;
     for (int ee = 0; ee < E; ++ee) {
-      unsigned long long m = __ballot(e == ee);
+      const unsigned long long m = __ballot(e == ee);
       if (e == ee) rank = __popcll(m & lt);
       if (lane == 0) wcnt[wave][ee] = __popcll(m);
     }
     __syncthreads();
-    if (tid < E) {
-      int run = base[tid];
-      for (int w = 0; w < kAlignWaves; ++w) {
-        int c = wcnt[w][tid];
-        wcnt[w][tid] = run;
-        run += c;
+    // Exclusive scan of the per-wave counts of each expert over the 16 waves
+    // (the 16 lanes of one expert sit in one wave), added to the expert's
+    // running base; the last wave's lane advances the base.
+    if (se < E) {
+      const int v = wcnt[sw][se];
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+        const int o = __shfl_up(incl, d, 16);
+        if (sw >= d) incl += o;
       }
-      base[tid] = run;
+      const int b = base[se];
+      wcnt[sw][se] = b + incl - v;
+      if (sw == 15) base[se] = b + incl;
     }
     __syncthreads();
-    if (e >= 0) a.sorted_slot[wcnt[wave][e] + rank] = s;
+    const int dst = e >= 0 ? wcnt[wave][e] + rank : -1;
     __syncthreads();
+    return dst;
+  };
+#pragma unroll
+  for (int i = 0; i < kIdsInRegs; ++i)  // each id is replaced by its destination row
+    if (i < nchunks) idv[i] = rank_of(idv[i]);
+
+  // Tile experts and pad sentinels (fewer than block_m pad rows per expert),
+  // then the slots of the chunks.
+  for (int e = 0; e < E; ++e) {
+    const int o0 = off[e], o1 = off[e + 1];
+    for (int i = o0 / bm + tid; i < o1 / bm; i += kAlignThreads) a.tile_expert[i] = e;
+    const int p = o0 + cnt[e] + tid;
+    if (p < o1) a.sorted_slot[p] = S;
+  }
+#pragma unroll
+  for (int i = 0; i < kIdsInRegs; ++i)
+    if (i < nchunks && idv[i] >= 0) a.sorted_slot[idv[i]] = i * kAlignThreads + tid;
+  // Batches beyond the register-held chunks (more than 32768 slots).
+  for (int i = kIdsInRegs; i < nchunks; ++i) {
+    const int d = rank_of(id_of(i));
+    if (d >= 0) a.sorted_slot[d] = i * kAlignThreads + tid;
   }
 }
 

@@ -130,6 +130,16 @@ __device__ __forceinline__ void quantise_row(const RouteArgs& a, int t, int lane
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   if (lane == 0) a.x_scale[t] = s;
+  // Correctly rounded x / s from one reciprocal per row (Markstein): with
+  // r = RN(1/s), q0 = RN(x*r) is within one ulp of x/s, the remainder
+  // x - s*q0 is exact in one fma, and RN(q0 + rem*r) is RN(x/s) whenever the
+  // quotient is a normal number; smaller quotients encode to (signed) zero
+  // either way, and copysign keeps the sign of a zero x.
+  const float r = 1.0f / s;
+  auto qdiv = [&](float x) {
+    const float q0 = x * r;
+    return clamp448(copysignf(fmaf(fmaf(-q0, s, x), r, q0), x));
+  };
   uint8_t* qr = a.x_q + (size_t)t * a.H;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -137,10 +147,8 @@ __device__ __forceinline__ void quantise_row(const RouteArgs& a, int t, int lane
     if (c < nchunk) {
       float xf[8];
       unpack8(xv[i], xf);
-      const uint32_t lo = f32x4_to_e4m3(clamp448(xf[0] / s), clamp448(xf[1] / s),
-                                        clamp448(xf[2] / s), clamp448(xf[3] / s));
-      const uint32_t hi = f32x4_to_e4m3(clamp448(xf[4] / s), clamp448(xf[5] / s),
-                                        clamp448(xf[6] / s), clamp448(xf[7] / s));
+      const uint32_t lo = f32x4_to_e4m3(qdiv(xf[0]), qdiv(xf[1]), qdiv(xf[2]), qdiv(xf[3]));
+      const uint32_t hi = f32x4_to_e4m3(qdiv(xf[4]), qdiv(xf[5]), qdiv(xf[6]), qdiv(xf[7]));
       *reinterpret_cast<uint2*>(qr + (size_t)c * 8) = make_uint2(lo, hi);
     }
   }

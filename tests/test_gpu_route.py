@@ -98,3 +98,20 @@ def test_fp8_conversion_of_every_bf16_value_in_range():
     x[:, per] = 0x43E0  # 448.0
     wr = workloads.to_bf16_bits(np.ones((2, H)) / H)
     check_route(x, wr, None, 1, tag="all bf16 codes")
+
+
+def test_fp8_quantisation_over_many_binades():
+    """Rows whose values span 2^-140 .. 2^10 (bf16 normals and subnormals, both signs,
+    zeros of both signs): codes and scales bit-exact against the oracle's fp32 divide."""
+    rng = np.random.default_rng(11)
+    T, H = 64, 4096
+    mant = rng.uniform(1.0, 2.0, (T, H))
+    expo = rng.integers(-140, 11, (T, H))
+    sign = rng.choice([-1.0, 1.0], (T, H))
+    x = workloads.to_bf16_bits((sign * mant * np.exp2(expo.astype(np.float64))).astype(np.float32))
+    x[3, ::7] = 0x8000  # -0.0
+    x[4, ::5] = 0x0000
+    x[5] = workloads.to_bf16_bits(rng.standard_normal(H) * 1e-30)  # a row of tiny values only
+    wr = workloads.to_bf16_bits(rng.standard_normal((8, H)) / 64)
+    check_route(x, wr, None, 2, tag="many binades")
+
