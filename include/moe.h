@@ -171,12 +171,16 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, c
  *                      code = e4m3fn(act_p / scale); fp32 accumulation)
  *   out[t, :] = bf16( sum_{j=0..k-1} w[t,j] * y_{t,j} ), summed in ascending j
  *   in fp32: a fixed order, no floating-point atomics, so results are
- *   reproducible bit for bit.
+ *   reproducible bit for bit on a given device. (At prefill sizes the tiles
+ *   of a partial last round of workgroups are cut into pieces along the
+ *   reduction whose partials are summed in piece order; the cut follows from
+ *   the number of workgroups the device runs at once.)
  *
  * act, act_amax from moe_stage1; w2, s2 from moe_preshuffle; topk_w fp32 [T,k]
  * out bf16 [T,H] (out); workspace [moe_stage2_workspace_bytes()] bytes (device,
- * 256-byte aligned): per-slot weighted partials and, for FP8, the requantised
- * intermediate.
+ * 256-byte aligned): per-slot weighted partials, for FP8 the requantised
+ * intermediate, and at prefill sizes the partials of those reduction pieces.
+ * Calls that use one workspace must be ordered (same stream or synchronised).
  */
 int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int I, int block_m);
 moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, const void* w2,

@@ -233,6 +233,8 @@ int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int
     const int64_t cap = capacity(T, k, E, block_m);
     bytes += up(cap * I) + up(cap * 4);  // requantised intermediate + row scales
   }
+  if (c.tail_split > 0)  // partials of the tail pieces
+    bytes += up((int64_t)moe::kTailPieces * 32 * c.mt * c.wg_n * 4);
   return bytes;
 }
 
@@ -274,6 +276,7 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
     if (err != hipSuccess) return hip_status(err, "moe_stage2 requantisation");
     x = act_q;
     xs = act_scale;
+    ws += up(cap * I) + up(cap * 4);
   }
   moe::GemmArgs a{};
   a.X = (const uint8_t*)x;
@@ -298,8 +301,21 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
   a.kg = c.kg;
   a.group_m = group_m(c.mt);
   a.k_magic = k_magic(k);
+  a.tail_split = c.tail_split;
+  if (c.tail_split > 0) {
+    a.tail_part = (float*)ws;
+    a.resident = moe::gemm_resident(dt, 2, c);
+    CHECK(a.resident > 0, MOE_ERR_HIP, "moe_stage2: occupancy query failed");
+  }
   err = moe::launch_gemm(dt, 2, c, a, stream);
   if (err != hipSuccess) return hip_status(err, "moe_stage2 GEMM launch");
+  if (c.tail_split > 0) {
+    moe::TailReduceArgs tr{a.tail_part, sorted_slot, total_padded, part, T * k, H, 32 * c.mt,
+                           c.wg_n, a.n_ntiles, a.group_m, a.resident, c.tail_split,
+                           a.K_bytes / c.ck};
+    err = moe::launch_tail_reduce(tr, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_stage2 tail reduction launch");
+  }
   moe::CombineArgs cb{part, T, k, H, c.kg, (uint16_t*)out};
   return hip_status(moe::launch_combine(cb, stream), "moe_stage2 combine launch");
 }

@@ -25,6 +25,8 @@
 #include "moe_device.h"
 #include "moe_launch.h"
 
+#include <atomic>
+
 namespace moe {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -97,6 +99,39 @@ constexpr int gemm_lds_bytes() {
   return 3 * KSPLIT * (CK / 64) * MT * kFrag;  // three token buffers
 }
 
+// Logical tile -> (row tile, feature tile): groups of group_m row tiles sweep
+// the feature tiles, so that co-resident workgroups of one XCD share weight
+// slabs and token rows in its L2. n_m row tiles in all.
+__device__ __forceinline__ void tile_coords(int logical, int n_m, int group_m, int n_ntiles,
+                                            int& mtile, int& ntile) {
+  const int per_group = group_m * n_ntiles;
+  const int grp = logical / per_group, rem = logical % per_group;
+  const int gm = min(group_m, n_m - grp * group_m);
+  mtile = grp * group_m + rem % gm;
+  ntile = rem / gm;
+}
+
+// Plan of a stage-2 launch over n_live tiles with `resident` workgroups per
+// round: the last, partial round's `tail` tiles are cut into `split` pieces
+// along the reduction (at most max_split, at most kTailPieces pieces, at most
+// one piece per chunk) when that gives at least two per tile; the first
+// n_full tiles run whole.
+struct TailPlan {
+  int n_full, tail, split;
+};
+__device__ __forceinline__ TailPlan tail_plan(int n_live, int resident, int max_split,
+                                              int nchunks) {
+  TailPlan p{n_live, 0, 1};
+  const int t = resident > 0 ? n_live % resident : 0;
+  if (max_split < 2 || t == 0) return p;
+  int s = min(min(max_split, resident / t), min(kTailPieces / t, nchunks));
+  if (s < 2) return p;
+  p.n_full = n_live - t;
+  p.tail = t;
+  p.split = s;
+  return p;
+}
+
 // silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp; the
 // product is rounded to bf16 or requantised right after).
 __device__ __forceinline__ float silu(float z) {
@@ -131,31 +166,52 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wk = wave / WN;
 
-  // Tile order: XCD-contiguous runs of logical tiles; inside a run, groups of
-  // gm M-tiles sweep the N-tiles so that co-resident workgroups of one XCD
-  // share weight slabs and token rows in its L2.
-  const int n_mn = a.n_mtiles * a.n_ntiles;
-  const int logical = xcd_remap(blockIdx.x, n_mn * a.kg);
-  const int kg = logical % a.kg;
-  const int mn = logical / a.kg;
-  const int per_group = a.group_m * a.n_ntiles;
-  const int grp = mn / per_group, rem = mn % per_group;
-  const int gm = min(a.group_m, a.n_mtiles - grp * a.group_m);
-  const int mtile = grp * a.group_m + rem % gm, ntile = rem / gm;
-
-  // The grouping's size and this tile's expert are read together (the
-  // expert index is in bounds for any tile of the launch), then the tile
-  // exits if it lies past the padded total.
-  const int row0 = mtile * BMT;
-  const int total = *a.total_padded;
-  const int e_raw = a.tile_expert[row0 / a.bm];
-  if (row0 >= total) return;
-  const int e = e_raw;
   const int S = a.T * a.k;
   const int Kb = a.K_bytes;                    // reduction bytes of a full row
   const int Kw = Kb / (KSPLIT * a.kg);         // reduction bytes per wave
-  const int nchunks = Kw / kChunk;
-  const int kbase = (kg * KSPLIT) * Kw;        // first reduction byte of this workgroup
+  int nchunks = Kw / kChunk;
+
+  // Tile order: XCD-contiguous runs of logical tiles (xcd_remap), grouped as
+  // tile_coords describes.
+  int kg = 0, mtile, ntile, total, e_raw;
+  int piece = -1, tail_idx = 0, n_tail = 0;  // stage-2 tail piece of this workgroup
+  int cbegin = 0;                            // first reduction chunk
+  if (a.tail_split == 0) {
+    const int logical = xcd_remap(blockIdx.x, a.n_mtiles * a.n_ntiles * a.kg);
+    kg = logical % a.kg;
+    tile_coords(logical / a.kg, a.n_mtiles, a.group_m, a.n_ntiles, mtile, ntile);
+    // The grouping's size and this tile's expert are read together (the
+    // expert index is in bounds for any tile of the launch), then the tile
+    // exits if it lies past the padded total.
+    total = *a.total_padded;
+    e_raw = a.tile_expert[mtile * BMT / a.bm];
+    if (mtile * BMT >= total) return;
+  } else {
+    // Live tiles only (the padded total is a multiple of the tile rows); the
+    // partial last round's tiles are cut into pieces along the reduction.
+    total = *a.total_padded;
+    const int n_m = total / BMT;
+    const TailPlan pl = tail_plan(n_m * a.n_ntiles, a.resident, a.tail_split, nchunks);
+    const int b = blockIdx.x;
+    int logical;
+    if (b < pl.n_full) {
+      logical = xcd_remap(b, pl.n_full);
+    } else {
+      const int pi = b - pl.n_full;
+      if (pi >= pl.tail * pl.split) return;
+      tail_idx = pi % pl.tail;
+      piece = pi / pl.tail;
+      n_tail = pl.tail;
+      logical = pl.n_full + tail_idx;
+      cbegin = piece * nchunks / pl.split;
+      nchunks = (piece + 1) * nchunks / pl.split - cbegin;
+    }
+    tile_coords(logical, n_m, a.group_m, a.n_ntiles, mtile, ntile);
+    e_raw = a.tile_expert[mtile * BMT / a.bm];
+  }
+  const int row0 = mtile * BMT;
+  const int e = e_raw;
+  const int kbase = (kg * KSPLIT) * Kw + cbegin * kChunk;  // first reduction byte of this workgroup
 
   // Token pieces this thread stages each stage. Piece q (thread tid, slot j):
   // 16-byte column c = q%4 of the 64-byte window, row r = (q/4)%32 of fragment
@@ -414,13 +470,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
           const float uv = acc[m][2 * q + 1][4 * g + r] * us[r];
           h[r] = silu(gv) * uv;
         }
-        const uint32_t lo = f32x2_to_bf16x2(h[0], h[1]), hi = f32x2_to_bf16x2(h[2], h[3]);
-        // row maximum of the stored (bf16) values: |x| of a bf16 is exact in fp32
-        amax[m] = fmaxf(amax[m], fmaxf(fmaxf(fabsf(__uint_as_float(lo << 16)),
-                                             fabsf(__uint_as_float(lo & 0xffff0000u))),
-                                       fmaxf(fabsf(__uint_as_float(hi << 16)),
-                                             fabsf(__uint_as_float(hi & 0xffff0000u)))));
-        *reinterpret_cast<uint2*>(act + (size_t)p * a.I + i0) = make_uint2(lo, hi);
+        // Rounding to bf16 is monotonic and odd, so the maximum of the stored
+        // magnitudes is the rounded maximum of these: rounded once, below.
+        amax[m] = fmaxf(amax[m],
+                        fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3]))));
+        *reinterpret_cast<uint2*>(act + (size_t)p * a.I + i0) =
+            make_uint2(f32x2_to_bf16x2(h[0], h[1]), f32x2_to_bf16x2(h[2], h[3]));
       }
     }
     if constexpr (DT == 1) {
@@ -430,7 +485,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const float v = fmaxf(amax[m], __shfl_xor(amax[m], 32, 64));
-        if (wk == 0 && lane < 32) wmax[wn * BMT + m * 32 + lane] = v;
+        const float vb = __uint_as_float(f32x2_to_bf16x2(v, 0.0f) << 16);
+        if (wk == 0 && lane < 32) wmax[wn * BMT + m * 32 + lane] = vb;
       }
       __syncthreads();
       for (int r = tid; r < BMT; r += 256) {
@@ -444,6 +500,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     // Down-projection epilogue: weighted per-slot partials, one writer per element.
     if (wk != 0) return;
     float* part = reinterpret_cast<float*>(a.out) + (size_t)kg * S * a.N;
+    // A tail piece writes its tile-local partial instead: rows of the tile,
+    // columns of the workgroup, in the piece's slice of the tail space.
+    float* const tp = a.tail_part + (size_t)(piece * n_tail + tail_idx) * BMT * WGN;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int slot = rslot[m];
@@ -464,7 +523,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
           o.y = acc[m][f][4 * g + 1] * ws[1] * sc;
           o.z = acc[m][f][4 * g + 2] * ws[2] * sc;
           o.w = acc[m][f][4 * g + 3] * ws[3] * sc;
-          *reinterpret_cast<float4*>(part + (size_t)slot * a.N + h0) = o;
+          if (piece < 0)
+            *reinterpret_cast<float4*>(part + (size_t)slot * a.N + h0) = o;
+          else
+            *reinterpret_cast<float4*>(tp + (size_t)(m * 32 + tok) * WGN + (h0 - ntile * WGN)) = o;
         }
     }
   }
@@ -530,6 +592,36 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
 }
 
+// part[slot][h] of the tail tiles = sum over pieces p = 0, 1, ... in order of
+// tail_part[p][tile][row][col]; one float4 per thread and step.
+__global__ __launch_bounds__(256) void tail_reduce_kernel(TailReduceArgs a) {
+  const int total = *a.total_padded;
+  const int n_m = total / a.bmt;
+  const TailPlan pl = tail_plan(n_m * a.n_ntiles, a.resident, a.tail_split, a.nchunks);
+  if (pl.split < 2) return;
+  const int c4n = a.wgn / 4;
+  const int64_t items = (int64_t)pl.tail * a.bmt * c4n;
+  const size_t piece_stride = (size_t)pl.tail * a.bmt * a.wgn;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < items;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int c4 = (int)(i % c4n), r = (int)(i / c4n % a.bmt), ti = (int)(i / ((int64_t)c4n * a.bmt));
+    int mtile, ntile;
+    tile_coords(pl.n_full + ti, n_m, a.group_m, a.n_ntiles, mtile, ntile);
+    const int slot = a.sorted_slot[mtile * a.bmt + r];
+    if (slot >= a.S) continue;
+    const float* src = a.tail_part + ((size_t)ti * a.bmt + r) * a.wgn + c4 * 4;
+    float4 acc = *reinterpret_cast<const float4*>(src);
+    for (int p = 1; p < pl.split; ++p) {
+      const float4 v = *reinterpret_cast<const float4*>(src + p * piece_stride);
+      acc.x = acc.x + v.x;
+      acc.y = acc.y + v.y;
+      acc.z = acc.z + v.z;
+      acc.w = acc.w + v.w;
+    }
+    *reinterpret_cast<float4*>(a.part + (size_t)slot * a.N + ntile * a.wgn + c4 * 4) = acc;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: configuration choice and dispatch.
 
@@ -552,6 +644,7 @@ void set_pipeline(GemmCfg& c) {
   c.ck = c.ksplit == 1 && c.mt * c.nf >= 16 ? 64 : 128;
   c.nb = 3;
   c.wg_n = (4 / c.ksplit) * c.nf * 32;
+  c.tail_split = 0;
 }
 
 }  // namespace
@@ -595,6 +688,9 @@ GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
     }
   }
   set_pipeline(c);
+  // Prefill tiles are long (the whole reduction of 128 rows x 512 features):
+  // a partial last round is cut into pieces.
+  if (c.mt == 4 && c.nf == 4 && c.ksplit == 1 && c.kg == 1) c.tail_split = 8;
   return c;
 }
 
@@ -604,7 +700,8 @@ bool gemm_cfg_ok(int dt, int stage, const GemmCfg& c, int N, int K) {
   if (c.nf != 2 && !(c.nf == 4 && c.mt == 4 && c.ksplit == 1)) return false;
   if (N % c.wg_n) return false;
   if (kbytes % ((int64_t)c.ksplit * c.kg * c.ck)) return false;
-  if (stage == 1 && c.kg != 1) return false;
+  if (stage == 1 && (c.kg != 1 || c.tail_split != 0)) return false;
+  if (c.tail_split != 0 && (c.ksplit != 1 || c.kg != 1)) return false;
   if (c.nb != 3) return false;
   if (c.ksplit == 4) return c.mt == 1 && c.ck == 128;
   if (c.ksplit == 2) return c.mt <= 2 && c.ck == 128;
@@ -614,35 +711,79 @@ bool gemm_cfg_ok(int dt, int stage, const GemmCfg& c, int N, int K) {
 
 namespace {
 
+constexpr int kMaxDevices = 64;
+
+// Launches the kernel, or (resident != nullptr) only reports how many of its
+// workgroups the current device runs at once (taken once per device).
 template <int DT, int STAGE, int MT, int NF, int KSPLIT, int NB, int CK>
-hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
-  const int64_t blocks = (int64_t)a.n_mtiles * a.n_ntiles * a.kg;
+hipError_t launch_one(const GemmArgs& a, hipStream_t st, int* resident) {
+  if (resident) {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int r = cache[dev].load(std::memory_order_relaxed);
+    if (r == 0) {
+      int per_cu = 0, cus = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, gemm_kernel<DT, STAGE, MT, NF, KSPLIT, NB, CK>, 256, 0);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      r = per_cu * cus > 0 ? per_cu * cus : 1;
+      cache[dev].store(r, std::memory_order_relaxed);
+    }
+    *resident = r;
+    return hipSuccess;
+  }
+  int64_t blocks = (int64_t)a.n_mtiles * a.n_ntiles * a.kg;
+  // The tail pieces take the place of the tail tiles: at most min(resident,
+  // kTailPieces) more workgroups.
+  if (a.tail_split > 0) blocks += a.resident < kTailPieces ? a.resident : kTailPieces;
   hipLaunchKernelGGL((gemm_kernel<DT, STAGE, MT, NF, KSPLIT, NB, CK>), dim3((unsigned)blocks),
                      dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <int DT, int STAGE>
-hipError_t launch_dt_stage(const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
-  if (c.ksplit == 4) return launch_one<DT, STAGE, 1, 2, 4, 3, 128>(a, st);
+hipError_t launch_dt_stage(const GemmCfg& c, const GemmArgs& a, hipStream_t st, int* res) {
+  if (c.ksplit == 4) return launch_one<DT, STAGE, 1, 2, 4, 3, 128>(a, st, res);
   if (c.ksplit == 2)
-    return c.mt == 1 ? launch_one<DT, STAGE, 1, 2, 2, 3, 128>(a, st)
-                     : launch_one<DT, STAGE, 2, 2, 2, 3, 128>(a, st);
-  if (c.nf == 4) return launch_one<DT, STAGE, 4, 4, 1, 3, 64>(a, st);
+    return c.mt == 1 ? launch_one<DT, STAGE, 1, 2, 2, 3, 128>(a, st, res)
+                     : launch_one<DT, STAGE, 2, 2, 2, 3, 128>(a, st, res);
+  if (c.nf == 4) return launch_one<DT, STAGE, 4, 4, 1, 3, 64>(a, st, res);
   switch (c.mt) {
-    case 1: return launch_one<DT, STAGE, 1, 2, 1, 3, 128>(a, st);
-    case 2: return launch_one<DT, STAGE, 2, 2, 1, 3, 128>(a, st);
-    case 4: return launch_one<DT, STAGE, 4, 2, 1, 3, 64>(a, st);
+    case 1: return launch_one<DT, STAGE, 1, 2, 1, 3, 128>(a, st, res);
+    case 2: return launch_one<DT, STAGE, 2, 2, 1, 3, 128>(a, st, res);
+    case 4: return launch_one<DT, STAGE, 4, 2, 1, 3, 64>(a, st, res);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t dispatch(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipStream_t st,
+                    int* res) {
+  if (dt == 0)
+    return stage == 1 ? launch_dt_stage<0, 1>(c, a, st, res) : launch_dt_stage<0, 2>(c, a, st, res);
+  return stage == 1 ? launch_dt_stage<1, 1>(c, a, st, res) : launch_dt_stage<1, 2>(c, a, st, res);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipStream_t st) {
   if (!gemm_cfg_ok(dt, stage, c, a.N, a.K_bytes / (dt == 0 ? 2 : 1))) return hipErrorInvalidValue;
-  if (dt == 0) return stage == 1 ? launch_dt_stage<0, 1>(c, a, st) : launch_dt_stage<0, 2>(c, a, st);
-  return stage == 1 ? launch_dt_stage<1, 1>(c, a, st) : launch_dt_stage<1, 2>(c, a, st);
+  if (c.tail_split != a.tail_split || (a.tail_split > 0 && (a.resident < 1 || !a.tail_part)))
+    return hipErrorInvalidValue;
+  return dispatch(dt, stage, c, a, st, nullptr);
+}
+
+int gemm_resident(int dt, int stage, const GemmCfg& c) {
+  int r = 0;
+  return dispatch(dt, stage, c, GemmArgs{}, 0, &r) == hipSuccess ? r : -1;
+}
+
+hipError_t launch_tail_reduce(const TailReduceArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3(1024), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_act(const QuantArgs& a, hipStream_t st) {

@@ -51,7 +51,14 @@ struct GemmCfg {
   int nb;      // weight pipeline depth (register stages)
   int ck;      // reduction bytes per pipeline stage (64 or 128)
   int wg_n;    // features (composite rows) per workgroup = (4 / ksplit) * nf * 32
+  int tail_split;  // stage 2: most pieces a tile of the last, partial round is cut into (0: off)
 };
+
+// Tiles of a partial last round of a stage-2 launch are cut along the
+// reduction into pieces, so that the round fills the device; the pieces'
+// partials are summed in piece order by tail_reduce. At most kTailPieces
+// pieces per launch (workspace).
+constexpr int kTailPieces = 256;
 GemmCfg stage1_cfg(int dt, int T, int k, int E, int H, int I, int bm);
 GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm);
 // Whether a configuration can run a stage with N output features and reduction length K.
@@ -74,8 +81,24 @@ struct GemmArgs {
   int n_mtiles, n_ntiles;  // row tiles (32*mt rows) and feature tiles (wg_n rows)
   int kg, group_m;         // reduction split over workgroups; M-tiles per schedule group
   uint64_t k_magic;        // ceil(2^35 / k): slot / k as a multiply
+  float* tail_part;        // stage 2 tail pieces: [kTailPieces][32*mt][wg_n] (tail_split > 0)
+  int resident;            // workgroups of this kernel the device runs at once
+  int tail_split;          // GemmCfg::tail_split
 };
 hipError_t launch_gemm(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipStream_t st);
+// Workgroups of the configuration's kernel that the current device runs at once.
+int gemm_resident(int dt, int stage, const GemmCfg& c);
+
+// Sum of the tail pieces of a stage-2 launch, in piece order, into the per-slot
+// partials (the same tile plan as the GEMM, from the device-side total).
+struct TailReduceArgs {
+  const float* tail_part;
+  const int32_t* sorted_slot;
+  const int32_t* total_padded;
+  float* part;             // [T*k][N]
+  int S, N, bmt, wgn, n_ntiles, group_m, resident, tail_split, nchunks;
+};
+hipError_t launch_tail_reduce(const TailReduceArgs& a, hipStream_t st);
 
 // FP8 stage 2 prologue: per-row amax from the partials, scale, requantise.
 struct QuantArgs {

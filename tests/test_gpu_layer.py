@@ -89,6 +89,28 @@ def test_stages_match_oracle(dtype, T, H, I, E, k, bm):
     assert e2 <= TOL[dtype]
 
 
+def test_stage2_tail_round_in_pieces():
+    # 4096 features (8 workgroup tiles of 512) and ~38 row tiles of 128: about
+    # 300 stage-2 tiles, so with 256 workgroups per round the last round's
+    # tiles (the last schedule group) run cut into pieces along the reduction
+    # and are summed by the tail reduction; the other tiles run whole.
+    T, H, I = 2200, 4096, 512
+    inp = make("fp8", T, H, I, 8, 2, seed=11, sigma_w=0.02)
+    say(f"stage-2 tail pieces: fp8 T={T} H={H} I={I}")
+    r = run_stages(inp, 128)
+    o = oracle.align(r["ids"], 8, 128)
+    ss = o["sorted_slot"]
+    n_m = o["total"] // 128
+    last_group = ss[max(0, n_m - 16) * 128:]
+    tail_toks = np.unique(last_group[last_group < T * 2] // 2)
+    rng = np.random.default_rng(1)
+    toks = np.unique(np.concatenate([tail_toks, rng.choice(T, 48, replace=False)])).astype(np.int32)
+    _, o64 = oracle.forward(inp, toks)
+    err = rel_err(r["out"][toks], o64)
+    say(f"  {toks.size} tokens ({tail_toks.size} in the last group): rel err {err:.3e}")
+    assert err <= TOL["fp8"]
+
+
 def test_skew_everything_to_one_pair():
     inp = make("fp8", 64, 256, 512, 8, 2, bias=[0, 0, 0, 0, 0, 50.0, 0, 60.0])
     r = run_stages(inp, 32)
