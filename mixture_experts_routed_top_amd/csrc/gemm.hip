@@ -160,8 +160,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // Token buffers (reused by the epilogue), then the column scales of this
   // workgroup's features (FP8), staged once so that the epilogue reads LDS.
   constexpr int SCL = DT == 1 ? WGN : 0;
-  __shared__ __align__(16) uint8_t lds[LDS + SCL * 4];
-  float* const scl = reinterpret_cast<float*>(lds + LDS);
+  // Stage 1 stages its bf16 output tile here after the main loop (rows of
+  // WGN/2 columns, padded by 8 bytes so that the 32 rows one write covers
+  // fall in different banks), reusing the token buffers, and keeps the row
+  // maxima of the FP8 epilogue past it.
+  constexpr int SP = WGN + 8;                               // staging row pitch, bytes
+  constexpr int STG = STAGE == 1 ? BMT * SP : 0;
+  constexpr int LDSX = (LDS > STG ? LDS : STG) + (STAGE == 1 && DT == 1 ? WN * BMT * 4 : 0);
+  __shared__ __align__(16) uint8_t lds[LDSX + SCL * 4];
+  float* const scl = reinterpret_cast<float*>(lds + LDSX);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wk = wave / WN;
@@ -450,7 +457,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     for (int m = 0; m < MT; ++m) {
       amax[m] = 0.0f;
       if (wk != 0) continue;
-      const int p = row0 + m * 32 + tok;
       const float xs = rslot[m] < S ? rsc[m] : 0.0f;  // pad rows: act = 0
 #pragma unroll
       for (int qg = 0; qg < NF / 2 * 4; ++qg) {
@@ -474,14 +480,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         // magnitudes is the rounded maximum of these: rounded once, below.
         amax[m] = fmaxf(amax[m],
                         fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3]))));
-        *reinterpret_cast<uint2*>(act + (size_t)p * a.I + i0) =
+        *reinterpret_cast<uint2*>(lds + (m * 32 + tok) * SP + (i0 - col0) * 2) =
             make_uint2(f32x2_to_bf16x2(h[0], h[1]), f32x2_to_bf16x2(h[2], h[3]));
+      }
+    }
+    // The tile leaves in whole row segments of WGN bytes: each wave store
+    // covers 64 x 16 contiguous-per-row bytes, full cache lines, written
+    // non-temporally (the intermediate is read back only by the next step).
+    __syncthreads();
+    {
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      constexpr int CPR = WGN / 16;  // 16-byte chunks per row
+#pragma unroll
+      for (int i = tid; i < BMT * CPR; i += 256) {
+        const int r = i / CPR, c = i % CPR;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + r * SP + c * 16);
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4_t*>(act + (size_t)(row0 + r) * a.I + col0 + c * 8));
       }
     }
     if constexpr (DT == 1) {
       // Partial row maxima over this workgroup's columns: lane halves, then waves.
-      float* wmax = reinterpret_cast<float*>(lds);
-      if constexpr (KSPLIT == 1) __syncthreads();  // LDS reuse after the main loop's last reads
+      float* wmax = reinterpret_cast<float*>(lds + (LDS > STG ? LDS : STG));
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const float v = fmaxf(amax[m], __shfl_xor(amax[m], 32, 64));
