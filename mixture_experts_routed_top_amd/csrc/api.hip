@@ -221,6 +221,7 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, c
   a.kg = 1;
   a.group_m = group_m(c.mt);
   a.k_magic = k_magic(k);
+  a.live_order = c.mt * c.nf < 16;
   return hip_status(moe::launch_gemm(dt, 1, c, a, stream), "moe_stage1 launch");
 }
 
@@ -302,6 +303,7 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
   a.group_m = group_m(c.mt);
   a.k_magic = k_magic(k);
   a.tail_split = c.tail_split;
+  a.live_order = c.mt * c.nf < 16;
   if (c.tail_split > 0) {
     a.tail_part = (float*)ws;
     a.resident = moe::gemm_resident(dt, 2, c);

@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   int kg = 0, mtile, ntile, total, e_raw;
   int piece = -1, tail_idx = 0, n_tail = 0;  // stage-2 tail piece of this workgroup
   int cbegin = 0;                            // first reduction chunk
-  if (a.tail_split == 0) {
+  if (a.tail_split == 0 && !a.live_order) {
     const int logical = xcd_remap(blockIdx.x, a.n_mtiles * a.n_ntiles * a.kg);
     kg = logical % a.kg;
     tile_coords(logical / a.kg, a.n_mtiles, a.group_m, a.n_ntiles, mtile, ntile);
@@ -194,11 +194,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     e_raw = a.tile_expert[mtile * BMT / a.bm];
     if (mtile * BMT >= total) return;
   } else {
-    // Live tiles only (the padded total is a multiple of the tile rows); the
-    // partial last round's tiles are cut into pieces along the reduction.
+    // Live tiles only, first in launch order (the padded total is a multiple
+    // of the tile rows). With few live row tiles (decode), a launch over the
+    // capacity would interleave them with exiting workgroups in a fixed
+    // pattern that the hardware's round-robin placement maps onto a subset of
+    // the CUs. Stage 2 also cuts the partial last round's tiles into pieces
+    // along the reduction (kg is 1 then).
     total = *a.total_padded;
     const int n_m = total / BMT;
-    const TailPlan pl = tail_plan(n_m * a.n_ntiles, a.resident, a.tail_split, nchunks);
+    const TailPlan pl = tail_plan(n_m * a.n_ntiles * a.kg, a.resident, a.tail_split, nchunks);
     const int b = blockIdx.x;
     int logical;
     if (b < pl.n_full) {
@@ -213,7 +217,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       cbegin = piece * nchunks / pl.split;
       nchunks = (piece + 1) * nchunks / pl.split - cbegin;
     }
-    tile_coords(logical, n_m, a.group_m, a.n_ntiles, mtile, ntile);
+    kg = logical % a.kg;
+    tile_coords(logical / a.kg, n_m, a.group_m, a.n_ntiles, mtile, ntile);
     e_raw = a.tile_expert[mtile * BMT / a.bm];
   }
   const int row0 = mtile * BMT;

@@ -84,6 +84,7 @@ struct GemmArgs {
   float* tail_part;        // stage 2 tail pieces: [kTailPieces][32*mt][wg_n] (tail_split > 0)
   int resident;            // workgroups of this kernel the device runs at once
   int tail_split;          // GemmCfg::tail_split
+  int live_order;          // index the live tiles first (decode shapes) instead of the capacity
 };
 hipError_t launch_gemm(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipStream_t st);
 // Workgroups of the configuration's kernel that the current device runs at once.
