@@ -15,6 +15,7 @@ The same line carries:
   decode_sweep  the FP8 decode batches T = 1, 4, 16, 64, 256: latency,
                 tokens/s, and weight-read bandwidth over the active experts'
                 weight bytes against 8 TB/s;
+  bf16_decode   the same for the BF16 decode batch T=16;
   cpu_baseline  the CPU oracle on the first tokens of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-sweep]
@@ -124,6 +125,36 @@ def decode_sweep(steps):
     del layer
     torch.cuda.empty_cache()
     return out
+
+
+def bf16_decode(steps):
+    """The BF16 decode batch (Mixtral shape, T=16): latency and weight-read bandwidth."""
+    import torch
+    import workloads
+    wl = workloads.config(1)
+    inp = workloads.generate(wl, threads=16)
+    layer = make_layer(inp)
+    x = dev(inp.x)
+    for _ in range(5):
+        layer(x)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        layer(x)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    active = int(torch.unique(layer.ids).numel())
+    wbytes = active * 3 * wl.H * wl.I * 2  # bf16 weights of the experts that get a slot
+    gbps = wbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] bf16 decode T={wl.T}: {ms * 1e3:.1f} us, {gbps:.0f} GB/s over {active} experts")
+    del layer
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "T": wl.T, "ms": round(ms, 4),
+            "tokens_per_s": round(wl.T / (ms * 1e-3), 1), "active_experts": active,
+            "weight_gbps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK, 4)}
 
 
 def traffic_from(fetch_db, write_db):
@@ -253,6 +284,7 @@ def main():
     }
     if not args.no_sweep:
         rec["decode_sweep"] = decode_sweep(max(10, args.steps))
+        rec["bf16_decode"] = bf16_decode(max(10, args.steps))
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)

@@ -38,7 +38,10 @@ def check(ids, E, bm):
 @pytest.mark.parametrize("T,k,E,bm", [(32, 2, 8, 32), (1, 2, 8, 32), (16, 2, 8, 32),
                                       (8192, 2, 8, 128), (8192, 2, 8, 256), (16384, 2, 8, 256),
                                       (257, 3, 64, 64), (1000, 1, 4, 32), (2049, 8, 8, 32),
-                                      (64, 2, 8, 128)])
+                                      (64, 2, 8, 128),
+                                      # around the one-wave path's limit of 2048 slots
+                                      (1024, 2, 8, 32), (2049, 1, 8, 64), (32, 2, 64, 32),
+                                      (33, 1, 1, 256), (65, 1, 8, 32)])
 def test_align_uniform(T, k, E, bm):
     check(ids_for(T, k, E, T + bm), E, bm)
 
