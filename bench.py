@@ -12,14 +12,18 @@ The same line carries:
                 with HIP events on the stream it runs on; traffic = HBM bytes
                 per launch from the committed counter summary (null if the
                 kernel source changed since);
-  decode_sweep  the FP8 decode batches T = 1, 4, 16, 64, 256: latency,
-                tokens/s, and weight-read bandwidth over the active experts'
-                weight bytes against 8 TB/s;
+  decode_sweep  the FP8 decode batches T = 1, 4, 16, 64, 256: median latency of
+                100 single calls (HIP events around each call; a 512 MB buffer is
+                rewritten before each call, untimed, so the Infinity Cache holds
+                no weights from the previous one), tokens/s, and weight-read
+                bandwidth over the active experts' weight bytes against 8 TB/s;
   bf16_decode   the same for the BF16 decode batch T=16;
   cpu_baseline  the CPU oracle on the first tokens of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-sweep]
                     [--no-cpu-baseline] [--cpu-tokens 64] [--copy-calibration]
+                    [--decode-runs 100]
+    python bench.py --decode-only T [--decode-runs N]   (one FP8 decode batch)
     python bench.py --traffic-from FETCH.db WRITE.db   (writes the traffic summary)
 """
 from __future__ import annotations
@@ -92,69 +96,86 @@ def cpu_baseline(inp, n_tokens):
                       f"flops 6*H*I per token-slot"}
 
 
-def decode_sweep(steps):
-    """FP8 decode batches: per-T latency of the whole layer, tokens/s, weight GB/s."""
+def timed_calls(layer, x, runs, flush):
+    """Median and mean latency (ms) of `runs` single layer calls, each bracketed by HIP
+    events on the current stream, with the flush buffer rewritten (untimed) before each call
+    so that no weights survive in the 256 MB Infinity Cache from the previous call."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(runs)]
+    for i in range(runs):
+        flush.fill_(i & 0x7F)
+        ev[i][0].record()
+        layer(x)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return float(np.median(ms)), float(ms.mean())
+
+
+def decode_line(wl, layer, x, runs, flush, bytes_per_weight):
+    import torch
+    for _ in range(5):
+        layer(x)
+    torch.cuda.synchronize()
+    med, mean = timed_calls(layer, x, runs, flush)
+    active = int(torch.unique(layer.ids).numel())
+    wbytes = active * 3 * wl.H * wl.I * bytes_per_weight  # weights of the experts that get a slot
+    gbps = wbytes / (med * 1e-3) / 1e9
+    log(f"[bench] {wl.name}: median {med * 1e3:.1f} us, {gbps:.0f} GB/s over {active} experts")
+    return {"T": wl.T, "ms": round(med, 4), "ms_mean": round(mean, 4),
+            "tokens_per_s": round(wl.T / (med * 1e-3), 1), "active_experts": active,
+            "weight_gbps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK, 4),
+            "tflops": round(wl.flops() / (med * 1e-3) / 1e12, 2)}
+
+
+def calibration_copy():
+    """One 1 GiB device-to-device copy: the reference reading for the byte counters."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def flush_buffer():
+    import torch
+    return torch.empty(512 << 20, dtype=torch.uint8, device="cuda")  # 2x the Infinity Cache
+
+
+def decode_sweep(runs):
+    """FP8 decode batches: per-T median latency of the whole layer over `runs` calls with
+    the Infinity Cache flushed between calls, tokens/s, weight GB/s."""
     import torch
     import workloads
     base = workloads.generate(workloads.config(3, workloads.DECODE_SWEEP[0]), threads=16)
     layer = make_layer(base)
+    flush = flush_buffer()
     torch.cuda.synchronize()
     out = []
     for T in workloads.DECODE_SWEEP:
         wl = workloads.config(3, T)
         x = dev(workloads.generate(wl, weights=False).x)
-        for _ in range(5):
-            layer(x)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(steps):
-            layer(x)
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / steps
-        active = int(torch.unique(layer.ids).numel())
-        wbytes = active * 3 * wl.H * wl.I  # e4m3fn weights of the experts that get a slot
-        gbps = wbytes / (ms * 1e-3) / 1e9
-        out.append({"T": T, "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
-                    "active_experts": active, "weight_gbps": round(gbps, 1),
-                    "frac_hbm": round(gbps / HBM_PEAK, 4),
-                    "tflops": round(wl.flops() / (ms * 1e-3) / 1e12, 2)})
-        log(f"[bench] decode T={T}: {ms * 1e3:.1f} us, {gbps:.0f} GB/s over {active} experts")
-    del layer
+        out.append(decode_line(wl, layer, x, runs, flush, 1))
+    del layer, flush
     torch.cuda.empty_cache()
     return out
 
 
-def bf16_decode(steps):
-    """The BF16 decode batch (Mixtral shape, T=16): latency and weight-read bandwidth."""
+def bf16_decode(runs):
+    """The BF16 decode batch (Mixtral shape, T=16), measured like the FP8 sweep."""
     import torch
     import workloads
     wl = workloads.config(1)
     inp = workloads.generate(wl, threads=16)
     layer = make_layer(inp)
-    x = dev(inp.x)
-    for _ in range(5):
-        layer(x)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
-        layer(x)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    active = int(torch.unique(layer.ids).numel())
-    wbytes = active * 3 * wl.H * wl.I * 2  # bf16 weights of the experts that get a slot
-    gbps = wbytes / (ms * 1e-3) / 1e9
-    log(f"[bench] bf16 decode T={wl.T}: {ms * 1e3:.1f} us, {gbps:.0f} GB/s over {active} experts")
-    del layer
+    flush = flush_buffer()
+    rec = decode_line(wl, layer, dev(inp.x), runs, flush, 2)
+    rec = {"workload": wl.name, **rec}
+    del layer, flush
     torch.cuda.empty_cache()
-    return {"workload": wl.name, "T": wl.T, "ms": round(ms, 4),
-            "tokens_per_s": round(wl.T / (ms * 1e-3), 1), "active_experts": active,
-            "weight_gbps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK, 4)}
+    return rec
 
 
 def traffic_from(fetch_db, write_db):
@@ -194,6 +215,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--decode-runs", type=int, default=100,
+                    help="single calls per decode batch (median reported)")
+    ap.add_argument("--decode-only", type=int, metavar="T", default=None,
+                    help="only time the FP8 decode batch T (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -210,6 +235,16 @@ def main():
 
     import torch
     import workloads
+
+    if args.decode_only is not None:
+        wl = workloads.config(3, args.decode_only)
+        inp = workloads.generate(wl, threads=16)
+        layer = make_layer(inp)
+        print(json.dumps({"decode": decode_line(wl, layer, dev(inp.x), args.decode_runs,
+                                                flush_buffer(), 1)}), flush=True)
+        if args.copy_calibration:
+            calibration_copy()
+        return
 
     wl = workloads.config(2)
     log(f"[bench] generating {wl.name}")
@@ -250,11 +285,7 @@ def main():
             traffic = t.get("bytes_per_launch")
 
     if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        calibration_copy()
     del layer
     torch.cuda.empty_cache()
 
@@ -283,8 +314,8 @@ def main():
                      "avg_launch_ms": round(s1_ms, 4)},
     }
     if not args.no_sweep:
-        rec["decode_sweep"] = decode_sweep(max(10, args.steps))
-        rec["bf16_decode"] = bf16_decode(max(10, args.steps))
+        rec["decode_sweep"] = decode_sweep(args.decode_runs)
+        rec["bf16_decode"] = bf16_decode(args.decode_runs)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
