@@ -241,6 +241,25 @@ class Layer:
         return self.out
 
 
+    def capture(self, x: torch.Tensor):
+        """Capture one layer call on `x` in a HIP graph (torch.cuda.CUDAGraph) and return it.
+        `x`'s memory is the graph's input and self.out its output: copy the next batch of
+        tokens into x, then graph.replay(). The sequence has no memsets and no host
+        synchronisation; every buffer is allocated here, before the capture."""
+        T = x.shape[0]
+        if T != self.T:
+            self._alloc(T)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self(x)  # first call outside the capture (per-device launch queries)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self(x)
+        return graph
+
+
 def forward(dtype, x, w_router, w1, w3, w2, s1=None, s3=None, s2=None, bias=None, k=2,
             block_m=None):
     """One-shot layer call (preshuffles the weights each time; use Layer for repeated calls)."""

@@ -1,0 +1,47 @@
+"""The layer captured in a HIP graph: every replay, with eager work and host
+synchronisations between replays, equals the eager call on the same tokens,
+bit for bit (decode-size FP8, and a BF16 shape whose stage 2 cuts its last
+round into reduction pieces)."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routed_top_amd as moe
+import workloads
+from gpu_util import dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def make(dtype, T, H, I, E, k, seed):
+    wl = workloads.Workload(f"graph-{dtype}", T, H, I, E, k, dtype, 1.0, 1.0 / np.sqrt(H), 0.05,
+                            seed)
+    return workloads.generate(wl)
+
+
+@pytest.mark.parametrize("dtype,T,H,I,E,k,bm", [
+    ("fp8", 16, 1024, 1024, 8, 2, 32),     # decode shape: split reductions, one-wave align
+    ("bf16", 700, 512, 768, 8, 2, 256),    # stage 2 tail pieces and their reduction
+])
+def test_graph_replays_match_eager(dtype, T, H, I, E, k, bm):
+    inp = make(dtype, T, H, I, E, k, seed=T)
+    say(f"graph {dtype} T={T} H={H} I={I} bm={bm}")
+    layer = moe.Layer(dtype, dev(inp.w_router), dev(inp.w1), dev(inp.w3), dev(inp.w2),
+                      dev(inp.s1), dev(inp.s3), dev(inp.s2), None, k, T, bm)
+    x = dev(inp.x)
+    graph = layer.capture(x)
+    rng = np.random.default_rng(7)
+    for rep in range(4):
+        # a new batch of tokens: eager reference first, then the replay on the same memory
+        xb = (rng.standard_normal((T, H)).astype(np.float32) *
+              (1.0 + rep)).astype(np.float32)
+        new = dev(workloads.to_bf16_bits(xb))
+        ref = host(moe.Layer.__call__(layer, new)).copy()
+        torch.cuda.synchronize()
+        x.copy_(new)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host(layer.out)
+        assert np.array_equal(got, ref), f"replay {rep} differs from the eager call"
+        # eager work of the program's own between replays
+        _ = (new.float() * 2).sum().item()
