@@ -18,6 +18,8 @@ The same line carries:
                 no weights from the previous one), tokens/s, and weight-read
                 bandwidth over the active experts' weight bytes against 8 TB/s;
   bf16_decode   the same for the BF16 decode batch T=16;
+  skewed        the FP8 skewed workload (T=16384, ~40% of slots on expert 0):
+                latency, effective TFLOP/s, slots and row tiles per expert, pad rows;
   cpu_baseline  the CPU oracle on the first tokens of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-sweep]
@@ -178,6 +180,43 @@ def bf16_decode(runs):
     return rec
 
 
+def skewed(steps):
+    """The skewed FP8 workload (T=16384, ~40% of slots on expert 0): latency, effective
+    TFLOP/s, and what the skew does to the grouping (slots and row tiles per expert, pad rows)."""
+    import torch
+    import workloads
+    wl = workloads.config(4)
+    inp = workloads.generate(wl, threads=16)
+    layer = make_layer(inp)
+    x = dev(inp.x)
+    for _ in range(3):
+        layer(x)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        layer(x)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    count = layer.grp.count.cpu().numpy().astype(int)
+    total = int(layer.grp.total.cpu().numpy()[0])
+    bm = layer.bm
+    tiles = [int(-(-c // bm)) for c in count]
+    tf = wl.flops() / (ms * 1e-3) / 1e12
+    log(f"[bench] {wl.name}: {ms:.3f} ms, {tf:.0f} TFLOP/s, expert slots {count.tolist()}")
+    del layer
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "T": wl.T, "ms": round(ms, 4), "tflops": round(tf, 2),
+            "frac_of_fp8_peak": round(tf / PEAK["fp8"], 4),
+            "tokens_per_s": round(wl.T / (ms * 1e-3), 1), "block_m": bm,
+            "expert_slots": count.tolist(),
+            "expert_share": [round(c / wl.slots, 4) for c in count],
+            "expert_row_tiles": tiles, "padded_rows": total,
+            "pad_fraction": round((total - wl.slots) / total, 4)}
+
+
 def traffic_from(fetch_db, write_db):
     """Stage-1 HBM bytes per launch from two rocprofv3 --pmc databases (FETCH_SIZE,
     WRITE_SIZE, in KiB per dispatch), each scaled by the same counter's reading for the
@@ -316,6 +355,7 @@ def main():
     if not args.no_sweep:
         rec["decode_sweep"] = decode_sweep(args.decode_runs)
         rec["bf16_decode"] = bf16_decode(args.decode_runs)
+        rec["skewed"] = skewed(max(5, args.steps // 2))
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)

@@ -50,7 +50,7 @@ def test_mixtral_bf16_decode_T16():
 
 
 def test_mixtral_fp8_prefill_T8192():
-    check_full(workloads.config(2), 12)
+    check_full(workloads.config(2), 48)
 
 
 def test_mixtral_fp8_decode_sweep():
@@ -68,4 +68,4 @@ def test_mixtral_fp8_decode_sweep():
 
 
 def test_mixtral_fp8_skewed_T16384():
-    check_full(workloads.config(4), 12)
+    check_full(workloads.config(4), 48)
