@@ -2,7 +2,8 @@
 // sort (the "dynamic expert sizes" of the routed MoE GEMM in the FlyDSL-in-JAX
 // talk summary, 5:56).
 //
-// One workgroup of 1024 threads (16 waves). Every thread first loads its ids
+// Three shapes by size. The general one: one workgroup of 1024 threads (16
+// waves). Every thread first loads its ids
 // for all 1024-slot chunks (thread t holds slot c*1024 + t of chunk c), so the
 // loads are in flight together. Pass 1 counts slots per expert with wave
 // ballots, one LDS integer atomic per wave and expert (order free). One
@@ -220,9 +221,130 @@ __global__ __launch_bounds__(64) void align_small_kernel(AlignArgs a) {
   }
 }
 
+// Prefill-size groupings with few experts (S <= kRunSlots * 1024, E <= 16):
+// thread t owns a contiguous run of slots, so one block-wide scan replaces the
+// per-chunk ballots. The ids go through LDS as bytes (coalesced loads, then
+// each thread reads its run); a thread counts its run in packed 16-bit
+// counters (expert e in half e%2 of word e/2: counts stay below 2^16 since
+// S <= 32768); an exclusive scan of those words over the threads gives every
+// thread, for every expert, the number of earlier slots; its slots then go to
+// offset[e] + that number + the rank inside its run, in ascending order, which
+// is the stable order.
+constexpr int kRunSlots = 32;                     // slots per thread at most
+constexpr int kRunMaxSlots = kRunSlots * kAlignThreads;
+constexpr int kRunWords = 8;                      // packed counter words (E <= 16)
+
+__global__ __launch_bounds__(kAlignThreads) void align_runs_kernel(AlignArgs a) {
+  __shared__ __align__(16) uint8_t ids8[kRunMaxSlots];
+  __shared__ uint32_t wtot[kAlignWaves][kRunWords];  // per-wave totals, then wave prefixes
+  __shared__ int cnt[2 * kRunWords];
+  __shared__ int off[2 * kRunWords + 1];
+  __shared__ int bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.S, E = a.E, bm = a.bm;
+  const int nchunks = (S + kAlignThreads - 1) / kAlignThreads;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  {
+    bool anybad = false;
+#pragma unroll
+    for (int i = 0; i < kRunSlots; ++i) {
+      const int s = i * kAlignThreads + tid;  // clamped load, then select: no branches
+      const int v = a.ids[min(s, S - 1)];
+      if (i < nchunks && s < S) {
+        anybad |= v < 0 || v >= E;
+        ids8[s] = (uint8_t)v;
+      }
+    }
+    if (anybad) bad = 1;
+  }
+  __syncthreads();
+  if (bad) {  // invalid ids: an empty grouping, nothing downstream runs
+    if (tid == 0) *a.total = 0;
+    return;
+  }
+  // This thread's run: slots [r0, r0 + n4) clipped to S, n4 a multiple of 4.
+  const int n4 = ((nchunks + 3) / 4) * 4;
+  const int r0 = tid * n4;
+  uint32_t cntw[kRunWords];
+#pragma unroll
+  for (int w = 0; w < kRunWords; ++w) cntw[w] = 0;
+  auto run_id = [&](int i) { return (int)ids8[r0 + i]; };
+  for (int i = 0; i < n4; ++i) {
+    if (r0 + i >= S) break;
+    const int e = run_id(i);
+    const uint32_t inc = (e & 1) ? 0x10000u : 1u;
+#pragma unroll
+    for (int w = 0; w < kRunWords; ++w) cntw[w] += (e >> 1) == w ? inc : 0u;
+  }
+  // Exclusive scan of the packed words over the threads (thread order = slot
+  // order): inside each wave with shuffles, then over the 16 wave totals.
+  uint32_t excl[kRunWords];
+#pragma unroll
+  for (int w = 0; w < kRunWords; ++w) {
+    uint32_t x = cntw[w];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(x, d, 64);
+      if (lane >= d) x += o;
+    }
+    excl[w] = x - cntw[w];
+    if (lane == 63) wtot[wave][w] = x;
+  }
+  __syncthreads();
+  if (tid < kRunWords) {  // wave prefixes in place, and the expert counts from the grand total
+    uint32_t acc = 0;
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const uint32_t t = wtot[w][tid];
+      wtot[w][tid] = acc;
+      acc += t;
+    }
+    cnt[2 * tid] = (int)(acc & 0xffffu);
+    cnt[2 * tid + 1] = (int)(acc >> 16);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kRunWords; ++w) excl[w] += wtot[wave][w];
+  if (tid == 0) {  // padded offsets
+    int pos = 0;
+    for (int e = 0; e < E; ++e) {
+      off[e] = pos;
+      pos += (cnt[e] + bm - 1) / bm * bm;
+    }
+    off[E] = pos;
+    *a.total = pos;
+  }
+  __syncthreads();
+  if (tid < E) a.count[tid] = cnt[tid];
+  if (tid <= E) a.offset[tid] = off[tid];
+  // Tile experts and pad sentinels (fewer than block_m pad rows per expert).
+  for (int e = 0; e < E; ++e) {
+    const int o0 = off[e], o1 = off[e + 1];
+    for (int i = o0 / bm + tid; i < o1 / bm; i += kAlignThreads) a.tile_expert[i] = e;
+    const int p = o0 + cnt[e] + tid;
+    if (p < o1) a.sorted_slot[p] = S;
+  }
+  // Stable scatter of this thread's run.
+  for (int i = 0; i < n4; ++i) {
+    const int s = r0 + i;
+    if (s >= S) break;
+    const int e = run_id(i);
+    uint32_t word = 0;
+#pragma unroll
+    for (int w = 0; w < kRunWords; ++w) word = (e >> 1) == w ? excl[w] : word;
+    const int rank = (int)((e & 1) ? (word >> 16) : (word & 0xffffu));
+    a.sorted_slot[off[e] + rank] = s;
+    const uint32_t inc = (e & 1) ? 0x10000u : 1u;
+#pragma unroll
+    for (int w = 0; w < kRunWords; ++w) excl[w] += (e >> 1) == w ? inc : 0u;
+  }
+}
+
 hipError_t launch_align(const AlignArgs& a, hipStream_t st) {
   if (a.S <= kSmallSlots)
     hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(64), 0, st, a);
+  else if (a.S <= kRunMaxSlots && a.E <= 2 * kRunWords)
+    hipLaunchKernelGGL(align_runs_kernel, dim3(1), dim3(kAlignThreads), 0, st, a);
   else
     hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, st, a);
   return hipGetLastError();

@@ -41,7 +41,11 @@ def check(ids, E, bm):
                                       (64, 2, 8, 128),
                                       # around the one-wave path's limit of 2048 slots
                                       (1024, 2, 8, 32), (2049, 1, 8, 64), (32, 2, 64, 32),
-                                      (33, 1, 1, 256), (65, 1, 8, 32)])
+                                      (33, 1, 1, 256), (65, 1, 8, 32),
+                                      # the per-thread-run path (2048 < S <= 32768, E <= 16)
+                                      # and the chunked path beyond it
+                                      (1025, 2, 16, 64), (3000, 2, 64, 64),
+                                      (20000, 2, 8, 128)])
 def test_align_uniform(T, k, E, bm):
     check(ids_for(T, k, E, T + bm), E, bm)
 
