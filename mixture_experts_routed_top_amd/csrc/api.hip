@@ -40,7 +40,11 @@ bool valid_bm(int bm) { return bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 uint64_t k_magic(int k) { return (((uint64_t)1 << 35) + k - 1) / k; }
 
 // M-tiles per scheduling group: about 2048 rows, one expert's share at prefill.
-int group_m(int mt) { return 2048 / (32 * mt); }
+// Row tiles per schedule group: 2048 rows, so that the tiles sharing an
+// expert's weights run together; decode tiles (32 rows, about one per
+// expert) run one at a time, so that the workgroups of an XCD stream
+// consecutive feature tiles of one expert (contiguous weights).
+int group_m(int mt) { return mt == 1 ? 1 : 2048 / (32 * mt); }
 
 int64_t capacity(int T, int k, int E, int bm) {
   int64_t n = (int64_t)T * k + (int64_t)E * (bm - 1);
