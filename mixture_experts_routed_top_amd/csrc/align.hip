@@ -1,18 +1,19 @@
 // Grouping of token-slots by expert, padded to the M-tile: a stable counting
 // sort (the "dynamic expert sizes" of the routed MoE GEMM in the FlyDSL-in-JAX
-// talk summary, 5:56).
-//
-// Three shapes by size. The general one: one workgroup of 1024 threads (16
-// waves). Every thread first loads its ids
-// for all 1024-slot chunks (thread t holds slot c*1024 + t of chunk c), so the
-// loads are in flight together. Pass 1 counts slots per expert with wave
-// ballots, one LDS integer atomic per wave and expert (order free). One
-// thread turns the padded counts into
-// offsets. Pass 2 walks the chunks in ascending order: inside a chunk a slot's
-// rank among equal experts is a wave ballot (lanes are in ascending slot
-// order) plus the counts of the lower waves, which one lane per (expert, wave)
-// pair obtains with a 16-lane shuffle scan; so the result is exactly the
-// stable order. Integer work only: bit-exact by construction.
+// talk summary, 5:56). Integer work only: bit-exact by construction. Three
+// kernels by size, each one workgroup:
+//  - align_small_kernel (S <= 2048 slots, decode): one wave, ids in registers,
+//    counts and ranks from ballots, offsets from a shuffle scan;
+//  - align_runs_kernel (S <= 32768, E <= 16): each thread takes a contiguous
+//    run of slots and counts it in packed 16-bit counters; one exclusive scan
+//    of those over the 1024 threads gives every slot its stable rank;
+//  - align_kernel (the rest): 1024 threads, slot c*1024 + t of each 1024-slot
+//    chunk c on thread t. Pass 1 counts slots per expert with wave ballots (one
+//    LDS integer atomic per wave and expert). Pass 2 walks the chunks in
+//    ascending order: inside a chunk a slot's rank among equal experts is a
+//    wave ballot (lanes are in ascending slot order) plus the counts of the
+//    lower waves, which one lane per (expert, wave) pair obtains with a 16-lane
+//    shuffle scan; so the result is exactly the stable order.
 #include "moe_device.h"
 #include "moe_launch.h"
 

@@ -12,16 +12,24 @@
 // starting at (l/32)*32, held as two 16-byte pieces; accumulator register i of
 // lane l is then output feature 8*(i/4) + 4*(l/32) + i%4 of token l%32.
 //
-// Workgroup = 4 waves. Each wave owns two weight fragments along the features
-// (64 rows: for stage 1 one gate block and the matching up block, so the SwiGLU
-// pairs sit in the same lane) and all MT token fragments of the tile; KSPLIT
-// waves may split the reduction instead of the features (decode shapes), and a
-// launch may split the reduction over KG workgroups (stage 2 decode).
-// Weights stream from HBM straight into registers, NB-1 pipeline stages ahead
-// (the preshuffle made each piece of a fragment one contiguous 1 KB block);
-// tokens are gathered by row (sorted_slot) into registers one stage ahead and
-// written to LDS in fragment order, double buffered, so the matrix-core reads
-// are contiguous 16-byte-per-lane blocks with no bank conflicts.
+// Workgroup = 4 waves. Each wave owns NF weight fragments along the features
+// (NF*32 rows; for stage 1 gate blocks and the matching up blocks, so the
+// SwiGLU pairs sit in the same lane) and all MT token fragments of the tile;
+// KSPLIT waves may split the reduction instead of the features (decode
+// shapes), and a launch may split the reduction over KG workgroups (stage 2
+// decode). Prefill tiles are 128 tokens x 512 features. Weights stream from HBM
+// straight into registers, NB-1 pipeline stages ahead (the preshuffle made each
+// piece of a fragment one contiguous 1 KB block); tokens are gathered by row
+// (sorted_slot) into registers and written to LDS in fragment order, three
+// buffers deep, so the matrix-core reads are contiguous 16-byte-per-lane blocks
+// with no bank conflicts.
+//
+// Tile order: XCD-contiguous runs of logical tiles, grouped so that the tiles
+// sharing an expert's weights run together (tile_coords). Decode shapes index
+// only the live tiles, from the device-side padded total. Stage 2 at prefill
+// sizes cuts the tiles of a partial last round of workgroups into reduction
+// pieces (tail_plan, tail_reduce_kernel). Stage 1 at prefill sizes stages its
+// bf16 output tile in LDS and writes whole row segments non-temporally.
 #include "moe_device.h"
 #include "moe_launch.h"
 
