@@ -28,8 +28,8 @@
 // sharing an expert's weights run together (tile_coords). Decode shapes index
 // only the live tiles, from the device-side padded total. Stage 2 at prefill
 // sizes cuts the tiles of a partial last round of workgroups into reduction
-// pieces (tail_plan, tail_reduce_kernel). Stage 1 at prefill sizes stages its
-// bf16 output tile in LDS and writes whole row segments non-temporally.
+// pieces (tail_plan, tail_reduce_kernel). Stage 1 stages its bf16 output tile
+// in LDS and writes whole row segments non-temporally.
 #include "moe_device.h"
 #include "moe_launch.h"
 
