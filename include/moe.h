@@ -108,7 +108,8 @@ moe_status moe_route(const void* x, const void* w_router, const float* bias, int
  * topk_ids int32 [T*k]; sorted_slot int32 [moe_align_capacity()];
  * tile_expert int32 [capacity/block_m]; expert_count int32 [E];
  * expert_offset int32 [E+1]; total_padded int32 [1]. All device memory.
- * An id outside [0,E) makes total_padded 0 (nothing downstream runs).
+ * An id outside [0,E) makes total_padded 0: the stages then compute nothing
+ * and moe_stage2 writes an all-zero output.
  * Supported: block_m in {32, 64, 128, 256}, 1 <= E <= 64.
  */
 int64_t moe_align_capacity(int T, int k, int E, int block_m); /* ceil((T*k+E*(bm-1))/bm)*bm */

@@ -322,7 +322,7 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
     err = moe::launch_tail_reduce(tr, stream);
     if (err != hipSuccess) return hip_status(err, "moe_stage2 tail reduction launch");
   }
-  moe::CombineArgs cb{part, T, k, H, c.kg, (uint16_t*)out};
+  moe::CombineArgs cb{part, total_padded, T, k, H, c.kg, (uint16_t*)out};
   return hip_status(moe::launch_combine(cb, stream), "moe_stage2 combine launch");
 }
 

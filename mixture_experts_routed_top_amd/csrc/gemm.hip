@@ -602,6 +602,12 @@ __global__ __launch_bounds__(256) void quant_act_kernel(QuantArgs a) {
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t n4 = (int64_t)a.T * a.H / 4;
   const size_t split = (size_t)a.T * a.k * a.H;
+  if (*a.total_padded == 0) {  // empty grouping (invalid ids): no partial was written
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x)
+      *reinterpret_cast<uint2*>(a.out + (size_t)i * 4) = make_uint2(0u, 0u);
+    return;
+  }
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i * 4 / a.H, h = i * 4 % a.H;

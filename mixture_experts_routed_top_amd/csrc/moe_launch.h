@@ -115,6 +115,7 @@ hipError_t launch_quant_act(const QuantArgs& a, hipStream_t st);
 // out[t,:] = bf16(sum_j sum_g part[g][t*k+j,:]), j ascending, then g ascending.
 struct CombineArgs {
   const float* part;  // [kg][T*k][H]
+  const int32_t* total_padded;  // 0: an empty grouping (invalid ids), the output is zero
   int T, k, H, kg;
   uint16_t* out;      // [T][H]
 };

@@ -4,6 +4,7 @@ import pytest
 import torch
 
 import mixture_experts_routed_top_amd as moe
+import workloads
 import oracle
 from gpu_util import dev, host, say
 
@@ -64,3 +65,21 @@ def test_align_rejects_out_of_range_ids_on_device():
     g = moe.align(dev(ids), 8, 32)
     torch.cuda.synchronize()
     assert int(host(g.total)[0]) == 0
+
+
+def test_empty_grouping_gives_zero_output():
+    # stages run on the empty grouping of invalid ids: stage 2's output is all zero
+    T, H, I, E, k = 10, 256, 256, 8, 2
+    wl = workloads.Workload("empty", T, H, I, E, k, "fp8", 1.0, 1.0 / 16.0, 0.05, 9)
+    inp = workloads.generate(wl)
+    ids = np.zeros((T, k), np.int32)
+    ids[0, 0] = E  # out of range
+    g = moe.align(dev(ids), E, 32)
+    pw = moe.preshuffle("fp8", dev(inp.w1), dev(inp.w3), dev(inp.w2), dev(inp.s1), dev(inp.s3),
+                        dev(inp.s2))
+    _, _, xq, xs, _ = moe.route(dev(inp.x), dev(inp.w_router), k, fp8=True)
+    act, amax = moe.stage1("fp8", xq, xs, pw, g)
+    w = torch.full((T, k), 0.5, dtype=torch.float32, device="cuda")
+    out = moe.stage2("fp8", act, amax, pw, g, w)
+    torch.cuda.synchronize()
+    assert np.all(host(out) == 0)
