@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "moe_oracle.c")
 
-BF16, FP8 = 0, 1
+BF16, FP8, MXFP8 = 0, 1, 2
 
 
 def build() -> str:
@@ -54,6 +54,9 @@ def lib():
         L.oracle_route.argtypes = [P, P, P, i, i, i, i, P, P, P]
         L.oracle_topk.argtypes = [P, i, i, i, P, P]
         L.oracle_quant_tokens.argtypes = [P, i, i, P, P]
+        L.oracle_quant_tokens_mx.argtypes = [P, i, i, P, P]
+        L.oracle_e8m0_to_f64.restype = ctypes.c_double
+        L.oracle_e8m0_to_f64.argtypes = [ctypes.c_uint8]
         L.oracle_align.restype = ctypes.c_int
         L.oracle_align.argtypes = [P, i, i, i, i, P, P, P, P, P]
         L.oracle_swiglu.argtypes = [i, P, P, P, P, P, i, i, i, P, P, i, P]
@@ -64,7 +67,7 @@ def lib():
         L.oracle_preshuffle_w2.argtypes = [i, i, i, i, P, P]
         L.oracle_threads.restype = ctypes.c_int
         for name in ("oracle_f32_to_e4m3fn_n", "oracle_e4m3fn_to_f64_n",
-                     "oracle_f32_to_bf16_n", "oracle_bf16_to_f64_n"):
+                     "oracle_f32_to_bf16_n", "oracle_bf16_to_f64_n", "oracle_e8m0_to_f64_n"):
             getattr(L, name).argtypes = [P, ctypes.c_long, P]
         _lib = L
     return _lib
@@ -78,7 +81,7 @@ def _p(a):
 
 
 def _dt(dtype: str) -> int:
-    return {"bf16": BF16, "fp8": FP8}[dtype]
+    return {"bf16": BF16, "fp8": FP8, "mxfp8": MXFP8}[dtype]
 
 
 # --- number formats --------------------------------------------------------
@@ -104,6 +107,10 @@ def e4m3fn_to_f64(q: np.ndarray) -> np.ndarray:
 
 def f32_to_e4m3fn(f: np.ndarray) -> np.ndarray:
     return _conv(lib().oracle_f32_to_e4m3fn_n, f, np.float32, np.uint8)
+
+
+def e8m0_to_f64(b: np.ndarray) -> np.ndarray:
+    return _conv(lib().oracle_e8m0_to_f64_n, b, np.uint8, np.float64)
 
 
 # --- router ----------------------------------------------------------------
@@ -147,6 +154,16 @@ def quant_tokens(x):
     return q, s
 
 
+def quant_tokens_mx(x):
+    """MX block quantisation of token rows -> (codes uint8 [T,H], E8M0 codes uint8 [T,H/32])."""
+    x = np.ascontiguousarray(x, np.uint16)
+    T, H = x.shape
+    q = np.empty((T, H), np.uint8)
+    s = np.empty((T, H // 32), np.uint8)
+    lib().oracle_quant_tokens_mx(_p(x), T, H, _p(q), _p(s))
+    return q, s
+
+
 # --- grouping --------------------------------------------------------------
 
 def capacity(T, k, E, bm):
@@ -187,7 +204,8 @@ def swiglu(dtype, x, w1, w3, s1, s3, tokens, experts):
 
 
 def store_intermediate(dtype, act):
-    """Storage rounding of the intermediate (bf16, or per-row e4m3fn requantisation)."""
+    """Storage rounding of the intermediate (bf16; per-row e4m3fn requantisation; or bf16
+    followed by the MX block quantisation)."""
     a = np.array(act, np.float64, copy=True, order="C")
     lib().oracle_store_intermediate(_dt(dtype), _p(a), a.shape[0], a.shape[1])
     return a

@@ -24,6 +24,16 @@
  * SwiGLU intermediate on the bf16 path, the per-row e4m3fn requantisation of the
  * intermediate on the fp8 path, and the bf16 output.
  *
+ * MXFP8 path (the second page, the PyTorch FlyDSL backend summary, section
+ * "Einschraenkungen": E4M3 operands with one E8M0 scale per 32 values along the
+ * reduction, K a multiple of 128). The pages fix only the format; how a block's
+ * scale is chosen is the OCP Microscaling specification's conversion, the
+ * plainest reading: scale = 2^(floor(log2 max|v|) - 8), 8 being the exponent of
+ * E4M3's largest normal, elements rounded to nearest even and saturated at 448.
+ * Weights arrive quantised (that page measures from quantised operands); the
+ * token rows are block-quantised on the path, and the SwiGLU intermediate is
+ * stored in bf16 and block-quantised again for the down projection.
+ *
  * Each function is plain loops; OpenMP only splits independent output rows.
  */
 #include <math.h>
@@ -34,7 +44,9 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_BF16 = 0, ORACLE_FP8 = 1 };
+enum { ORACLE_BF16 = 0, ORACLE_FP8 = 1, ORACLE_MXFP8 = 2 };
+
+enum { MX_BLOCK = 32 }; /* values per E8M0 scale along the reduction */
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                            */
@@ -107,11 +119,64 @@ uint8_t oracle_f32_to_e4m3fn(float v)
     return sign | (uint8_t)c;
 }
 
+/* OCP E8M0 shared scale: eight exponent bits, no sign, no mantissa; code b
+ * is 2^(b - 127) and 0xFF is NaN. */
+double oracle_e8m0_to_f64(uint8_t b)
+{
+    if (b == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* One MX block of n values: returns the E8M0 code of the shared scale and
+ * writes the n e4m3fn codes. The shared exponent is floor(log2 amax) - 8,
+ * clamped to E8M0's [-127, 127]; an all-zero block gets exponent 0 (scale 1).
+ * Elements: e4m3fn(clamp(v / 2^x, -448, 448)); dividing by a power of two is
+ * exact, so the only rounding is the encoder's. */
+static uint8_t mx_block(const float* v, int n, uint8_t* q)
+{
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i)
+        if (fabs((double)v[i]) > amax)
+            amax = fabs((double)v[i]);
+    int x = 0;
+    if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex); /* amax = m * 2^ex, 0.5 <= m < 1: floor(log2 amax) = ex - 1 */
+        x = ex - 1 - 8;
+        if (x < -127)
+            x = -127;
+        if (x > 127)
+            x = 127;
+    }
+    for (int i = 0; i < n; ++i) {
+        double r = ldexp((double)v[i], -x);
+        if (r > 448.0)
+            r = 448.0;
+        if (r < -448.0)
+            r = -448.0;
+        q[i] = oracle_f32_to_e4m3fn((float)r);
+    }
+    return (uint8_t)(x + 127);
+}
+
 static double wval(int dtype, const void* w, size_t idx)
 {
     if (dtype == ORACLE_BF16)
         return oracle_bf16_to_f64(((const uint16_t*)w)[idx]);
     return oracle_e4m3fn_to_f64(((const uint8_t*)w)[idx]);
+}
+
+/* Dequantisation factor of weight element (row, col) of a matrix with K
+ * columns: per output row (fp32 scale) on the fp8 path, per row and 32-column
+ * block (E8M0 code) on the MXFP8 path, 1 for bf16. */
+static double wscale(int dtype, const void* s, size_t row, int col, int K)
+{
+    if (dtype == ORACLE_FP8)
+        return (double)((const float*)s)[row];
+    if (dtype == ORACLE_MXFP8)
+        return oracle_e8m0_to_f64(((const uint8_t*)s)[row * (size_t)(K / MX_BLOCK) + col / MX_BLOCK]);
+    return 1.0;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -225,6 +290,23 @@ void oracle_quant_tokens(const uint16_t* x, int T, int H, uint8_t* xq, float* xs
     }
 }
 
+/* MX block quantisation of token rows (MXFP8 path): for each token and each
+ * block of 32 consecutive hidden values, one E8M0 scale code xs[t, h/32] and
+ * the e4m3fn codes xq[t, h] (mx_block). H must be a multiple of 32. */
+void oracle_quant_tokens_mx(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        float v[MX_BLOCK];
+        for (int b = 0; b < H / MX_BLOCK; ++b) {
+            for (int i = 0; i < MX_BLOCK; ++i)
+                v[i] = (float)oracle_bf16_to_f64(x[(size_t)t * H + b * MX_BLOCK + i]);
+            xs[(size_t)t * (H / MX_BLOCK) + b] =
+                mx_block(v, MX_BLOCK, xq + (size_t)t * H + b * MX_BLOCK);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Grouping token-slots by expert, padded to the M-tile                      */
 
@@ -263,8 +345,9 @@ int oracle_align(const int32_t* ids, int T, int k, int E, int bm, int32_t* sorte
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* Input row x_hat of token t in fp64: the bf16 value, or on the fp8 path the
- * dequantised code of the per-token quantisation. */
+/* Input row x_hat of token t in fp64: the bf16 value; on the fp8 path the
+ * dequantised code of the per-token quantisation; on the MXFP8 path the
+ * dequantised code of the per-block quantisation (code * 2^(scale - 127)). */
 static void token_row(int dtype, const uint16_t* x, int t, int H, double* xh)
 {
     const uint16_t* r = x + (size_t)t * H;
@@ -274,6 +357,15 @@ static void token_row(int dtype, const uint16_t* x, int t, int H, double* xh)
         return;
     }
     uint8_t* q = (uint8_t*)malloc((size_t)H);
+    if (dtype == ORACLE_MXFP8) {
+        uint8_t* sb = (uint8_t*)malloc((size_t)H / MX_BLOCK);
+        oracle_quant_tokens_mx(r, 1, H, q, sb);
+        for (int h = 0; h < H; ++h)
+            xh[h] = oracle_e4m3fn_to_f64(q[h]) * oracle_e8m0_to_f64(sb[h / MX_BLOCK]);
+        free(sb);
+        free(q);
+        return;
+    }
     float s;
     oracle_quant_tokens(r, 1, H, q, &s);
     for (int h = 0; h < H; ++h)
@@ -283,19 +375,18 @@ static void token_row(int dtype, const uint16_t* x, int t, int H, double* xh)
 
 /* SwiGLU intermediate of one (token, expert) pair, before storage rounding:
  * a_i = silu(g_i) * u_i, g = W1[e] x_hat, u = W3[e] x_hat, with dequantised
- * weights W = code * s[e,i] on the fp8 path. */
+ * weights: code * s[e,i] on the fp8 path, code * 2^(s[e,i,h/32] - 127) on the
+ * MXFP8 path (wscale). */
 static void swiglu_row(int dtype, const double* xh, const void* w1, const void* w3,
-                       const float* s1, const float* s3, int e, int H, int I, double* a)
+                       const void* s1, const void* s3, int e, int H, int I, double* a)
 {
 #pragma omp parallel for schedule(static)
     for (int i = 0; i < I; ++i) {
-        size_t row = ((size_t)e * I + i) * (size_t)H;
-        double sg = dtype == ORACLE_FP8 ? (double)s1[(size_t)e * I + i] : 1.0;
-        double su = dtype == ORACLE_FP8 ? (double)s3[(size_t)e * I + i] : 1.0;
+        size_t r = (size_t)e * I + i, row = r * (size_t)H;
         double g = 0.0, u = 0.0;
         for (int h = 0; h < H; ++h) {
-            g += xh[h] * (wval(dtype, w1, row + h) * sg);
-            u += xh[h] * (wval(dtype, w3, row + h) * su);
+            g += xh[h] * (wval(dtype, w1, row + h) * wscale(dtype, s1, r, h, H));
+            u += xh[h] * (wval(dtype, w3, row + h) * wscale(dtype, s3, r, h, H));
         }
         a[i] = silu(g) * u;
     }
@@ -304,12 +395,25 @@ static void swiglu_row(int dtype, const double* xh, const void* w1, const void* 
 /* The intermediate as stage two reads it: bf16 storage on the bf16 path
  * (fp32, then bf16, both round-to-nearest-even); on the fp8 path a per-row
  * requantisation, scale = max|a| / 448 (1 if zero), code = e4m3fn(a / scale),
- * value = code * scale. */
+ * value = code * scale; on the MXFP8 path bf16 storage, then the MX block
+ * quantisation of each 32 consecutive values (mx_block), value = code * 2^x. */
 static void store_intermediate(int dtype, double* a, int I)
 {
     if (dtype == ORACLE_BF16) {
         for (int i = 0; i < I; ++i)
             a[i] = oracle_bf16_to_f64(oracle_f32_to_bf16((float)a[i]));
+        return;
+    }
+    if (dtype == ORACLE_MXFP8) {
+        float v[MX_BLOCK];
+        uint8_t q[MX_BLOCK];
+        for (int b = 0; b < I / MX_BLOCK; ++b) {
+            for (int i = 0; i < MX_BLOCK; ++i)
+                v[i] = (float)oracle_bf16_to_f64(oracle_f32_to_bf16((float)a[b * MX_BLOCK + i]));
+            double sc = oracle_e8m0_to_f64(mx_block(v, MX_BLOCK, q));
+            for (int i = 0; i < MX_BLOCK; ++i)
+                a[b * MX_BLOCK + i] = oracle_e4m3fn_to_f64(q[i]) * sc;
+        }
         return;
     }
     double amax = 0.0;
@@ -327,17 +431,17 @@ static void store_intermediate(int dtype, double* a, int I)
     }
 }
 
-/* Down projection y_h = sum_i a_i * W2[e,h,i]. */
-static void down_row(int dtype, const double* a, const void* w2, const float* s2, int e,
+/* Down projection y_h = sum_i a_i * W2[e,h,i] (weights dequantised as in
+ * swiglu_row, the reduction running over i). */
+static void down_row(int dtype, const double* a, const void* w2, const void* s2, int e,
                      int H, int I, double* y)
 {
 #pragma omp parallel for schedule(static)
     for (int h = 0; h < H; ++h) {
-        size_t row = ((size_t)e * H + h) * (size_t)I;
-        double sd = dtype == ORACLE_FP8 ? (double)s2[(size_t)e * H + h] : 1.0;
+        size_t r = (size_t)e * H + h, row = r * (size_t)I;
         double acc = 0.0;
         for (int i = 0; i < I; ++i)
-            acc += a[i] * (wval(dtype, w2, row + i) * sd);
+            acc += a[i] * (wval(dtype, w2, row + i) * wscale(dtype, s2, r, i, I));
         y[h] = acc;
     }
 }
@@ -345,7 +449,7 @@ static void down_row(int dtype, const double* a, const void* w2, const float* s2
 /* SwiGLU intermediate rows for given (token, expert) pairs, before storage
  * rounding (stage-one parity). act[n, I] in fp64. */
 void oracle_swiglu(int dtype, const uint16_t* x, const void* w1, const void* w3,
-                   const float* s1, const float* s3, int T, int H, int I,
+                   const void* s1, const void* s3, int T, int H, int I,
                    const int32_t* tokens, const int32_t* experts, int n, double* act)
 {
     double* xh = (double*)malloc(sizeof(double) * (size_t)H);
@@ -359,7 +463,7 @@ void oracle_swiglu(int dtype, const uint16_t* x, const void* w1, const void* w3,
 
 /* Down projection of given intermediate rows (already in the value they are
  * stored at) through given experts: y[n, H] in fp64 (stage-two parity). */
-void oracle_down(int dtype, const double* act, const void* w2, const float* s2,
+void oracle_down(int dtype, const double* act, const void* w2, const void* s2,
                  int H, int I, const int32_t* experts, int n, double* y)
 {
     for (int r = 0; r < n; ++r)
@@ -371,8 +475,8 @@ void oracle_down(int dtype, const double* act, const void* w2, const float* s2,
  * sum taken in ascending j. out_bf16[n,H]; out_f64[n,H] (the value before the
  * final rounding) when non-NULL. */
 void oracle_forward(int dtype, const uint16_t* x, const uint16_t* w_router, const float* bias,
-                    const void* w1, const void* w3, const void* w2, const float* s1,
-                    const float* s3, const float* s2, int T, int H, int I, int E, int k,
+                    const void* w1, const void* w3, const void* w2, const void* s1,
+                    const void* s3, const void* s2, int T, int H, int I, int E, int k,
                     const int32_t* tokens, int n, uint16_t* out_bf16, double* out_f64)
 {
     double* xh = (double*)malloc(sizeof(double) * (size_t)H);
@@ -479,6 +583,12 @@ int oracle_threads(void)
 }
 
 /* Array forms of the format conversions (same definitions, element by element). */
+void oracle_e8m0_to_f64_n(const uint8_t* b, long n, double* v)
+{
+    for (long i = 0; i < n; ++i)
+        v[i] = oracle_e8m0_to_f64(b[i]);
+}
+
 void oracle_f32_to_e4m3fn_n(const float* v, long n, uint8_t* q)
 {
     for (long i = 0; i < n; ++i)

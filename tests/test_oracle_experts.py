@@ -24,9 +24,27 @@ def _to_fp8_codes(v32):
         torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+def _e8m0_f64(b):
+    return torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e8m0fnu).double().numpy()
+
+
+def _mx_quant(a):
+    """MX block quantisation along the last axis from numpy's log2 and torch's casts."""
+    R, C = a.shape
+    b = a.astype(np.float64).reshape(R, C // 32, 32)
+    amax = np.abs(b).max(2)
+    x = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, 0)
+    x = np.clip(x, -127, 127)
+    codes = _to_fp8_codes((b * np.exp2(-x)[:, :, None]).reshape(R, C))
+    return _fp8_f64(codes) * np.exp2(x).repeat(32, axis=1)
+
+
 def deq_weights(inp):
     if inp.wl.dtype == "bf16":
         return _bf16_f64(inp.w1), _bf16_f64(inp.w3), _bf16_f64(inp.w2)
+    if inp.wl.dtype == "mxfp8":
+        return tuple(_fp8_f64(w) * _e8m0_f64(s).repeat(32, axis=2)
+                     for w, s in ((inp.w1, inp.s1), (inp.w3, inp.s3), (inp.w2, inp.s2)))
     return (_fp8_f64(inp.w1) * inp.s1[:, :, None], _fp8_f64(inp.w3) * inp.s3[:, :, None],
             _fp8_f64(inp.w2) * inp.s2[:, :, None])
 
@@ -35,6 +53,8 @@ def token_inputs(inp):
     x = _bf16_f64(inp.x)
     if inp.wl.dtype == "bf16":
         return x
+    if inp.wl.dtype == "mxfp8":
+        return _mx_quant(x)
     xf = x.astype(np.float32)
     amax = np.abs(xf).max(1)
     s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
@@ -45,6 +65,8 @@ def token_inputs(inp):
 def store(dtype, a):
     if dtype == "bf16":
         return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    if dtype == "mxfp8":  # bf16 storage, then the block quantisation
+        return _mx_quant(torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).double().numpy())
     amax = np.abs(a).max(1, keepdims=True)
     s = np.where(amax > 0, amax / 448.0, 1.0)
     return _fp8_f64(_to_fp8_codes((a / s).astype(np.float32))) * s
@@ -76,7 +98,7 @@ def small(dtype, E, k, T=24, H=256, I=384, seed=9, bias=None):
     return inp
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8"])
 def test_single_expert_equals_swiglu_mlp(dtype):
     inp = small(dtype, E=1, k=1)
     out, o64 = oracle.forward(inp)
@@ -87,11 +109,11 @@ def test_single_expert_equals_swiglu_mlp(dtype):
     assert np.mean(out.view(np.int16) == ref_b) > 0.999
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8"])
 def test_dense_then_mask_equals_routed(dtype):
     wl = workloads.config(0)
-    if dtype == "fp8":
-        wl = workloads.scaled(wl, dtype="fp8")
+    if dtype != "bf16":
+        wl = workloads.scaled(wl, dtype=dtype)
     inp = workloads.generate(wl)
     out, o64 = oracle.forward(inp)
     ids, w, _ = oracle.route(inp.x, inp.w_router, None, wl.k)
@@ -135,7 +157,30 @@ def test_doubling_down_weights_doubles_output_exactly():
     assert np.array_equal(o64b, 2.0 * o64)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_mx_down_scale_code_plus_one_doubles_output_exactly():
+    inp = small("mxfp8", E=4, k=2)
+    _, o64 = oracle.forward(inp)
+    assert np.all(inp.s2 < 254)
+    inp.s2 = (inp.s2 + 1).astype(np.uint8)
+    _, o64b = oracle.forward(inp)
+    assert np.array_equal(o64b, 2.0 * o64)
+
+
+def test_mx_gate_scale_block_is_used_per_32_columns():
+    # raising the scale code of one 32-column block of W1 changes the result exactly as
+    # doubling those 32 weight values does in the dense reference
+    inp = small("mxfp8", E=1, k=1)
+    inp.s1 = inp.s1.copy()
+    inp.s1[0, :, 3] += 1
+    _, o64 = oracle.forward(inp)
+    ref = expert_outputs(inp, token_inputs(inp))[0]
+    assert rel(o64, ref) < 1e-9
+    inp2 = small("mxfp8", E=1, k=1)
+    _, o64_0 = oracle.forward(inp2)
+    assert rel(o64, o64_0) > 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8"])
 def test_swiglu_and_down_rows(dtype):
     inp = small(dtype, E=4, k=2)
     xh = token_inputs(inp)

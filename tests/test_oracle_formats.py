@@ -87,3 +87,94 @@ def test_bf16_round_trip_matches_torch():
 def test_bf16_nan_stays_nan():
     v = np.array([np.nan], np.float32)
     assert np.isnan(oracle.bf16_to_f64(oracle.f32_to_bf16(v)))[0]
+
+
+# --- MX (E8M0 block scale, E4M3 elements) ------------------------------------
+
+def test_e8m0_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e8m0_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.isnan(ours[255]) and np.isnan(ref[255])
+    assert np.array_equal(ours[:255], ref[:255])
+    assert ours[127] == 1.0 and ours[0] == 2.0 ** -127 and ours[254] == 2.0 ** 127
+
+
+def mx_reference(xf32):
+    """Block quantisation from numpy's log2 and torch's e4m3fn cast (library routines)."""
+    T, H = xf32.shape
+    b = xf32.astype(np.float64).reshape(T, H // 32, 32)
+    amax = np.abs(b).max(2)
+    with np.errstate(divide="ignore"):
+        x = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, 0)
+    x = np.clip(x, -127, 127).astype(np.int64)
+    r = np.clip(b * np.exp2(-x)[:, :, None], -448, 448).astype(np.float32)
+    q = torch.from_numpy(r.reshape(T, H)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return q, (x + 127).astype(np.uint8)
+
+
+def _bf16(v):
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def _mx_rows():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((40, 256)).astype(np.float32)
+    x[1] *= 1e-3
+    x[2] *= 300.0
+    x[3, :32] = 0.0                                   # an all-zero block
+    x[4, 32:64] = np.float32(2.0 ** -130)             # a subnormal block: scale clamps at 2^-127
+    x[5, 64:96] = np.linspace(-511.0, 511.0, 32)      # block maximum just under a power of two
+    x[6, 96:128] = np.float32(256.0)                  # block maximum exactly a power of two
+    x[7] = rng.standard_normal(256).astype(np.float32) * np.float32(2.0 ** 100)
+    return _bf16(x)
+
+
+def test_mx_quant_matches_library_reference():
+    xb = _mx_rows()
+    q, s = oracle.quant_tokens_mx(xb)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    rq, rs = mx_reference(xf)
+    assert np.array_equal(s, rs)
+    assert np.array_equal(q, rq)
+    assert np.all(s[3, 0] == 127) and np.all(q[3, :32] == 0)
+    assert s[4, 1] == 0
+
+
+def test_mx_quant_closed_forms():
+    xb = _mx_rows()
+    q, s = oracle.quant_tokens_mx(xb)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    vals = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    deq = vals * np.exp2(s.astype(np.float64) - 127).repeat(32, axis=1)
+    b = np.abs(xf).reshape(40, 8, 32).max(2)
+    big = np.abs(vals).reshape(40, 8, 32).max(2)
+    live = (b > 2.0 ** -100)
+    # the block maximum lands in [256, 448]: the top binade of e4m3fn (saturating above 448)
+    assert np.all((big[live] >= 256) & (big[live] <= 448))
+    # relative error of every element at most half an e4m3fn ulp of its binade (2^-4),
+    # except the saturated ones (|x| / 2^e in (448, 512))
+    scale = np.exp2(s.astype(np.float64) - 127).repeat(32, axis=1)
+    sat = np.abs(xf) / scale > 448
+    norm = (np.abs(xf) / scale >= 2.0 ** -6) & ~sat
+    assert np.all(np.abs(deq - xf)[norm] <= 2.0 ** -4 * np.abs(xf)[norm] * (1 + 1e-12))
+    assert np.all(np.abs(deq[sat]) == 448 * scale[sat])
+
+
+def test_mx_quant_is_blockwise_and_scale_equivariant():
+    xb = _mx_rows()[8:]
+    q, s = oracle.quant_tokens_mx(xb)
+    # x * 2^3 (exact in bf16 for these values): same codes, every scale + 3
+    x8 = (xb.astype(np.uint32) + (3 << 7)).astype(np.uint16)
+    assert np.all((xb & 0x7F80) != 0) and np.all((x8 & 0x7F80) != 0x7F80)
+    q8, s8 = oracle.quant_tokens_mx(x8)
+    assert np.array_equal(q8, q) and np.array_equal(s8.astype(int), s.astype(int) + 3)
+    # changing one block leaves the other blocks' codes and scales alone
+    x2 = xb.copy()
+    x2[:, 64:96] = _bf16(np.full((xb.shape[0], 32), 1000.0))
+    q2, s2 = oracle.quant_tokens_mx(x2)
+    keep = np.ones(256, bool)
+    keep[64:96] = False
+    assert np.array_equal(q2[:, keep], q[:, keep])
+    assert np.array_equal(np.delete(s2, 2, axis=1), np.delete(s, 2, axis=1))

@@ -1,5 +1,6 @@
 """The seeded workloads: determinism, shapes, and the skewed workload's routing shares."""
 import numpy as np
+import torch
 
 import oracle
 import workloads
@@ -29,3 +30,18 @@ def test_skewed_workload_shares():
     share = np.bincount(ids.ravel(), minlength=wl.E) / ids.size
     assert 0.39 <= share[0] <= 0.41
     assert share[6] < 0.03 and share[7] < 0.03
+
+
+def test_mx_weight_blocks_dequantise_to_the_drawn_values():
+    rng = np.random.default_rng(4)
+    a = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    q, s = workloads.quantize_blocks_mx(a)
+    assert q.shape == a.shape and s.shape == (64, 8) and s.dtype == np.uint8
+    vals = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy()
+    deq = vals * torch.from_numpy(s).view(torch.float8_e8m0fnu).double().numpy().repeat(32, 1)
+    scale = torch.from_numpy(s).view(torch.float8_e8m0fnu).double().numpy().repeat(32, 1)
+    err = np.abs(deq - a) / np.abs(a).reshape(64, 8, 32).max(2).repeat(32, 1)
+    sat = np.abs(a) / scale > 448
+    assert err[~sat].max() <= 2.0 ** -4  # at most half an ulp of the block's top binade
+    assert np.all(np.abs(deq[sat]) == 448 * scale[sat])
+    assert workloads.mxfp8(16).dtype == "mxfp8" and workloads.mxfp8(16).H == 4096

@@ -16,6 +16,10 @@ Weight quantisation for the fp8 workloads (one fp32 scale per output channel,
 scale = amax/448, codes by round-to-nearest-even with saturation) is load-time
 input preparation, done here with torch's float8_e4m3fn cast. It is not part of
 the hot path: the library's entry points take the codes and scales as inputs.
+The MXFP8 workloads (the second page, the PyTorch FlyDSL backend summary,
+"Einschraenkungen": E4M3 values with one E8M0 scale per 32 along the reduction;
+its measurements start from quantised operands) store the weights the same way
+per 32-value block of each row, with the OCP MX scale 2^(floor(log2 amax) - 8).
 """
 from __future__ import annotations
 
@@ -40,7 +44,7 @@ class Workload:
     I: int
     E: int
     k: int
-    dtype: str            # "bf16" or "fp8"
+    dtype: str            # "bf16", "fp8" or "mxfp8"
     sigma_x: float
     sigma_r: float
     sigma_w: float
@@ -83,6 +87,14 @@ def config(i: int, T: int | None = None) -> Workload:
 DECODE_SWEEP = (1, 4, 16, 64, 256)
 
 
+def mxfp8(T: int) -> Workload:
+    """The Mixtral expert layer with MXFP8 operands (block-scaled weights and tokens) at
+    batch T; weights and router drawn like the fp8 workloads, seed 5."""
+    m = MIXTRAL
+    return Workload(f"mixtral-mxfp8-T{T}", int(T), m["H"], m["I"], m["E"], m["k"], "mxfp8",
+                    1.0, 1.0 / 64.0, 0.02, 5, x_seed=(int(T),))
+
+
 def scaled(w: Workload, **kw) -> Workload:
     """A copy of a workload with some fields replaced (used for small parity shapes)."""
     d = dict(w.__dict__)
@@ -113,6 +125,26 @@ def quantize_rows_fp8(a: np.ndarray):
     return q.view(torch.uint8).numpy(), s.numpy().astype(np.float32)
 
 
+def quantize_blocks_mx(a: np.ndarray, block: int = 32):
+    """Per-block e4m3fn codes and E8M0 scale codes along each row (OCP MX storage).
+
+    Block b of row r (columns b*block .. +block-1) gets exponent
+    x = floor(log2 amax) - 8 (0 for an all-zero block), clamped to [-127, 127];
+    codes = e4m3fn(clamp(a / 2^x, -448, 448)). Returns (codes uint8 [R, C],
+    scale codes uint8 [R, C/block] = x + 127).
+    """
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    R, C = t.shape
+    b = t.reshape(R, C // block, block)
+    amax = b.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)  # amax = m * 2^ex with 0.5 <= m < 1
+    x = torch.where(amax > 0, (ex - 9).clamp(-127, 127), torch.zeros_like(ex))
+    q = torch.ldexp(b, (-x).unsqueeze(2).to(torch.float32)).clamp(-448.0, 448.0)
+    q = q.to(torch.float8_e4m3fn).view(torch.uint8).reshape(R, C)
+    return q.numpy(), (x + 127).to(torch.uint8).numpy()
+
+
 # ---------------------------------------------------------------------------
 
 @dataclass
@@ -125,9 +157,9 @@ class Inputs:
     w1: np.ndarray           # bf16 uint16 or e4m3fn uint8, [E, I, H] (gate)
     w3: np.ndarray           # same, [E, I, H] (up)
     w2: np.ndarray           # same, [E, H, I] (down)
-    s1: np.ndarray | None    # float32 [E, I] (fp8 only)
-    s3: np.ndarray | None    # float32 [E, I]
-    s2: np.ndarray | None    # float32 [E, H]
+    s1: np.ndarray | None    # fp8: float32 [E, I]; mxfp8: E8M0 uint8 [E, I, H/32]
+    s3: np.ndarray | None    # same as s1
+    s2: np.ndarray | None    # fp8: float32 [E, H]; mxfp8: E8M0 uint8 [E, H, I/32]
 
 
 def _normal(seed_words, shape, sigma) -> np.ndarray:
@@ -174,6 +206,9 @@ def generate(wl: Workload, weights: bool = True, threads: int = 8) -> Inputs:
         a = _normal((wl.seed, 2 + m, e), (rows, cols), wl.sigma_w)
         if wl.dtype == "bf16":
             return job, to_bf16_bits(a), None
+        if wl.dtype == "mxfp8":
+            q, s = quantize_blocks_mx(a)
+            return job, q, s
         q, s = quantize_rows_fp8(a)
         return job, q, s
 
@@ -182,10 +217,15 @@ def generate(wl: Workload, weights: bool = True, threads: int = 8) -> Inputs:
     w3 = np.empty((E, I, H), wdt)
     w2 = np.empty((E, H, I), wdt)
     mats = (w1, w3, w2)
-    fp8 = wl.dtype == "fp8"
-    s1 = np.empty((E, I), np.float32) if fp8 else None
-    s3 = np.empty((E, I), np.float32) if fp8 else None
-    s2 = np.empty((E, H), np.float32) if fp8 else None
+    fp8 = wl.dtype in ("fp8", "mxfp8")
+    if wl.dtype == "mxfp8":
+        s1 = np.empty((E, I, H // 32), np.uint8)
+        s3 = np.empty((E, I, H // 32), np.uint8)
+        s2 = np.empty((E, H, I // 32), np.uint8)
+    else:
+        s1 = np.empty((E, I), np.float32) if fp8 else None
+        s3 = np.empty((E, I), np.float32) if fp8 else None
+        s2 = np.empty((E, H), np.float32) if fp8 else None
     scales = (s1, s3, s2)
     with ThreadPoolExecutor(max(1, threads)) as ex:
         for (m, e, _, _), q, s in ex.map(draw, jobs):
