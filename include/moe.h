@@ -15,8 +15,13 @@
  * taking device pointers, sizes and a stream.
  *
  * Shapes: x[T,H] tokens, W_r[E,H] router, W1/W3[E,I,H] gate/up, W2[E,H,I] down,
- * top-k with k <= E. Element types: bf16, or OCP e4m3fn ("FP8", the precision the
- * talk summary's Mixtral 8x7B kernel runs in, 5:56/7:31) with fp32 scales.
+ * top-k with k <= E. Element types: bf16; OCP e4m3fn ("FP8", the precision the
+ * talk summary's Mixtral 8x7B kernel runs in, 5:56/7:31) with fp32 scales; or
+ * MXFP8 (the second page's scaled-GEMM format, "Einschraenkungen": e4m3fn values
+ * with one E8M0 scale per 32 values along the reduction; scale code b means
+ * 2^(b-127)). MXFP8 block scales are chosen as in the OCP Microscaling
+ * specification: x = floor(log2 max|v|) - 8 (0 for an all-zero block), clamped
+ * to [-127, 127], code x + 127; values e4m3fn(clamp(v / 2^x, -448, 448)).
  *
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers owned by the caller, allocated
@@ -51,7 +56,7 @@ typedef enum {
     MOE_ERR_HIP = 4          /* a HIP launch reported an error                      */
 } moe_status;
 
-typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3FN = 1 } moe_dtype;
+typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3FN = 1, MOE_MXFP8 = 2 } moe_dtype;
 
 /* Static string for a status code. */
 const char* moe_status_string(int status);
@@ -92,6 +97,23 @@ moe_status moe_route(const void* x, const void* w_router, const float* bias, int
                      float* x_scale, hipStream_t stream);
 
 /*
+ * moe_route_mx - moe_route with the MXFP8 quantisation of x instead of the
+ * per-token one (the block format of the second page, "Einschraenkungen").
+ * Routing (ids, weights, logits) is exactly moe_route's. Then, for every token
+ * t and block b of 32 consecutive hidden values: x = floor(log2 max|x[t, 32b..
+ * 32b+31]|) - 8 (0 if that block is all zero), clamped to [-127, 127];
+ * x_scale_e8m0[t, b] = x + 127; x_q[t, h] = e4m3fn(clamp(x[t,h] / 2^x, -448,
+ * 448)), round to nearest even (the division by a power of two is exact).
+ *
+ * x_q uint8 [T,H] (out, 8-byte aligned); x_scale_e8m0 uint8 [T, H/32] (out;
+ * 8-byte aligned when it feeds moe_stage1). Both required. Other arguments and
+ * the supported shapes as moe_route.
+ */
+moe_status moe_route_mx(const void* x, const void* w_router, const float* bias, int T, int H,
+                        int E, int k, int32_t* topk_ids, float* topk_w, float* logits, void* x_q,
+                        void* x_scale_e8m0, hipStream_t stream);
+
+/*
  * moe_align - groups the T*k token-slots by expert and pads each group to the
  * M-tile (the "dynamic expert sizes" of the talk summary, 5:56).
  *
@@ -125,20 +147,31 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
  * values, one 32x32 matrix-core step), stored row-block major then reduction
  * block. A fragment is two 1 KB pieces; in piece pc the 16 bytes at l*16
  * (lane l = 0..63) are row l mod 32, bytes (l/32)*32 + pc*16 .. +15 of the
- * fragment's 64. Gate and up rows are interleaved in blocks of 32 (W1 block,
- * W3 block, ...), so one wave holds the gate and up value of the same
- * intermediate column.
+ * fragment's 64 (MXFP8: bytes pc*32 + (l/32)*16 .. +15, so that each piece
+ * pair is one 32-value scale block in the matrix-core instruction's grouping).
+ * Gate and up rows are interleaved in blocks of 32 (W1 block, W3 block, ...),
+ * so one wave holds the gate and up value of the same intermediate column.
  *
  * w1, w3   [E,I,H] row-major; w2 [E,H,I] row-major (bf16 or e4m3fn codes)
- * s1, s3   fp32 [E,I]; s2 fp32 [E,H] per-output-channel scales (FP8 only, else NULL)
+ * s1, s3   FP8: fp32 [E,I]; s2 FP8: fp32 [E,H] per-output-channel scales.
+ *          MXFP8: E8M0 codes, s1, s3 uint8 [E,I,H/32]; s2 uint8 [E,H,I/32]
+ *          (one per row and 32 reduction values). BF16: NULL.
  * w13_out  [moe_preshuffle_bytes(dt,E,H,I,0)] bytes; w2_out [.., 1] bytes
- * s13_out  fp32 [E,2,I] (gate scales then up scales); s2_out fp32 [E,H]   (FP8 only)
- * Supported: H % 128 == 0 and I % 128 == 0 (bf16), H % 256 and I % 256 (FP8).
+ * s13_out  [.., 2] bytes; s2_out [.., 3] bytes (FP8 and MXFP8, else unused).
+ *          FP8: fp32 [E,2,I] (gate scales then up scales) and fp32 [E,H].
+ *          MXFP8 (4-byte aligned): the codes in the order the kernels read
+ *          them: per expert, groups of four 32-row blocks (composite rows as
+ *          above), then reduction fragment kb (64 values), then lane l = 0..63,
+ *          then the four blocks: the code of row l mod 32 of the block, value
+ *          block 2*kb + l/32.
+ * Supported: H % 128 == 0 and I % 128 == 0 (bf16), H % 256 and I % 256 (FP8,
+ * MXFP8).
  */
-int64_t moe_preshuffle_bytes(moe_dtype dt, int E, int H, int I, int which /*0: W1+W3, 1: W2*/);
+int64_t moe_preshuffle_bytes(moe_dtype dt, int E, int H, int I,
+                             int which /*0: W1+W3, 1: W2, 2: their scales s13, 3: s2*/);
 moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, const void* w3,
-                          const void* w2, const float* s1, const float* s3, const float* s2,
-                          void* w13_out, void* w2_out, float* s13_out, float* s2_out,
+                          const void* w2, const void* s1, const void* s3, const void* s2,
+                          void* w13_out, void* w2_out, void* s13_out, void* s2_out,
                           hipStream_t stream);
 
 /*
@@ -146,22 +179,26 @@ moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, con
  * SwiGLU of its glossary). For each padded row p < total_padded with slot
  * s = sorted_slot[p], token t = s / k, expert e = tile_expert[p / block_m]:
  *   g = W1[e] x_t, u = W3[e] x_t (fp32 accumulation; FP8: x_t = x_q[t]*x_scale[t],
- *   W = code * scale), act[p, i] = bf16(silu(g_i) * u_i), silu(z) = z/(1+e^-z).
+ *   W = code * scale; MXFP8: every value times 2^(code - 127) of its 32-value
+ *   block, tokens and weights alike), act[p, i] = bf16(silu(g_i) * u_i),
+ *   silu(z) = z/(1+e^-z).
  * Pad rows (s == T*k) get act = 0.
  * FP8 also writes act_amax: per row p, partial maxima of |act[p,:]| over column
  * blocks, [capacity][moe_stage1_amax_floats()/capacity] floats (row-major);
  * stage 2 reduces them.
  *
- * x_or_xq  bf16 [T,H] (BF16) or e4m3fn [T,H] (FP8, from moe_route)
- * x_scale  fp32 [T] (FP8) or NULL; w13, s13 from moe_preshuffle
+ * x_or_xq  bf16 [T,H] (BF16) or e4m3fn [T,H] (FP8 from moe_route, MXFP8 from
+ *          moe_route_mx)
+ * x_scale  fp32 [T] (FP8), E8M0 uint8 [T,H/32] (MXFP8, 8-byte aligned) or NULL;
+ * w13, s13 from moe_preshuffle
  * sorted_slot, tile_expert, total_padded from moe_align with the same block_m
- * act      bf16 [capacity, I] (out); act_amax as above (FP8) or NULL
+ * act      bf16 [capacity, I] (out); act_amax as above (FP8) or NULL (else unused)
  * Supported: block_m in {32, 64, 128, 256}; H, I multiples of 128 (bf16) or 256
- * (FP8); H <= 8192 is not required here; activations below 2 GiB.
+ * (FP8, MXFP8); MXFP8 also H <= 8192 and I <= 16384; activations below 2 GiB.
  */
 int64_t moe_stage1_amax_floats(moe_dtype dt, int T, int k, int E, int H, int I, int block_m);
-moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, const void* w13,
-                      const float* s13, const int32_t* sorted_slot, const int32_t* tile_expert,
+moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, const void* w13,
+                      const void* s13, const int32_t* sorted_slot, const int32_t* tile_expert,
                       const int32_t* total_padded, int T, int k, int E, int H, int I,
                       int block_m, void* act, float* act_amax, hipStream_t stream);
 
@@ -169,7 +206,9 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, c
  * moe_stage2 - grouped down GEMM + weighted scatter-combine (talk summary 5:56,
  * "Scatter"). For each real row p (slot s, token t = s / k, expert e):
  *   y = W2[e] act_p   (FP8: act_p requantised per row, scale = max|act_p|/448,
- *                      code = e4m3fn(act_p / scale); fp32 accumulation)
+ *                      code = e4m3fn(act_p / scale); MXFP8: act_p quantised
+ *                      per block of 32 values as moe_route_mx does x;
+ *                      fp32 accumulation)
  *   out[t, :] = bf16( sum_{j=0..k-1} w[t,j] * y_{t,j} ), summed in ascending j
  *   in fp32: a fixed order, no floating-point atomics, so results are
  *   reproducible bit for bit on a given device. (At prefill sizes the tiles
@@ -177,15 +216,17 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, c
  *   reduction whose partials are summed in piece order; the cut follows from
  *   the number of workgroups the device runs at once.)
  *
- * act, act_amax from moe_stage1; w2, s2 from moe_preshuffle; topk_w fp32 [T,k]
+ * act, act_amax from moe_stage1 (act_amax unused, may be NULL, unless FP8);
+ * w2, s2 from moe_preshuffle; topk_w fp32 [T,k]
  * out bf16 [T,H] (out); workspace [moe_stage2_workspace_bytes()] bytes (device,
- * 256-byte aligned): per-slot weighted partials, for FP8 the requantised
- * intermediate, and at prefill sizes the partials of those reduction pieces.
+ * 256-byte aligned): per-slot weighted partials, for FP8 and MXFP8 the
+ * requantised intermediate, and at prefill sizes the partials of those
+ * reduction pieces.
  * Calls that use one workspace must be ordered (same stream or synchronised).
  */
 int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int I, int block_m);
 moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, const void* w2,
-                      const float* s2, const int32_t* sorted_slot, const int32_t* tile_expert,
+                      const void* s2, const int32_t* sorted_slot, const int32_t* tile_expert,
                       const int32_t* total_padded, const float* topk_w, int T, int k, int E,
                       int H, int I, int block_m, void* out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);

@@ -10,6 +10,10 @@ library's HIP kernels; torch provides device memory and streams only.
     pw = preshuffle("fp8", w1, w3, w2, s1, s3, s2)          # once, at load time
     act, amax = stage1("fp8", x_q, x_scale, pw, grp)
     out = stage2("fp8", act, amax, pw, grp, w)
+
+The MXFP8 path ("mxfp8": e4m3fn values with one E8M0 scale code per 32 values
+along the reduction) is the same sequence with route(..., mx=True), which
+returns the block codes of x as x_scale, and block-scaled weights.
 """
 from __future__ import annotations
 
@@ -17,7 +21,7 @@ from dataclasses import dataclass
 
 import torch
 
-from ._lib import BF16, FP8, MoEError, check, lib
+from ._lib import BF16, FP8, MXFP8, MoEError, check, lib
 
 __all__ = ["route", "align", "preshuffle", "stage1", "stage2", "forward", "Layer",
            "pick_block_m", "align_capacity", "MoEError"]
@@ -28,6 +32,8 @@ def _dt(dtype) -> int:
         return BF16
     if dtype in ("fp8", FP8):
         return FP8
+    if dtype in ("mxfp8", MXFP8):
+        return MXFP8
     raise ValueError(f"dtype {dtype!r}")
 
 
@@ -54,15 +60,22 @@ def align_capacity(T: int, k: int, E: int, block_m: int) -> int:
 
 
 def route(x: torch.Tensor, w_router: torch.Tensor, k: int, bias: torch.Tensor | None = None,
-          fp8: bool = False, want_logits: bool = False):
+          fp8: bool = False, want_logits: bool = False, mx: bool = False):
     """-> (topk_ids int32 [T,k], topk_w fp32 [T,k], x_q uint8 [T,H] | None,
-    x_scale fp32 [T] | None, logits fp32 [T,E] | None)."""
+    x_scale | None, logits fp32 [T,E] | None). x_scale is fp32 [T] with fp8=True, the
+    E8M0 block codes uint8 [T, H/32] with mx=True."""
     T, H = x.shape
     E = w_router.shape[0]
     dev = x.device
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     lg = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    if mx:
+        xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+        check(lib().moe_route_mx(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, _ptr(ids),
+                                 _ptr(w), _ptr(lg), _ptr(xq), _ptr(xs), _stream()))
+        return ids, w, xq, xs, lg
     xq = torch.empty((T, H), dtype=torch.uint8, device=dev) if fp8 else None
     xs = torch.empty((T,), dtype=torch.float32, device=dev) if fp8 else None
     check(lib().moe_route(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, _ptr(ids), _ptr(w),
@@ -126,8 +139,12 @@ def preshuffle(dtype, w1, w3, w2, s1=None, s3=None, s2=None) -> Weights:
     dev = w1.device
     w13p = torch.empty(n13, dtype=torch.uint8, device=dev)
     w2p = torch.empty(n2, dtype=torch.uint8, device=dev)
-    s13p = torch.empty((E, 2, I), dtype=torch.float32, device=dev) if dt == FP8 else None
-    s2p = torch.empty((E, H), dtype=torch.float32, device=dev) if dt == FP8 else None
+    if dt == MXFP8:  # block codes in the kernels' order (opaque bytes)
+        s13p = torch.empty(L.moe_preshuffle_bytes(dt, E, H, I, 2), dtype=torch.uint8, device=dev)
+        s2p = torch.empty(L.moe_preshuffle_bytes(dt, E, H, I, 3), dtype=torch.uint8, device=dev)
+    else:
+        s13p = torch.empty((E, 2, I), dtype=torch.float32, device=dev) if dt == FP8 else None
+        s2p = torch.empty((E, H), dtype=torch.float32, device=dev) if dt == FP8 else None
     check(L.moe_preshuffle(dt, E, H, I, _ptr(w1), _ptr(w3), _ptr(w2), _ptr(s1), _ptr(s3),
                            _ptr(s2), _ptr(w13p), _ptr(w2p), _ptr(s13p), _ptr(s2p), _stream()))
     return Weights(dt, E, H, I, w13p, w2p, s13p, s2p)
@@ -183,6 +200,7 @@ class Layer:
                  k=2, T=None, block_m=None):
         self.dt = _dt(dtype)
         self.fp8 = self.dt == FP8
+        self.mx = self.dt == MXFP8
         self.E, self.I, self.H = w1.shape
         self.k = k
         self.w_router = w_router
@@ -200,8 +218,11 @@ class Layer:
         L = lib()
         self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
-        self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev) if self.fp8 else None
-        self.xs = torch.empty((T,), dtype=torch.float32, device=dev) if self.fp8 else None
+        self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev) if self.fp8 or self.mx else None
+        if self.mx:
+            self.xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+        else:
+            self.xs = torch.empty((T,), dtype=torch.float32, device=dev) if self.fp8 else None
         self.grp = Grouping(torch.empty(cap, dtype=torch.int32, device=dev),
                             torch.empty(cap // self.bm, dtype=torch.int32, device=dev),
                             torch.empty(E, dtype=torch.int32, device=dev),
@@ -222,11 +243,12 @@ class Layer:
             self._alloc(T)
         L, st = lib(), _stream()
         E, H, I, k, bm, g = self.E, self.H, self.I, self.k, self.bm, self.grp
-        check(L.moe_route(_ptr(x), _ptr(self.w_router), _ptr(self.bias), T, H, E, k,
-                          _ptr(self.ids), _ptr(self.w), None, _ptr(self.xq), _ptr(self.xs), st))
+        route_fn = L.moe_route_mx if self.mx else L.moe_route
+        check(route_fn(_ptr(x), _ptr(self.w_router), _ptr(self.bias), T, H, E, k,
+                       _ptr(self.ids), _ptr(self.w), None, _ptr(self.xq), _ptr(self.xs), st))
         check(L.moe_align(_ptr(self.ids), T, k, E, bm, _ptr(g.sorted_slot), _ptr(g.tile_expert),
                           _ptr(g.count), _ptr(g.offset), _ptr(g.total), st))
-        xin = self.xq if self.fp8 else x
+        xin = x if self.dt == BF16 else self.xq
         if events is not None:
             events[0].record()
         check(L.moe_stage1(self.dt, _ptr(xin), _ptr(self.xs), _ptr(self.pw.w13), _ptr(self.pw.s13),

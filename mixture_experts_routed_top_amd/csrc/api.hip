@@ -52,8 +52,10 @@ int64_t capacity(int T, int k, int E, int bm) {
 }
 
 // Checks shared by the two GEMM stages.
+bool valid_dt(int dt) { return dt == MOE_BF16 || dt == MOE_FP8_E4M3FN || dt == MOE_MXFP8; }
+
 moe_status check_stage(int dt, int T, int k, int E, int H, int I, int bm) {
-  CHECK(dt == MOE_BF16 || dt == MOE_FP8_E4M3FN, MOE_ERR_INVALID_ARG, "dtype %d", dt);
+  CHECK(valid_dt(dt), MOE_ERR_INVALID_ARG, "dtype %d", dt);
   CHECK(T >= 0 && k >= 1 && E >= 1 && H > 0 && I > 0, MOE_ERR_INVALID_ARG,
         "sizes T=%d k=%d E=%d H=%d I=%d", T, k, E, H, I);
   CHECK(k <= E && k <= 8 && E <= 64, MOE_ERR_UNSUPPORTED, "k=%d E=%d (need k<=min(E,8), E<=64)", k,
@@ -62,6 +64,8 @@ moe_status check_stage(int dt, int T, int k, int E, int H, int I, int bm) {
   const int q = dt == MOE_BF16 ? 128 : 256;
   CHECK(H % q == 0 && I % q == 0, MOE_ERR_UNSUPPORTED, "H=%d I=%d must be multiples of %d", H, I,
         q);
+  CHECK(dt != MOE_MXFP8 || (H <= moe::kMxMaxH && I <= moe::kMxMaxI), MOE_ERR_UNSUPPORTED,
+        "MXFP8 needs H <= %d and I <= %d (H=%d I=%d)", moe::kMxMaxH, moe::kMxMaxI, H, I);
   CHECK((int64_t)T * k <= (1 << 30) && capacity(T, k, E, bm) <= (1 << 30), MOE_ERR_UNSUPPORTED,
         "T*k too large");
   // Activation rows are addressed with 32-bit buffer offsets below 2 GiB.
@@ -110,8 +114,28 @@ moe_status moe_route(const void* x, const void* w_router, const float* bias, int
   CHECK(aligned(x, 16) && aligned(w_router, 16) && aligned(x_q, 8), MOE_ERR_INVALID_ARG,
         "x and w_router must be 16-byte aligned, x_q 8-byte aligned");
   moe::RouteArgs a{(const uint16_t*)x, (const uint16_t*)w_router, bias, T, H, E, k, topk_ids,
-                   topk_w, logits, (uint8_t*)x_q, x_scale};
+                   topk_w, logits, (uint8_t*)x_q, x_scale, nullptr};
   return hip_status(moe::launch_route(a, stream), "moe_route launch");
+}
+
+moe_status moe_route_mx(const void* x, const void* w_router, const float* bias, int T, int H,
+                        int E, int k, int32_t* topk_ids, float* topk_w, float* logits, void* x_q,
+                        void* x_scale_e8m0, hipStream_t stream) {
+  CHECK(T >= 0 && H > 0, MOE_ERR_INVALID_ARG, "sizes T=%d H=%d", T, H);
+  CHECK(E >= 1 && k >= 1, MOE_ERR_INVALID_ARG, "E=%d k=%d", E, k);
+  CHECK(E <= 64 && k <= E && k <= 8, MOE_ERR_UNSUPPORTED, "E=%d k=%d (need E<=64, k<=min(E,8))",
+        E, k);
+  CHECK(H % 128 == 0 && H <= 8192, MOE_ERR_UNSUPPORTED,
+        "H=%d must be a multiple of 128, at most 8192", H);
+  CHECK((int64_t)T * H <= ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "T*H too large");
+  if (T == 0) return ok();
+  CHECK(x && w_router && topk_ids && topk_w && x_q && x_scale_e8m0, MOE_ERR_INVALID_ARG,
+        "null x/w_router/topk_ids/topk_w/x_q/x_scale_e8m0");
+  CHECK(aligned(x, 16) && aligned(w_router, 16) && aligned(x_q, 8), MOE_ERR_INVALID_ARG,
+        "x and w_router must be 16-byte aligned, x_q 8-byte aligned");
+  moe::RouteArgs a{(const uint16_t*)x, (const uint16_t*)w_router, bias, T, H, E, k, topk_ids,
+                   topk_w, logits, (uint8_t*)x_q, nullptr, (uint8_t*)x_scale_e8m0};
+  return hip_status(moe::launch_route(a, stream), "moe_route_mx launch");
 }
 
 int64_t moe_align_capacity(int T, int k, int E, int block_m) {
@@ -135,18 +159,24 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
 }
 
 int64_t moe_preshuffle_bytes(moe_dtype dt, int E, int H, int I, int which) {
-  if ((dt != MOE_BF16 && dt != MOE_FP8_E4M3FN) || E < 1 || H < 1 || I < 1) return -1;
+  if (!valid_dt(dt) || E < 1 || H < 1 || I < 1) return -1;
   const int64_t es = dt == MOE_BF16 ? 2 : 1;
   if (which == 0) return 2 * (int64_t)E * I * H * es;
   if (which == 1) return (int64_t)E * H * I * es;
+  if (which == 2 || which == 3) {
+    if (dt == MOE_BF16) return 0;
+    const int64_t rows = which == 2 ? 2 * (int64_t)E * I : (int64_t)E * H;
+    if (dt == MOE_FP8_E4M3FN) return rows * 4;                // one fp32 per output row
+    return rows * ((which == 2 ? H : I) / 32);                 // one E8M0 code per 32 values
+  }
   return -1;
 }
 
 moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, const void* w3,
-                          const void* w2, const float* s1, const float* s3, const float* s2,
-                          void* w13_out, void* w2_out, float* s13_out, float* s2_out,
+                          const void* w2, const void* s1, const void* s3, const void* s2,
+                          void* w13_out, void* w2_out, void* s13_out, void* s2_out,
                           hipStream_t stream) {
-  CHECK(dt == MOE_BF16 || dt == MOE_FP8_E4M3FN, MOE_ERR_INVALID_ARG, "dtype %d", (int)dt);
+  CHECK(valid_dt(dt), MOE_ERR_INVALID_ARG, "dtype %d", (int)dt);
   CHECK(E >= 1 && H > 0 && I > 0, MOE_ERR_INVALID_ARG, "sizes E=%d H=%d I=%d", E, H, I);
   const int q = dt == MOE_BF16 ? 128 : 256;
   CHECK(H % q == 0 && I % q == 0, MOE_ERR_UNSUPPORTED, "H=%d I=%d must be multiples of %d", H, I,
@@ -155,15 +185,19 @@ moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, con
   CHECK(aligned(w1, 16) && aligned(w3, 16) && aligned(w2, 16) && aligned(w13_out, 16) &&
             aligned(w2_out, 16),
         MOE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
-  const bool fp8 = dt == MOE_FP8_E4M3FN;
-  if (fp8)
-    CHECK(s1 && s3 && s2 && s13_out && s2_out, MOE_ERR_INVALID_ARG, "FP8 needs all scale pointers");
-  const int64_t es = fp8 ? 1 : 2;
+  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = dt == MOE_MXFP8;
+  if (fp8 || mx)
+    CHECK(s1 && s3 && s2 && s13_out && s2_out, MOE_ERR_INVALID_ARG,
+          "FP8 and MXFP8 need all scale pointers");
+  if (mx)
+    CHECK(aligned(s13_out, 4) && aligned(s2_out, 4), MOE_ERR_INVALID_ARG,
+          "MXFP8 scale outputs must be 4-byte aligned");
+  const int64_t es = dt == MOE_BF16 ? 2 : 1;
   moe::PreshuffleArgs a13{(const uint8_t*)w1, (const uint8_t*)w3, (uint8_t*)w13_out, E, 2 * I,
-                          H * es};
+                          H * es, mx};
   hipError_t err = moe::launch_preshuffle(a13, stream);
   if (err != hipSuccess) return hip_status(err, "preshuffle W1/W3");
-  moe::PreshuffleArgs a2{(const uint8_t*)w2, nullptr, (uint8_t*)w2_out, E, H, I * es};
+  moe::PreshuffleArgs a2{(const uint8_t*)w2, nullptr, (uint8_t*)w2_out, E, H, I * es, mx};
   err = moe::launch_preshuffle(a2, stream);
   if (err != hipSuccess) return hip_status(err, "preshuffle W2");
   if (fp8) {
@@ -176,6 +210,15 @@ moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, con
       err = hipMemcpyAsync(s2_out, s2, (size_t)E * H * 4, hipMemcpyDeviceToDevice, stream);
     if (err != hipSuccess) return hip_status(err, "preshuffle scales");
   }
+  if (mx) {
+    moe::PreshuffleArgs m13{(const uint8_t*)s1, (const uint8_t*)s3, (uint8_t*)s13_out, E, 2 * I, H,
+                            1};
+    err = moe::launch_preshuffle_mx_scales(m13, stream);
+    if (err != hipSuccess) return hip_status(err, "preshuffle W1/W3 block scales");
+    moe::PreshuffleArgs m2{(const uint8_t*)s2, nullptr, (uint8_t*)s2_out, E, H, I, 1};
+    err = moe::launch_preshuffle_mx_scales(m2, stream);
+    if (err != hipSuccess) return hip_status(err, "preshuffle W2 block scales");
+  }
   return ok();
 }
 
@@ -186,27 +229,36 @@ int64_t moe_stage1_amax_floats(moe_dtype dt, int T, int k, int E, int H, int I, 
   return capacity(T, k, E, block_m) * (2 * (int64_t)I / c.wg_n);
 }
 
-moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, const void* w13,
-                      const float* s13, const int32_t* sorted_slot, const int32_t* tile_expert,
+moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, const void* w13,
+                      const void* s13, const int32_t* sorted_slot, const int32_t* tile_expert,
                       const int32_t* total_padded, int T, int k, int E, int H, int I, int block_m,
                       void* act, float* act_amax, hipStream_t stream) {
   moe_status s = check_stage(dt, T, k, E, H, I, block_m);
   if (s != MOE_OK) return s;
   if (T == 0) return ok();
-  const bool fp8 = dt == MOE_FP8_E4M3FN;
+  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = dt == MOE_MXFP8;
   CHECK(x_or_xq && w13 && sorted_slot && tile_expert && total_padded && act, MOE_ERR_INVALID_ARG,
         "null pointer argument");
   CHECK(!fp8 || (x_scale && s13 && act_amax), MOE_ERR_INVALID_ARG,
         "FP8 needs x_scale, s13 and act_amax");
-  CHECK(aligned(x_or_xq, 16) && aligned(w13, 16) && aligned(act, 16) && aligned(s13, 16),
-        MOE_ERR_INVALID_ARG, "x, w13, act and s13 must be 16-byte aligned");
+  CHECK(!mx || (x_scale && s13), MOE_ERR_INVALID_ARG, "MXFP8 needs x_scale and s13");
+  CHECK(aligned(x_or_xq, 16) && aligned(w13, 16) && aligned(act, 16) &&
+            aligned(s13, mx ? 4 : 16) && aligned(x_scale, mx ? 8 : 4),
+        MOE_ERR_INVALID_ARG,
+        "x, w13 and act must be 16-byte aligned, s13 16-byte (MXFP8: 4), x_scale 4-byte "
+        "(MXFP8: 8)");
   moe::GemmCfg c = moe::stage1_cfg(dt, T, k, E, H, I, block_m);
   const int64_t cap = capacity(T, k, E, block_m);
   moe::GemmArgs a{};
   a.X = (const uint8_t*)x_or_xq;
-  a.x_scale = x_scale;
   a.W = (const uint8_t*)w13;
-  a.w_scale = s13;
+  if (mx) {
+    a.x_mx = (const uint8_t*)x_scale;
+    a.w_mx = (const uint8_t*)s13;
+  } else {
+    a.x_scale = (const float*)x_scale;
+    a.w_scale = (const float*)s13;
+  }
   a.sorted_slot = sorted_slot;
   a.tile_expert = tile_expert;
   a.total_padded = total_padded;
@@ -218,7 +270,7 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const float* x_scale, c
   a.I = I;
   a.cap = (int)cap;
   a.bm = block_m;
-  a.K_bytes = H * (fp8 ? 1 : 2);
+  a.K_bytes = H * (dt == MOE_BF16 ? 2 : 1);
   a.x_bytes = (int64_t)T * a.K_bytes;
   a.n_mtiles = (int)(cap / (32 * c.mt));
   a.n_ntiles = 2 * I / c.wg_n;
@@ -238,25 +290,30 @@ int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int
     const int64_t cap = capacity(T, k, E, block_m);
     bytes += up(cap * I) + up(cap * 4);  // requantised intermediate + row scales
   }
+  if (dt == MOE_MXFP8) {
+    const int64_t cap = capacity(T, k, E, block_m);
+    bytes += up(cap * I) + up(cap * (I / 32));  // requantised intermediate + block codes
+  }
   if (c.tail_split > 0)  // partials of the tail pieces
     bytes += up((int64_t)moe::kTailPieces * 32 * c.mt * c.wg_n * 4);
   return bytes;
 }
 
 moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, const void* w2,
-                      const float* s2, const int32_t* sorted_slot, const int32_t* tile_expert,
+                      const void* s2, const int32_t* sorted_slot, const int32_t* tile_expert,
                       const int32_t* total_padded, const float* topk_w, int T, int k, int E, int H,
                       int I, int block_m, void* out, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
   moe_status s = check_stage(dt, T, k, E, H, I, block_m);
   if (s != MOE_OK) return s;
   if (T == 0) return ok();
-  const bool fp8 = dt == MOE_FP8_E4M3FN;
+  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = dt == MOE_MXFP8;
   CHECK(act && w2 && sorted_slot && tile_expert && total_padded && topk_w && out && workspace,
         MOE_ERR_INVALID_ARG, "null pointer argument");
   CHECK(!fp8 || (act_amax && s2), MOE_ERR_INVALID_ARG, "FP8 needs act_amax and s2");
+  CHECK(!mx || s2, MOE_ERR_INVALID_ARG, "MXFP8 needs s2");
   CHECK(aligned(act, 16) && aligned(w2, 16) && aligned(out, 8) && aligned(workspace, 256) &&
-            aligned(s2, 16),
+            aligned(s2, mx ? 4 : 16),
         MOE_ERR_INVALID_ARG, "act/w2/s2 16-byte, out 8-byte, workspace 256-byte alignment");
   const int64_t need = moe_stage2_workspace_bytes(dt, T, k, E, H, I, block_m);
   CHECK((int64_t)workspace_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu bytes < %lld needed",
@@ -270,6 +327,7 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
   ws += up((int64_t)c.kg * T * k * H * 4);
   const void* x = act;
   const float* xs = nullptr;
+  const uint8_t* xmx = nullptr;
   hipError_t err;
   if (fp8) {
     uint8_t* act_q = (uint8_t*)ws;
@@ -283,11 +341,26 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
     xs = act_scale;
     ws += up(cap * I) + up(cap * 4);
   }
+  if (mx) {
+    uint8_t* act_q = (uint8_t*)ws;
+    uint8_t* act_mx = (uint8_t*)(ws + up(cap * I));
+    moe::QuantMxArgs q{(const uint16_t*)act, (int)cap, I, total_padded, act_q, act_mx};
+    err = moe::launch_quant_act_mx(q, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_stage2 block requantisation");
+    x = act_q;
+    xmx = act_mx;
+    ws += up(cap * I) + up(cap * (I / 32));
+  }
   moe::GemmArgs a{};
   a.X = (const uint8_t*)x;
   a.x_scale = xs;
   a.W = (const uint8_t*)w2;
-  a.w_scale = s2;
+  if (mx) {
+    a.x_mx = xmx;
+    a.w_mx = (const uint8_t*)s2;
+  } else {
+    a.w_scale = (const float*)s2;
+  }
   a.sorted_slot = sorted_slot;
   a.tile_expert = tile_expert;
   a.total_padded = total_padded;
@@ -299,7 +372,7 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
   a.I = I;
   a.cap = (int)cap;
   a.bm = block_m;
-  a.K_bytes = I * (fp8 ? 1 : 2);
+  a.K_bytes = I * (dt == MOE_BF16 ? 2 : 1);
   a.x_bytes = cap * a.K_bytes;
   a.n_mtiles = (int)(cap / (32 * c.mt));
   a.n_ntiles = H / c.wg_n;

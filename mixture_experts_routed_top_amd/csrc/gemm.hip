@@ -10,7 +10,11 @@
 // (output features) by 64 reduction bytes; the B operand is the same shape cut
 // from 32 token rows. Lane l supplies row l%32 and the 32 reduction bytes
 // starting at (l/32)*32, held as two 16-byte pieces; accumulator register i of
-// lane l is then output feature 8*(i/4) + 4*(l/32) + i%4 of token l%32.
+// lane l is then output feature 8*(i/4) + 4*(l/32) + i%4 of token l%32. (The
+// instruction itself pairs K differently: lanes r and r+32 together hold its
+// first 32 values in their first pieces. Any order shared by both operands
+// gives the same sums; the MXFP8 path, whose scales follow the instruction's
+// own grouping, stores piece pc of lane l as bytes 32*pc + 16*(l/32).)
 //
 // Workgroup = 4 waves. Each wave owns NF weight fragments along the features
 // (NF*32 rows; for stage 1 gate blocks and the matching up blocks, so the
@@ -42,12 +46,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kPiece = 1024;  // one fragment piece: 64 lanes x 16 B
 constexpr int kFrag = 2048;   // one fragment: 32 rows x 64 reduction bytes
 
+// One 32x32 step over 64 reduction bytes. ws and xs carry the E8M0 block
+// scales of the MXFP8 path (byte OA of ws for the weight operand, byte OB of
+// xs for the token operand: lane l's byte scales its 32 values); the other
+// element types ignore them. The instruction reads the scale from byte 0 of
+// its register whatever its byte-select field says, so the byte is shifted
+// down first.
 template <int DT>
 struct Mma;
 template <>
 struct Mma<1> {  // e4m3fn x e4m3fn, 32x32x64, unscaled form
+  template <int OA, int OB>
   static __device__ __forceinline__ f32x16 run(const uint4 (&w)[2], const uint4 (&x)[2],
-                                               f32x16 c) {
+                                               f32x16 c, int, int) {
     i32x8 a = {(int)w[0].x, (int)w[0].y, (int)w[0].z, (int)w[0].w,
                (int)w[1].x, (int)w[1].y, (int)w[1].z, (int)w[1].w};
     i32x8 b = {(int)x[0].x, (int)x[0].y, (int)x[0].z, (int)x[0].w,
@@ -56,9 +67,23 @@ struct Mma<1> {  // e4m3fn x e4m3fn, 32x32x64, unscaled form
   }
 };
 template <>
-struct Mma<0> {  // bf16: one 32x32x16 per piece
+struct Mma<2> {  // e4m3fn x e4m3fn with E8M0 block scales (MXFP8), 32x32x64
+  template <int OA, int OB>
   static __device__ __forceinline__ f32x16 run(const uint4 (&w)[2], const uint4 (&x)[2],
-                                               f32x16 c) {
+                                               f32x16 c, int ws, int xs) {
+    i32x8 a = {(int)w[0].x, (int)w[0].y, (int)w[0].z, (int)w[0].w,
+               (int)w[1].x, (int)w[1].y, (int)w[1].z, (int)w[1].w};
+    i32x8 b = {(int)x[0].x, (int)x[0].y, (int)x[0].z, (int)x[0].w,
+               (int)x[1].x, (int)x[1].y, (int)x[1].z, (int)x[1].w};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        a, b, c, 0, 0, 0, (int)((uint32_t)ws >> (8 * OA)), 0, (int)((uint32_t)xs >> (8 * OB)));
+  }
+};
+template <>
+struct Mma<0> {  // bf16: one 32x32x16 per piece
+  template <int OA, int OB>
+  static __device__ __forceinline__ f32x16 run(const uint4 (&w)[2], const uint4 (&x)[2],
+                                               f32x16 c, int, int) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[0]),
                                                 __builtin_bit_cast(bf16x8, x[0]), c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[1]),
@@ -85,12 +110,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 constexpr uint32_t kPadOffset = 0x80000000u;
 
 // LDS slot swizzle of the token tile. The 16-byte column c (0..3) of a row's
-// 64-byte window goes to piece c&1, slot s = row + 32*(c>>1), stored at slot
-// s ^ lds_swz(c). The four columns of a row (written by four adjacent lanes)
-// then land in different bank groups, for both 8- and 16-lane LDS passes:
-// over 2 rows x 4 columns the slots differ mod 8, over 4 rows x 4 columns
-// mod 16. Readers apply the same permutation (it keeps bit 5 of the slot, so
-// it is a bijection inside each piece).
+// 64-byte window goes to piece c&1, slot s = row + 32*(c>>1) (MXFP8: piece
+// c>>1, slot row + 32*(c&1)), stored at slot s ^ lds_swz(c). The four columns
+// of a row (written by four adjacent lanes) then land in different bank
+// groups, for both 8- and 16-lane LDS passes: over 2 rows x 4 columns the
+// slots differ mod 8, over 4 rows x 4 columns mod 16 (a piece is 64 slots, so
+// the piece does not change a slot's bank group). Readers apply the same
+// permutation (it keeps bit 5 of the slot, so it is a bijection inside each
+// piece).
 __device__ __forceinline__ int lds_swz(int c) { return 4 * (c & 1) + 10 * (c >> 1); }
 
 // n / k for 0 <= n < 2^30 and 1 <= k <= 32 with magic = ceil(2^35 / k):
@@ -165,6 +192,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   static_assert(WN * BMT * 4 <= LDS, "amax space");
   static_assert(NB == 3 || NB == 4, "weight pipeline depth");
 
+  // MXFP8: the E8M0 codes of the tile's token rows over this workgroup's
+  // reduction range sit after the token buffers for the main loop, laid out
+  // [column][token][fragment] (a column covers 32 reduction values), so that
+  // one LDS read gives a lane the codes of all MT fragments in one column.
+  constexpr bool MX = DT == 2;
+  constexpr int XCOLS = MX ? (STAGE == 1 ? kMxMaxH : kMxMaxI) / 32 + 16 : 0;
+  constexpr int XST = XCOLS * BMT;
   // Token buffers (reused by the epilogue), then the column scales of this
   // workgroup's features (FP8), staged once so that the epilogue reads LDS.
   constexpr int SCL = DT == 1 ? WGN : 0;
@@ -174,7 +208,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // maxima of the FP8 epilogue past it.
   constexpr int SP = WGN + 8;                               // staging row pitch, bytes
   constexpr int STG = STAGE == 1 ? BMT * SP : 0;
-  constexpr int LDSX = (LDS > STG ? LDS : STG) + (STAGE == 1 && DT == 1 ? WN * BMT * 4 : 0);
+  constexpr int MAIN = LDS + XST;  // main loop: token buffers and the MXFP8 code tile
+  constexpr int LDSX = (MAIN > STG ? MAIN : STG) + (STAGE == 1 && DT == 1 ? WN * BMT * 4 : 0);
   __shared__ __align__(16) uint8_t lds[LDSX + SCL * 4];
   float* const scl = reinterpret_cast<float*>(lds + LDSX);
 
@@ -255,8 +290,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const uint32_t row = STAGE == 1 ? div_k(min(slot, S - 1), a.k_magic) : (uint32_t)p;
     const uint32_t rowbase = slot < S ? row * (uint32_t)Kb : kPadOffset;  // select, no branch
     xoff[j] = rowbase + (uint32_t)(kbase + ks * Kw + s * 64 + c * 16);
-    loff[j] = ((ks * kSub + s) * MT + m) * kFrag + (c & 1) * kPiece +
-              ((r + 32 * (c >> 1)) ^ lds_swz(c)) * 16;
+    // Column c goes to piece c&1 of lane half c>>1 (MXFP8: piece c>>1 of lane
+    // half c&1, so that each piece is one 32-value scale block).
+    const int pce = MX ? (c >> 1) : (c & 1), hlf = MX ? (c & 1) : (c >> 1);
+    loff[j] = ((ks * kSub + s) * MT + m) * kFrag + pce * kPiece +
+              ((r + 32 * hlf) ^ lds_swz(c)) * 16;
   }
 
   // This wave's weight fragments: composite row blocks rb0 .. rb0+NF-1;
@@ -266,6 +304,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const uint8_t* wbase = a.W + (((int64_t)e * RB + rb0) * KB + (kbase + wk * Kw) / 64) * kFrag +
                          lane * 16;
   const int64_t wfrag_stride = KB * kFrag;  // next row block
+  // MXFP8 weight codes of this wave's row blocks: per fragment one 32-bit
+  // (NF = 4) or 16-bit (NF = 2) word per lane whose byte f belongs to row
+  // block rb0 + f (rb0 is a multiple of NF).
+  const uint8_t* wsp = nullptr;
+  if constexpr (MX)
+    wsp = a.w_mx + (((int64_t)e * (RB / 4) + rb0 / 4) * KB + (kbase + wk * Kw) / 64) * 256 +
+          lane * 4 + (rb0 & 3);
 
   f32x16 acc[MT][NF];
 #pragma unroll
@@ -277,6 +322,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 
   uint4 xr[2][PPT];             // token prefetch, by chunk parity
   uint4 wbuf[NB][kSub][NF][2];  // weight prefetch: [stage][sub-block][fragment][piece]
+  uint32_t wsr[NB][kSub];       // MXFP8 weight codes, staged like the weights
+  uint32_t xsr[2][kSub];        // MXFP8 token codes, by chunk parity
 
   auto load_x = [&](int c, uint4 (&x)[PPT]) {
 #pragma unroll
@@ -293,6 +340,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     w = *reinterpret_cast<const uint4*>(wbase + f * wfrag_stride +
                                         ((int64_t)c * kSub + s) * kFrag + pc * kPiece);
   };
+  auto load_ws = [&](int c, int sb, uint32_t& r) {
+    const uint8_t* p = wsp + ((int64_t)c * kSub + sb) * 256;
+    if constexpr (NF == 4)
+      r = *reinterpret_cast<const uint32_t*>(p);
+    else
+      r = *reinterpret_cast<const uint16_t*>(p);
+  };
   auto load_w = [&](int c, uint4 (&w)[kSub][NF][2]) {
 #pragma unroll
     for (int s = 0; s < kSub; ++s)
@@ -301,12 +355,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int pc = 0; pc < 2; ++pc) load_w1(c, s, f, pc, w[s][f][pc]);
   };
-  const int rd0 = (lane ^ lds_swz(2 * (lane >> 5))) * 16;           // piece 0 slot of this lane
-  const int rd1 = kPiece + (lane ^ lds_swz(1 + 2 * (lane >> 5))) * 16;  // piece 1
+  // Column whose bytes this lane's piece 0 / piece 1 holds, and their slots.
+  const int rc0 = MX ? (lane >> 5) : 2 * (lane >> 5), rc1 = MX ? 2 + (lane >> 5) : 1 + 2 * (lane >> 5);
+  const int rd0 = (lane ^ lds_swz(rc0)) * 16;           // piece 0 slot of this lane
+  const int rd1 = kPiece + (lane ^ lds_swz(rc1)) * 16;  // piece 1
   auto read_frag = [&](int buf, int t, uint4 (&x)[2]) {
     const uint8_t* pp = lds + buf * BUF + (wk * NSTEP + t) * kFrag;
     x[0] = *reinterpret_cast<const uint4*>(pp + rd0);
     x[1] = *reinterpret_cast<const uint4*>(pp + rd1);
+  };
+  // MXFP8 token codes of chunk c: per sub-block one word whose byte m is the
+  // code of fragment m's row (this lane's token) in this lane's column.
+  int xs_lane = 0;  // byte offset of this lane's column of chunk 0 in the code tile
+  auto read_xs = [&](int c, uint32_t (&r)[kSub]) {
+#pragma unroll
+    for (int sb = 0; sb < kSub; ++sb) {
+      const uint8_t* p = lds + LDS + xs_lane + (c * (kChunk / 32) + 2 * sb) * BMT;
+      if constexpr (MT == 4)
+        r[sb] = *reinterpret_cast<const uint32_t*>(p);
+      else if constexpr (MT == 2)
+        r[sb] = *reinterpret_cast<const uint16_t*>(p);
+      else
+        r[sb] = *p;
+    }
   };
 
   // One pipeline stage for chunk c (u = c mod the unroll period). Its token
@@ -324,7 +395,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   uint4 xf[2][2];
   auto step = [&](int c, auto u_const) {
     constexpr int u = decltype(u_const)::value;
-    constexpr int NLOAD = PPT + kSub * NF * 2;
+    constexpr int NWL = PPT + kSub * NF * 2;  // token and weight loads
+    constexpr int NLOAD = NWL + (MX ? kSub : 0);
     constexpr int NM = NSTEP * NF;
     const int last = nchunks - 1;
     const int cx = min(c + 3, last), cw = min(c + NB - 1, last);
@@ -334,34 +406,38 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         xr[(u + 1) & 1][j] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff[j] + (uint32_t)cx * kChunk,
                                                          0, 0));
-      } else {
+      } else if constexpr (j < NWL) {
         constexpr int q = j - PPT, s = q / (NF * 2), f = (q / 2) % NF, pc = q % 2;
         load_w1(cw, s, f, pc, wbuf[(u + NB - 1) % NB][s][f][pc]);
+      } else {
+        load_ws(cw, j - NWL, wsr[(u + NB - 1) % NB][j - NWL]);
       }
     };
-#pragma unroll
-    for (int t = 0; t < NSTEP; ++t) {
-      if (t + 1 < NSTEP)
+    static_for<NSTEP>([&](auto t_const) {
+      constexpr int t = decltype(t_const)::value;
+      if constexpr (t + 1 < NSTEP)
         read_frag(u % 3, t + 1, xf[(t + 1) & 1]);
       else
         read_frag((u + 1) % 3, 0, xf[(t + 1) & 1]);
-      const int s = t / MT, m = t % MT;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        acc[m][f] = Mma<DT>::run(wbuf[u % NB][s][f], xf[t & 1], acc[m][f]);
-        const int mi = t * NF + f;
+      if constexpr (MX && t == 0) read_xs(min(c + 1, last), xsr[(u + 1) & 1]);
+      constexpr int s = t / MT, m = t % MT;
+      static_for<NF>([&](auto f_const) {
+        constexpr int f = decltype(f_const)::value;
+        acc[m][f] = Mma<DT>::template run<f, m>(wbuf[u % NB][s][f], xf[t & 1], acc[m][f],
+                                                (int)wsr[u % NB][s], (int)xsr[u & 1][s]);
+        constexpr int mi = t * NF + f;
         static_for<NLOAD>([&](auto j_const) {
           constexpr int j = decltype(j_const)::value;
-          if (j * NM / NLOAD == mi) issue(j_const);
+          if constexpr (j * NM / NLOAD == mi) issue(j_const);
         });
         __builtin_amdgcn_sched_barrier(0);
-      }
-      if (t == NSTEP / 2 - 1) {
+      });
+      if constexpr (t == NSTEP / 2 - 1) {
         __syncthreads();
         store_x((u + 2) % 3, xr[u & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    });
   };
 
   // Epilogue inputs, fetched now so that their latency hides behind the main
@@ -405,15 +481,56 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   {
     const int last = nchunks - 1;
 #pragma unroll
-    for (int u = 0; u < NB - 1; ++u) load_w(min(u, last), wbuf[u]);
+    for (int u = 0; u < NB - 1; ++u) {
+      load_w(min(u, last), wbuf[u]);
+      if constexpr (MX)
+#pragma unroll
+        for (int sb = 0; sb < kSub; ++sb) load_ws(min(u, last), sb, wsr[u][sb]);
+    }
     load_x(0, xr[0]);
     load_x(min(1, last), xr[1]);
     if constexpr (DT == 1) load_colsc();
+    if constexpr (MX) {
+      // The code tile: row r of the tile (fragment r/32, token r%32), columns
+      // gstart .. cend of the E8M0 codes of its X row (this workgroup's
+      // reduction range, gstart rounded down to a multiple of 8), in 8-byte
+      // loads. Pad rows read past the buffer, as zeros (their values are zero
+      // too).
+      const int col0 = kbase >> 5, gstart = col0 & ~7;
+      const int cend = (kbase + (KSPLIT - 1) * Kw + nchunks * kChunk) >> 5;
+      const int ng = (cend - gstart + 7) >> 3;
+      const int r = tid % BMT;
+      const int slot = a.sorted_slot[row0 + r];
+      const uint32_t srow = STAGE == 1 ? div_k(min(slot, S - 1), a.k_magic) : (uint32_t)(row0 + r);
+      const uint32_t sbase = slot < S ? srow * (uint32_t)(Kb >> 5) + (uint32_t)gstart : kPadOffset;
+      const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)a.x_mx, (short)0, (int)(a.x_bytes >> 5), 0x00020000);
+      uint8_t* dst = lds + LDS + (r & 31) * MT + (r >> 5);
+      constexpr int GS = 256 / BMT, BATCH = 8;
+      for (int g0 = tid / BMT; g0 < ng; g0 += GS * BATCH) {
+        uint2 v[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j)
+          v[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                               srsrc, sbase + 8u * (uint32_t)(g0 + GS * j), 0, 0));
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+          const int g = g0 + GS * j;
+          if (g < ng) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              dst[(8 * g + i) * BMT] = (uint8_t)((i < 4 ? v[j].x : v[j].y) >> (8 * (i & 3)));
+          }
+        }
+      }
+      xs_lane = (col0 - gstart + wk * (Kw >> 5) + (lane >> 5)) * BMT + (lane & 31) * MT;
+    }
     store_x(0, xr[0]);
     store_x(1, xr[1]);
     load_x(min(2, last), xr[0]);
     __syncthreads();
     read_frag(0, 0, xf[0]);
+    if constexpr (MX) read_xs(0, xsr[0]);
   }
 
   // Steady state, unrolled by the period P = lcm(2, 3, NB) (token registers
@@ -596,6 +713,45 @@ __global__ __launch_bounds__(256) void quant_act_kernel(QuantArgs a) {
     *reinterpret_cast<uint2*>(q + c * 8) =
         make_uint2(f32x4_to_e4m3(f[0], f[1], f[2], f[3]), f32x4_to_e4m3(f[4], f[5], f[6], f[7]));
   }
+}
+
+// MX block quantisation of the bf16 intermediate (MXFP8 stage 2): one thread
+// per block of 32 values of a row p < total_padded; the block maximum sets the
+// shared exponent (mx_exponent), codes = e4m3fn(clamp(v * 2^-x)).
+__global__ __launch_bounds__(256) void quant_act_mx_kernel(QuantMxArgs a) {
+  const int nb = a.I / 32;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t p = i / nb;
+  const int b = (int)(i % nb);
+  if (p >= *a.total_padded) return;
+  const uint4* src = reinterpret_cast<const uint4*>(a.act + (size_t)p * a.I + (size_t)b * 32);
+  uint4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = src[j];
+  float f[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[8 * j + 2 * q] = bf16_bits_to_f32(w[q] & 0xffffu);
+      f[8 * j + 2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) m = fmaxf(m, fabsf(f[j]));
+  const int x = mx_exponent(m);
+  const float inv = mx_inv_scale(x);
+  uint32_t c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    c[j] = f32x4_to_e4m3(clamp448(f[4 * j] * inv), clamp448(f[4 * j + 1] * inv),
+                         clamp448(f[4 * j + 2] * inv), clamp448(f[4 * j + 3] * inv));
+  uint4* dq = reinterpret_cast<uint4*>(a.act_q + (size_t)p * a.I + (size_t)b * 32);
+  dq[0] = make_uint4(c[0], c[1], c[2], c[3]);
+  dq[1] = make_uint4(c[4], c[5], c[6], c[7]);
+  a.act_mx[(size_t)p * nb + b] = (uint8_t)(x + 127);
 }
 
 // out[t,:] = bf16( sum_j sum_g part[g][t*k+j][:] ), j ascending, then split g ascending.
@@ -803,6 +959,8 @@ hipError_t dispatch(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipS
                     int* res) {
   if (dt == 0)
     return stage == 1 ? launch_dt_stage<0, 1>(c, a, st, res) : launch_dt_stage<0, 2>(c, a, st, res);
+  if (dt == 2)
+    return stage == 1 ? launch_dt_stage<2, 1>(c, a, st, res) : launch_dt_stage<2, 2>(c, a, st, res);
   return stage == 1 ? launch_dt_stage<1, 1>(c, a, st, res) : launch_dt_stage<1, 2>(c, a, st, res);
 }
 
@@ -827,6 +985,12 @@ hipError_t launch_tail_reduce(const TailReduceArgs& a, hipStream_t st) {
 
 hipError_t launch_quant_act(const QuantArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(quant_act_kernel, dim3(a.cap), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_mx(const QuantMxArgs& a, hipStream_t st) {
+  const int64_t n = (int64_t)a.cap * (a.I / 32);
+  hipLaunchKernelGGL(quant_act_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

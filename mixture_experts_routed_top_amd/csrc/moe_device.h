@@ -43,6 +43,25 @@ __device__ __forceinline__ float clamp448(float v) {
   return fminf(fmaxf(v, -448.0f), 448.0f);
 }
 
+// Shared exponent of an MX block with E4M3 elements (OCP Microscaling): the
+// largest magnitude amax sets x = floor(log2 amax) - 8, 8 being the exponent
+// of E4M3's largest normal (448 = 1.75 * 2^8), clamped to the E8M0 range
+// [-127, 127]; an all-zero block gets 0. The E8M0 code is x + 127. floor(log2)
+// of a normal float is its unbiased exponent field; a subnormal amax is below
+// 2^-126, so its x clamps to -127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  return ef == 0 ? -127 : max(ef - 127 - 8, -127);
+}
+
+// 2^-x for an exponent from mx_exponent (x <= 119, so 127 - x is in [8, 254]:
+// a normal float). Multiplying by it is exact wherever the product is a normal
+// float; smaller products encode to a zero e4m3fn code either way.
+__device__ __forceinline__ float mx_inv_scale(int x) {
+  return __uint_as_float((uint32_t)(127 - x) << 23);
+}
+
 // Physical workgroup id -> logical tile id so that each XCD (workgroups are
 // dealt round robin over the 8 XCDs) gets one contiguous run of logical tiles;
 // neighbouring logical tiles then share operands in that XCD's L2.

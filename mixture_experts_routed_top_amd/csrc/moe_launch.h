@@ -15,7 +15,8 @@ struct RouteArgs {
   float* topk_w;             // [T,k]
   float* logits;             // [T,E] or null
   uint8_t* x_q;              // [T,H] or null
-  float* x_scale;            // [T]
+  float* x_scale;            // [T] (per-token FP8)
+  uint8_t* x_mx;             // [T][H/32] E8M0 codes (MXFP8: x_q holds block-scaled codes), or null
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 
@@ -38,8 +39,14 @@ struct PreshuffleArgs {
   uint8_t* dst;
   int E, R;             // R: composite rows per expert (2I or H)
   int64_t K_bytes;      // reduction length in bytes (multiple of 64)
+  int mx_order;         // MXFP8 byte order inside a fragment (see preshuffle_kernel)
 };
 hipError_t launch_preshuffle(const PreshuffleArgs& a, hipStream_t st);
+// The E8M0 block scales of the same matrices ([E][rows][K/32] codes, K_bytes =
+// K for e4m3fn) into the order the GEMM reads them: per expert, groups of four
+// 32-row blocks, then reduction fragment (64 values), then lane l (row l%32 of
+// each block, 32-value block l/32 of the fragment), then the four blocks.
+hipError_t launch_preshuffle_mx_scales(const PreshuffleArgs& a, hipStream_t st);
 
 // Kernel configuration of a grouped GEMM stage, chosen on the host from the
 // shapes; the same choice sizes the FP8 amax partials.
@@ -69,6 +76,8 @@ struct GemmArgs {
   const float* x_scale;    // FP8: per-token (stage 1) or per-row (stage 2) activation scale
   const uint8_t* W;        // preshuffled weights
   const float* w_scale;    // FP8: s13 [E][2][I] (stage 1) or s2 [E][H] (stage 2)
+  const uint8_t* x_mx;     // MXFP8: E8M0 codes of X's rows, [rows of X][K/32]
+  const uint8_t* w_mx;     // MXFP8: preshuffled E8M0 weight codes (launch_preshuffle_mx_scales)
   const int32_t* sorted_slot;
   const int32_t* tile_expert;
   const int32_t* total_padded;
@@ -111,6 +120,23 @@ struct QuantArgs {
   float* act_scale;        // [cap]
 };
 hipError_t launch_quant_act(const QuantArgs& a, hipStream_t st);
+
+// MXFP8 stage 2 prologue: the MX block quantisation of every row p < total of
+// the bf16 intermediate (32 values per E8M0 code).
+struct QuantMxArgs {
+  const uint16_t* act;     // bf16 [cap][I]
+  int cap, I;
+  const int32_t* total_padded;
+  uint8_t* act_q;          // [cap][I] e4m3fn codes
+  uint8_t* act_mx;         // [cap][I/32] E8M0 codes
+};
+hipError_t launch_quant_act_mx(const QuantMxArgs& a, hipStream_t st);
+
+// Token-scale tile of the MXFP8 GEMMs: the E8M0 columns (32 reduction values
+// each) a workgroup covers, plus 16 for alignment. Stage 1 reduces over H
+// (at most 8192), stage 2 over I (at most 16384).
+constexpr int kMxMaxH = 8192;
+constexpr int kMxMaxI = 16384;
 
 // out[t,:] = bf16(sum_j sum_g part[g][t*k+j,:]), j ascending, then g ascending.
 struct CombineArgs {

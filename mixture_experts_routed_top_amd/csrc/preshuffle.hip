@@ -7,6 +7,10 @@
 // lane l (16 bytes at l*16) holds row l%32 and reduction bytes
 // (l/32)*32 + pc*16 .. +15, so a wave loads one piece as one contiguous,
 // fully coalesced block and each lane receives exactly its operand register.
+// MXFP8 uses bytes pc*32 + (l/32)*16 .. +15 instead: the scaled instruction
+// applies the scale of lane r (r < 32) to what lanes r and r+32 hold in their
+// first 16-byte piece and the scale of lane r+32 to their second pieces, so
+// each piece must be one 32-value block of the row.
 // Fragments are ordered by 32-row block, then by reduction block. For
 // gate/up, composite row c of an expert is row (c/64)*32 + c%32 of W1 when
 // (c/32) is even and of W3 when it is odd.
@@ -36,10 +40,48 @@ __global__ __launch_bounds__(256) void preshuffle_kernel(PreshuffleArgs a) {
       row = (c / 64) * 32 + c % 32;
       if ((c / 32) % 2) src = a.src1;
     }
-    const int64_t kbyte = kb * 64 + (lane / 32) * 32 + pc * 16;
+    const int64_t kbyte = kb * 64 + (a.mx_order ? pc * 32 + (lane / 32) * 16
+                                                : (lane / 32) * 32 + pc * 16);
     const int64_t sb = (e * rows_src + row) * a.K_bytes + kbyte;
     *reinterpret_cast<uint4*>(a.dst + b) = *reinterpret_cast<const uint4*>(src + sb);
   }
+}
+
+// MXFP8 weight scales: one E8M0 code per row and 32 reduction values. Output
+// byte o of an expert: j = o % 4 (which of four row blocks), lane = (o/4) % 64,
+// fragment kb = (o/256) % KB, block group g = o / (256*KB); it is the code of
+// composite row (4g + j)*32 + lane%32, value block 2*kb + lane/32. A lane of a
+// GEMM wave then loads the codes of its four (or two) row blocks for one
+// fragment as one 32-bit (16-bit) word, and the matrix-core instruction picks
+// the byte.
+__global__ __launch_bounds__(256) void preshuffle_mx_scales_kernel(PreshuffleArgs a) {
+  const int64_t nb = a.K_bytes / 32;               // codes per row
+  const int64_t kblocks = a.K_bytes / 64;
+  const int64_t per_expert = (int64_t)a.R * nb;
+  const int64_t n = per_expert * a.E;
+  const int64_t rows_src = a.src1 ? a.R / 2 : a.R;
+  for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < n;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = o / per_expert, rem = o % per_expert;
+    const int j = (int)(rem % 4), lane = (int)(rem / 4 % 64);
+    const int64_t kb = rem / 256 % kblocks, g = rem / (256 * kblocks);
+    const int64_t c = (4 * g + j) * 32 + lane % 32;
+    const uint8_t* src = a.src0;
+    int64_t row = c;
+    if (a.src1) {
+      row = (c / 64) * 32 + c % 32;
+      if ((c / 32) % 2) src = a.src1;
+    }
+    a.dst[o] = src[(e * rows_src + row) * nb + 2 * kb + lane / 32];
+  }
+}
+
+hipError_t launch_preshuffle_mx_scales(const PreshuffleArgs& a, hipStream_t st) {
+  int64_t n = (int64_t)a.R * (a.K_bytes / 32) * a.E;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(preshuffle_mx_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_preshuffle(const PreshuffleArgs& a, hipStream_t st) {

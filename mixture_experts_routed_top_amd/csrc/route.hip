@@ -1,6 +1,7 @@
-// Router logits, top-k, renormalised routing weights and the per-token FP8
-// quantisation of x (the top-2 routing of the Mixtral layer in the FlyDSL-in-JAX
-// talk summary, 8:14).
+// Router logits, top-k, renormalised routing weights and the per-token FP8 or
+// per-block MXFP8 quantisation of x (the top-2 routing of the Mixtral layer in
+// the FlyDSL-in-JAX talk summary, 8:14; the MX format of the PyTorch FlyDSL
+// backend summary, "Einschraenkungen").
 //
 // Fixed logit order (part of the layer's contract, so that ids can be compared
 // bit for bit): element h goes to partial (h/8) mod 64; each partial adds its
@@ -154,6 +155,48 @@ __device__ __forceinline__ void quantise_row(const RouteArgs& a, int t, int lane
   }
 }
 
+// MX block quantisation of the token row (MXFP8): each block of 32 values is
+// four consecutive 8-value chunks, held by four adjacent lanes (chunk c on lane
+// c mod 64), so the block maximum is two lane exchanges away. H is a multiple
+// of 128, so the four lanes of a block are all in range or all out.
+template <int NCH>
+__device__ __forceinline__ void quantise_row_mx(const RouteArgs& a, int t, int lane, int nchunk,
+                                                const uint4 (&xv)[NCH]) {
+  uint8_t* qr = a.x_q + (size_t)t * a.H;
+  uint8_t* sr = a.x_mx + (size_t)t * (a.H / 32);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    float xf[8];
+    unpack8(xv[i], xf);  // zeros past the row (load_row)
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(xf[j]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const int x = mx_exponent(m);
+    const float inv = mx_inv_scale(x);
+    if (c < nchunk) {
+      const uint32_t lo = f32x4_to_e4m3(clamp448(xf[0] * inv), clamp448(xf[1] * inv),
+                                        clamp448(xf[2] * inv), clamp448(xf[3] * inv));
+      const uint32_t hi = f32x4_to_e4m3(clamp448(xf[4] * inv), clamp448(xf[5] * inv),
+                                        clamp448(xf[6] * inv), clamp448(xf[7] * inv));
+      *reinterpret_cast<uint2*>(qr + (size_t)c * 8) = make_uint2(lo, hi);
+      if ((lane & 3) == 0) sr[c / 4] = (uint8_t)(x + 127);
+    }
+  }
+}
+
+// Per-token (FP8) or per-block (MXFP8) quantisation of the row.
+template <int NCH>
+__device__ __forceinline__ void quantise(const RouteArgs& a, int t, int lane, int nchunk,
+                                         const uint4 (&xv)[NCH]) {
+  if (a.x_mx)
+    quantise_row_mx<NCH>(a, t, lane, nchunk, xv);
+  else
+    quantise_row<NCH>(a, t, lane, nchunk, xv);
+}
+
 template <int NCH>
 __device__ __forceinline__ void load_row(const uint16_t* xr, int lane, int nchunk,
                                          uint4 (&xv)[NCH]) {
@@ -181,7 +224,7 @@ __global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
     __syncthreads();
     if (wave == 0) {
       select_topk(a, t, lane, lane < a.E ? logit[lane] : -__builtin_inff());
-      if (a.x_q) quantise_row<NCH>(a, t, lane, nchunk, xv);
+      if (a.x_q) quantise<NCH>(a, t, lane, nchunk, xv);
     }
     __syncthreads();
   }
@@ -248,7 +291,7 @@ __global__ __launch_bounds__(256) void route_wave_kernel(RouteArgs a) {
       }
     }
     select_topk(a, t, lane, mine);
-    if (a.x_q) quantise_row<NCH>(a, t, lane, nchunk, xv);
+    if (a.x_q) quantise<NCH>(a, t, lane, nchunk, xv);
   }
 }
 

@@ -138,3 +138,34 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_mxfp8_size_queries_and_checks():
+    L = _lib.lib()
+    E, H, I = 8, 4096, 14336
+    assert L.moe_preshuffle_bytes(2, E, H, I, 0) == 2 * E * I * H            # one byte per value
+    assert L.moe_preshuffle_bytes(2, E, H, I, 2) == 2 * E * I * (H // 32)    # one code per 32
+    assert L.moe_preshuffle_bytes(2, E, H, I, 3) == E * H * (I // 32)
+    assert L.moe_preshuffle_bytes(1, E, H, I, 2) == 2 * E * I * 4            # fp32 per row
+    assert L.moe_preshuffle_bytes(0, E, H, I, 3) == 0
+    assert L.moe_stage1_amax_floats(2, 8192, 2, E, H, I, 128) == 0          # no row maxima
+    cap = L.moe_align_capacity(16, 2, E, 32)
+    need = L.moe_stage2_workspace_bytes(2, 16, 2, E, H, I, 32)
+    up = lambda b: (b + 255) // 256 * 256
+    assert need >= up(16 * 2 * H * 4) + up(cap * I) + up(cap * I // 32)
+    # MXFP8 limits: H <= 8192 (stage 1 token-code tile), I <= 16384
+    s1 = [2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 8, 4096, 14336, 32, FAKE, None, None]
+    a = list(s1); a[11] = 8192 + 256
+    assert status("moe_stage1", *a) == _lib.ERR_UNSUPPORTED
+    a = list(s1); a[12] = 16384 + 256
+    assert status("moe_stage1", *a) == _lib.ERR_UNSUPPORTED
+    a = list(s1); a[2] = None
+    assert status("moe_stage1", *a) == _lib.ERR_INVALID_ARG          # block codes of x missing
+    a = list(s1); a[2] = FAKE + 4
+    assert status("moe_stage1", *a) == _lib.ERR_INVALID_ARG          # x codes 8-byte aligned
+    r = [FAKE, FAKE, None, 4, 4096, 8, 2, FAKE, FAKE, None, FAKE, None, None]
+    assert status("moe_route_mx", *r) == _lib.ERR_INVALID_ARG         # codes output missing
+    a = list(r); a[4] = 4096 + 64
+    assert status("moe_route_mx", *a) == _lib.ERR_UNSUPPORTED         # H % 128
+    a = list(r); a[3] = 0; a[10] = None
+    assert status("moe_route_mx", *a) == _lib.OK

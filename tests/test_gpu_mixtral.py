@@ -32,6 +32,9 @@ def check_full(wl, n_sample, inp=None):
     if wl.dtype == "fp8":
         oq, os_ = oracle.quant_tokens(inp.x)
         assert np.array_equal(host(up.layer.xq), oq) and np.array_equal(host(up.layer.xs), os_)
+    if wl.dtype == "mxfp8":
+        oq, os_ = oracle.quant_tokens_mx(inp.x)
+        assert np.array_equal(host(up.layer.xq), oq) and np.array_equal(host(up.layer.xs), os_)
     toks = sample_tokens(oid, wl.E, n_sample)
     say(f"{wl.name}: oracle on {toks.size} tokens")
     _, o64 = oracle.forward(inp, toks)
@@ -69,3 +72,12 @@ def test_mixtral_fp8_decode_sweep():
 
 def test_mixtral_fp8_skewed_T16384():
     check_full(workloads.config(4), 48)
+
+
+def test_mixtral_mxfp8_prefill_T8192_and_decode_T16():
+    base = check_full(workloads.mxfp8(8192), 32)
+    wl = workloads.mxfp8(16)
+    xi = workloads.generate(wl, weights=False)
+    inp = workloads.Inputs(wl, xi.x, base.w_router, None, base.w1, base.w3, base.w2, base.s1,
+                           base.s3, base.s2)
+    check_full(wl, 8, inp)
