@@ -20,6 +20,9 @@ The same line carries:
   bf16_decode   the same for the BF16 decode batch T=16;
   skewed        the FP8 skewed workload (T=16384, ~40% of slots on expert 0):
                 latency, effective TFLOP/s, slots and row tiles per expert, pad rows;
+  mxfp8         the MXFP8 layer (E8M0 scale per 32 values): prefill T=8192 (whole
+                layer and stage-1 kernel TFLOP/s) and the decode batch T=16 measured
+                like the FP8 sweep;
   cpu_baseline  the CPU oracle on the first tokens of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-sweep]
@@ -217,6 +220,52 @@ def skewed(steps):
             "pad_fraction": round((total - wl.slots) / total, 4)}
 
 
+def timed_steps(layer, x, steps):
+    """Mean whole-layer ms over `steps` back-to-back calls and the mean stage-1 kernel ms
+    (HIP events on the stream the stages run on)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        layer(x, events=ev[i])
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def mxfp8(steps, runs):
+    """The MXFP8 layer at the Mixtral shape: prefill T=8192 and decode T=16."""
+    import torch
+    import workloads
+    wl = workloads.mxfp8(8192)
+    inp = workloads.generate(wl, threads=16)
+    layer = make_layer(inp)
+    x = dev(inp.x)
+    for _ in range(3):
+        layer(x)
+    ms, s1_ms = timed_steps(layer, x, steps)
+    tf = wl.flops() / (ms * 1e-3) / 1e12
+    s1_tf = 4.0 * wl.H * wl.I * wl.slots / (s1_ms * 1e-3) / 1e12
+    log(f"[bench] {wl.name}: {ms:.3f} ms, {tf:.0f} TFLOP/s; stage 1 {s1_ms:.3f} ms")
+    prefill = {"workload": wl.name, "T": wl.T, "block_m": layer.bm, "ms": round(ms, 4),
+               "tflops": round(tf, 2), "frac_of_fp8_peak": round(tf / PEAK["fp8"], 4),
+               "tokens_per_s": round(wl.T / (ms * 1e-3), 1),
+               "stage1_ms": round(s1_ms, 4), "stage1_tflops": round(s1_tf, 2),
+               "stage1_frac": round(s1_tf / PEAK["fp8"], 4)}
+    wd = workloads.mxfp8(16)
+    flush = flush_buffer()
+    dec = decode_line(wd, layer, dev(workloads.generate(wd, weights=False).x), runs, flush,
+                      1.0 + 1.0 / 32.0)  # codes plus one E8M0 byte per 32
+    dec = {"workload": wd.name, **dec}
+    del layer, flush
+    torch.cuda.empty_cache()
+    return {"prefill": prefill, "decode": dec}
+
+
 def traffic_from(fetch_db, write_db):
     """Stage-1 HBM bytes per launch from two rocprofv3 --pmc databases (FETCH_SIZE,
     WRITE_SIZE, in KiB per dispatch), each scaled by the same counter's reading for the
@@ -298,18 +347,7 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: K whole-layer steps; stage 1 bracketed by events on the same stream.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        layer(x, events=ev[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
-    s1_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms, s1_ms = timed_steps(layer, x, args.steps)
     log(f"[bench] {ms:.3f} ms/step, stage-1 kernel {s1_ms:.3f} ms")
 
     tflops = wl.flops() / (ms * 1e-3) / 1e12
@@ -356,6 +394,7 @@ def main():
         rec["decode_sweep"] = decode_sweep(args.decode_runs)
         rec["bf16_decode"] = bf16_decode(args.decode_runs)
         rec["skewed"] = skewed(max(5, args.steps // 2))
+        rec["mxfp8"] = mxfp8(max(5, args.steps // 2), args.decode_runs)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
