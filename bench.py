@@ -29,6 +29,7 @@ The same line carries:
                     [--no-cpu-baseline] [--cpu-tokens 64] [--copy-calibration]
                     [--decode-runs 100]
     python bench.py --decode-only T [--decode-runs N]   (one FP8 decode batch)
+    python bench.py --mxfp8-only [--steps K]           (the MXFP8 lines only)
     python bench.py --traffic-from FETCH.db WRITE.db   (writes the traffic summary)
 """
 from __future__ import annotations
@@ -312,6 +313,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
+    ap.add_argument("--mxfp8-only", action="store_true",
+                    help="only the MXFP8 prefill and decode lines (for profiler runs)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
@@ -323,6 +326,10 @@ def main():
 
     import torch
     import workloads
+
+    if args.mxfp8_only:
+        print(json.dumps({"mxfp8": mxfp8(args.steps, args.decode_runs)}), flush=True)
+        return
 
     if args.decode_only is not None:
         wl = workloads.config(3, args.decode_only)

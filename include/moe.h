@@ -17,9 +17,9 @@
  * Shapes: x[T,H] tokens, W_r[E,H] router, W1/W3[E,I,H] gate/up, W2[E,H,I] down,
  * top-k with k <= E. Element types: bf16; OCP e4m3fn ("FP8", the precision the
  * talk summary's Mixtral 8x7B kernel runs in, 5:56/7:31) with fp32 scales; or
- * MXFP8 (the second page's scaled-GEMM format, "Einschraenkungen": e4m3fn values
- * with one E8M0 scale per 32 values along the reduction; scale code b means
- * 2^(b-127)). MXFP8 block scales are chosen as in the OCP Microscaling
+ * MXFP8 (the second page's scaled-GEMM format, section "Grenzen und Folgen
+ * für Anwender": e4m3fn values with one E8M0 scale per 32 values along the
+ * reduction; scale code b means 2^(b-127)). MXFP8 block scales are chosen as in the OCP Microscaling
  * specification: x = floor(log2 max|v|) - 8 (0 for an all-zero block), clamped
  * to [-127, 127], code x + 127; values e4m3fn(clamp(v / 2^x, -448, 448)).
  *
@@ -98,7 +98,8 @@ moe_status moe_route(const void* x, const void* w_router, const float* bias, int
 
 /*
  * moe_route_mx - moe_route with the MXFP8 quantisation of x instead of the
- * per-token one (the block format of the second page, "Einschraenkungen").
+ * per-token one (the block format of the second page, section "Grenzen und
+ * Folgen für Anwender").
  * Routing (ids, weights, logits) is exactly moe_route's. Then, for every token
  * t and block b of 32 consecutive hidden values: x = floor(log2 max|x[t, 32b..
  * 32b+31]|) - 8 (0 if that block is all zero), clamped to [-127, 127];

@@ -1,7 +1,7 @@
 // Router logits, top-k, renormalised routing weights and the per-token FP8 or
 // per-block MXFP8 quantisation of x (the top-2 routing of the Mixtral layer in
 // the FlyDSL-in-JAX talk summary, 8:14; the MX format of the PyTorch FlyDSL
-// backend summary, "Einschraenkungen").
+// backend news item, "Grenzen und Folgen für Anwender").
 //
 // Fixed logit order (part of the layer's contract, so that ids can be compared
 // bit for bit): element h goes to partial (h/8) mod 64; each partial adds its

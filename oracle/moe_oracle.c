@@ -24,9 +24,9 @@
  * SwiGLU intermediate on the bf16 path, the per-row e4m3fn requantisation of the
  * intermediate on the fp8 path, and the bf16 output.
  *
- * MXFP8 path (the second page, the PyTorch FlyDSL backend summary, section
- * "Einschraenkungen": E4M3 operands with one E8M0 scale per 32 values along the
- * reduction, K a multiple of 128). The pages fix only the format; how a block's
+ * MXFP8 path (the second page, the PyTorch FlyDSL backend news item, section
+ * "Grenzen und Folgen für Anwender": E4M3 operands with one E8M0 scale per 32
+ * values along the reduction, K a multiple of 128). The pages fix only the format; how a block's
  * scale is chosen is the OCP Microscaling specification's conversion, the
  * plainest reading: scale = 2^(floor(log2 max|v|) - 8), 8 being the exponent of
  * E4M3's largest normal, elements rounded to nearest even and saturated at 448.

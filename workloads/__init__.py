@@ -16,10 +16,11 @@ Weight quantisation for the fp8 workloads (one fp32 scale per output channel,
 scale = amax/448, codes by round-to-nearest-even with saturation) is load-time
 input preparation, done here with torch's float8_e4m3fn cast. It is not part of
 the hot path: the library's entry points take the codes and scales as inputs.
-The MXFP8 workloads (the second page, the PyTorch FlyDSL backend summary,
-"Einschraenkungen": E4M3 values with one E8M0 scale per 32 along the reduction;
-its measurements start from quantised operands) store the weights the same way
-per 32-value block of each row, with the OCP MX scale 2^(floor(log2 amax) - 8).
+The MXFP8 workloads (the second page, the PyTorch FlyDSL backend news item,
+"Grenzen und Folgen für Anwender": E4M3 values with one E8M0 scale per 32 along
+the reduction; its "Gemessene Leistung" measurements start from quantised
+operands) store the weights the same way per 32-value block of each row, with
+the OCP MX scale 2^(floor(log2 amax) - 8).
 """
 from __future__ import annotations
 
