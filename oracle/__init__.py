@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "moe_oracle.c")
 
-BF16, FP8, MXFP8 = 0, 1, 2
+BF16, FP8, MXFP8, MXFP4 = 0, 1, 2, 3
 
 
 def build() -> str:
@@ -67,7 +67,8 @@ def lib():
         L.oracle_preshuffle_w2.argtypes = [i, i, i, i, P, P]
         L.oracle_threads.restype = ctypes.c_int
         for name in ("oracle_f32_to_e4m3fn_n", "oracle_e4m3fn_to_f64_n",
-                     "oracle_f32_to_bf16_n", "oracle_bf16_to_f64_n", "oracle_e8m0_to_f64_n"):
+                     "oracle_f32_to_bf16_n", "oracle_bf16_to_f64_n", "oracle_e8m0_to_f64_n",
+                     "oracle_e2m1_to_f64_n", "oracle_f32_to_e2m1_n"):
             getattr(L, name).argtypes = [P, ctypes.c_long, P]
         _lib = L
     return _lib
@@ -81,7 +82,7 @@ def _p(a):
 
 
 def _dt(dtype: str) -> int:
-    return {"bf16": BF16, "fp8": FP8, "mxfp8": MXFP8}[dtype]
+    return {"bf16": BF16, "fp8": FP8, "mxfp8": MXFP8, "mxfp4": MXFP4}[dtype]
 
 
 # --- number formats --------------------------------------------------------
@@ -111,6 +112,15 @@ def f32_to_e4m3fn(f: np.ndarray) -> np.ndarray:
 
 def e8m0_to_f64(b: np.ndarray) -> np.ndarray:
     return _conv(lib().oracle_e8m0_to_f64_n, b, np.uint8, np.float64)
+
+
+def e2m1_to_f64(q: np.ndarray) -> np.ndarray:
+    """E2M1 codes (low 4 bits of each byte) -> values."""
+    return _conv(lib().oracle_e2m1_to_f64_n, q, np.uint8, np.float64)
+
+
+def f32_to_e2m1(f: np.ndarray) -> np.ndarray:
+    return _conv(lib().oracle_f32_to_e2m1_n, f, np.float32, np.uint8)
 
 
 # --- router ----------------------------------------------------------------
@@ -215,7 +225,7 @@ def down(dtype, act, w2, s2, experts):
     """Down projection of intermediate rows act[n, I] (fp64 values) -> fp64 [n, H]."""
     act = np.ascontiguousarray(act, np.float64)
     experts = np.ascontiguousarray(experts, np.int32)
-    E, H, I = w2.shape
+    H, I = w2.shape[1], act.shape[1]  # w2 rows hold I values (I/2 bytes for packed E2M1)
     y = np.empty((experts.size, H), np.float64)
     lib().oracle_down(_dt(dtype), _p(act), _p(w2), _p(s2), H, I, _p(experts), experts.size, _p(y))
     return y

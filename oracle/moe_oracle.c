@@ -34,6 +34,11 @@
  * token rows are block-quantised on the path, and the SwiGLU intermediate is
  * stored in bf16 and block-quantised again for the down projection.
  *
+ * MXFP4 path (same page and section: "packed FP4-E2M1 operands" with the same
+ * E8M0 scale per 32 values): the expert weights are E2M1 codes, two per byte
+ * (value 2i in the low nibble of byte i), with E8M0 block scales; tokens and
+ * the intermediate are MXFP8 exactly as above.
+ *
  * Each function is plain loops; OpenMP only splits independent output rows.
  */
 #include <math.h>
@@ -44,7 +49,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_BF16 = 0, ORACLE_FP8 = 1, ORACLE_MXFP8 = 2 };
+enum { ORACLE_BF16 = 0, ORACLE_FP8 = 1, ORACLE_MXFP8 = 2, ORACLE_MXFP4 = 3 };
 
 enum { MX_BLOCK = 32 }; /* values per E8M0 scale along the reduction */
 
@@ -160,10 +165,41 @@ static uint8_t mx_block(const float* v, int n, uint8_t* q)
     return (uint8_t)(x + 127);
 }
 
+/* OCP 4-bit float E2M1: 1 sign bit, 2 exponent bits with bias 1, 1 mantissa
+ * bit; exponent field 0 is subnormal (m * 0.5). Magnitudes 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6; no infinity or NaN. Only the low 4 bits of q are read. */
+double oracle_e2m1_to_f64(uint8_t q)
+{
+    int s = (q >> 3) & 1, e = (q >> 1) & 3, m = q & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* Nearest E2M1 code to v, ties to the even code; |v| beyond 6 saturates. */
+uint8_t oracle_f32_to_e2m1(float v)
+{
+    uint8_t sign = signbit(v) ? 0x8 : 0x0;
+    double a = fabs((double)v);
+    if (isnan(v) || a >= 6.0)
+        return sign | 0x7;
+    int best = 0;
+    double bd = a;
+    for (int c = 1; c < 8; ++c) {
+        double d = fabs(a - oracle_e2m1_to_f64((uint8_t)c));
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
 static double wval(int dtype, const void* w, size_t idx)
 {
     if (dtype == ORACLE_BF16)
         return oracle_bf16_to_f64(((const uint16_t*)w)[idx]);
+    if (dtype == ORACLE_MXFP4)
+        return oracle_e2m1_to_f64((uint8_t)(((const uint8_t*)w)[idx / 2] >> (4 * (idx % 2))));
     return oracle_e4m3fn_to_f64(((const uint8_t*)w)[idx]);
 }
 
@@ -174,7 +210,7 @@ static double wscale(int dtype, const void* s, size_t row, int col, int K)
 {
     if (dtype == ORACLE_FP8)
         return (double)((const float*)s)[row];
-    if (dtype == ORACLE_MXFP8)
+    if (dtype == ORACLE_MXFP8 || dtype == ORACLE_MXFP4)
         return oracle_e8m0_to_f64(((const uint8_t*)s)[row * (size_t)(K / MX_BLOCK) + col / MX_BLOCK]);
     return 1.0;
 }
@@ -357,7 +393,7 @@ static void token_row(int dtype, const uint16_t* x, int t, int H, double* xh)
         return;
     }
     uint8_t* q = (uint8_t*)malloc((size_t)H);
-    if (dtype == ORACLE_MXFP8) {
+    if (dtype == ORACLE_MXFP8 || dtype == ORACLE_MXFP4) {
         uint8_t* sb = (uint8_t*)malloc((size_t)H / MX_BLOCK);
         oracle_quant_tokens_mx(r, 1, H, q, sb);
         for (int h = 0; h < H; ++h)
@@ -404,7 +440,7 @@ static void store_intermediate(int dtype, double* a, int I)
             a[i] = oracle_bf16_to_f64(oracle_f32_to_bf16((float)a[i]));
         return;
     }
-    if (dtype == ORACLE_MXFP8) {
+    if (dtype == ORACLE_MXFP8 || dtype == ORACLE_MXFP4) {
         float v[MX_BLOCK];
         uint8_t q[MX_BLOCK];
         for (int b = 0; b < I / MX_BLOCK; ++b) {
@@ -583,6 +619,18 @@ int oracle_threads(void)
 }
 
 /* Array forms of the format conversions (same definitions, element by element). */
+void oracle_e2m1_to_f64_n(const uint8_t* q, long n, double* v)
+{
+    for (long i = 0; i < n; ++i)
+        v[i] = oracle_e2m1_to_f64(q[i]);
+}
+
+void oracle_f32_to_e2m1_n(const float* v, long n, uint8_t* q)
+{
+    for (long i = 0; i < n; ++i)
+        q[i] = oracle_f32_to_e2m1(v[i]);
+}
+
 void oracle_e8m0_to_f64_n(const uint8_t* b, long n, double* v)
 {
     for (long i = 0; i < n; ++i)

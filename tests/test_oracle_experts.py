@@ -39,7 +39,20 @@ def _mx_quant(a):
     return _fp8_f64(codes) * np.exp2(x).repeat(32, axis=1)
 
 
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0,
+                  -4.0, -6.0])  # the OCP E2M1 values by code
+
+
+def _fp4_f64(packed):
+    """Packed E2M1 codes (value 2i in the low nibble of byte i) -> values by table lookup."""
+    codes = np.stack([packed & 15, packed >> 4], -1).reshape(*packed.shape[:-1], -1)
+    return _E2M1[codes]
+
+
 def deq_weights(inp):
+    if inp.wl.dtype == "mxfp4":
+        return tuple(_fp4_f64(w) * _e8m0_f64(s).repeat(32, axis=2)
+                     for w, s in ((inp.w1, inp.s1), (inp.w3, inp.s3), (inp.w2, inp.s2)))
     if inp.wl.dtype == "bf16":
         return _bf16_f64(inp.w1), _bf16_f64(inp.w3), _bf16_f64(inp.w2)
     if inp.wl.dtype == "mxfp8":
@@ -53,7 +66,7 @@ def token_inputs(inp):
     x = _bf16_f64(inp.x)
     if inp.wl.dtype == "bf16":
         return x
-    if inp.wl.dtype == "mxfp8":
+    if inp.wl.dtype in ("mxfp8", "mxfp4"):
         return _mx_quant(x)
     xf = x.astype(np.float32)
     amax = np.abs(xf).max(1)
@@ -65,7 +78,7 @@ def token_inputs(inp):
 def store(dtype, a):
     if dtype == "bf16":
         return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).double().numpy()
-    if dtype == "mxfp8":  # bf16 storage, then the block quantisation
+    if dtype in ("mxfp8", "mxfp4"):  # bf16 storage, then the MXFP8 block quantisation
         return _mx_quant(torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).double().numpy())
     amax = np.abs(a).max(1, keepdims=True)
     s = np.where(amax > 0, amax / 448.0, 1.0)
@@ -98,7 +111,7 @@ def small(dtype, E, k, T=24, H=256, I=384, seed=9, bias=None):
     return inp
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8", "mxfp4"])
 def test_single_expert_equals_swiglu_mlp(dtype):
     inp = small(dtype, E=1, k=1)
     out, o64 = oracle.forward(inp)
@@ -109,7 +122,7 @@ def test_single_expert_equals_swiglu_mlp(dtype):
     assert np.mean(out.view(np.int16) == ref_b) > 0.999
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8", "mxfp4"])
 def test_dense_then_mask_equals_routed(dtype):
     wl = workloads.config(0)
     if dtype != "bf16":
@@ -157,8 +170,9 @@ def test_doubling_down_weights_doubles_output_exactly():
     assert np.array_equal(o64b, 2.0 * o64)
 
 
-def test_mx_down_scale_code_plus_one_doubles_output_exactly():
-    inp = small("mxfp8", E=4, k=2)
+@pytest.mark.parametrize("dtype", ["mxfp8", "mxfp4"])
+def test_mx_down_scale_code_plus_one_doubles_output_exactly(dtype):
+    inp = small(dtype, E=4, k=2)
     _, o64 = oracle.forward(inp)
     assert np.all(inp.s2 < 254)
     inp.s2 = (inp.s2 + 1).astype(np.uint8)
@@ -180,7 +194,7 @@ def test_mx_gate_scale_block_is_used_per_32_columns():
     assert rel(o64, o64_0) > 1e-3
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8", "mxfp4"])
 def test_swiglu_and_down_rows(dtype):
     inp = small(dtype, E=4, k=2)
     xh = token_inputs(inp)

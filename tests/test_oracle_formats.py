@@ -178,3 +178,54 @@ def test_mx_quant_is_blockwise_and_scale_equivariant():
     keep[64:96] = False
     assert np.array_equal(q2[:, keep], q[:, keep])
     assert np.array_equal(np.delete(s2, 2, axis=1), np.delete(s, 2, axis=1))
+
+
+# --- E2M1 (MXFP4 elements) ----------------------------------------------------
+
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # OCP MX specification's E2M1 values
+
+
+def test_e2m1_decode_all_codes_match_the_published_table():
+    vals = oracle.e2m1_to_f64(np.arange(16, dtype=np.uint8))
+    assert list(vals[:8]) == E2M1_TABLE
+    assert list(-vals[8:]) == E2M1_TABLE and np.all(np.signbit(vals[8:]))
+    # only the low nibble is read
+    assert np.array_equal(oracle.e2m1_to_f64(np.arange(16, dtype=np.uint8) | 0xF0), vals)
+
+
+def test_e2m1_encode_is_nearest_ties_to_even_bruteforce():
+    tab = np.array(E2M1_TABLE)
+    mids = (tab[:-1] + tab[1:]) / 2
+    rng = np.random.default_rng(5)
+    v = np.concatenate([tab, mids, np.nextafter(mids, 0), np.nextafter(mids, 9),
+                        rng.uniform(0, 6, 20000), [0.0]]).astype(np.float32)
+    v = np.concatenate([v, -v])
+    ours = oracle.f32_to_e2m1(v).astype(int)
+    for x, q in zip(v.astype(np.float64), ours):
+        d = np.abs(tab - abs(x))
+        cand = np.nonzero(d == d.min())[0]
+        if len(cand) > 1:
+            cand = cand[cand % 2 == 0]
+        assert q == int(cand[0]) | (8 if np.signbit(x) else 0), (x, q)
+
+
+def test_e2m1_encode_saturates():
+    v = np.array([6.0, 6.5, 100.0, -7.0, np.inf], np.float32)
+    assert list(oracle.f32_to_e2m1(v)) == [7, 7, 7, 15, 7]
+
+
+def test_mx4_weight_storage_matches_the_oracle_encoder():
+    import workloads
+    rng = np.random.default_rng(6)
+    a = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    a[3, :32] = 0.0
+    packed, s = workloads.quantize_blocks_mx4(a)
+    codes = np.stack([packed & 15, packed >> 4], -1).reshape(16, 256)
+    scale = oracle.e8m0_to_f64(s).repeat(32, 1)
+    ref = oracle.f32_to_e2m1((a / scale).astype(np.float32))  # a / 2^x is exact
+    assert np.array_equal(codes, ref)
+    assert s[3, 0] == 127
+    # block maxima land in the top binade [4, 6] (saturating above 6)
+    big = np.abs(oracle.e2m1_to_f64(codes)).reshape(16, 8, 32).max(2)
+    live = np.abs(a).reshape(16, 8, 32).max(2) > 0
+    assert np.all((big[live] >= 4) & (big[live] <= 6))

@@ -20,7 +20,9 @@ The MXFP8 workloads (the second page, the PyTorch FlyDSL backend news item,
 "Grenzen und Folgen für Anwender": E4M3 values with one E8M0 scale per 32 along
 the reduction; its "Gemessene Leistung" measurements start from quantised
 operands) store the weights the same way per 32-value block of each row, with
-the OCP MX scale 2^(floor(log2 amax) - 8).
+the OCP MX scale 2^(floor(log2 amax) - 8). The MXFP4 workloads (same section:
+"packed FP4-E2M1 operands") store E2M1 weight codes, two per byte, with the
+scale 2^(floor(log2 amax) - 2) (6 = 1.5 * 2^2 is E2M1's largest value).
 """
 from __future__ import annotations
 
@@ -45,7 +47,7 @@ class Workload:
     I: int
     E: int
     k: int
-    dtype: str            # "bf16", "fp8" or "mxfp8"
+    dtype: str            # "bf16", "fp8", "mxfp8" or "mxfp4" (weights; tokens mxfp8)
     sigma_x: float
     sigma_r: float
     sigma_w: float
@@ -86,6 +88,14 @@ def config(i: int, T: int | None = None) -> Workload:
 
 
 DECODE_SWEEP = (1, 4, 16, 64, 256)
+
+
+def mxfp4(T: int) -> Workload:
+    """The Mixtral expert layer with MXFP4 expert weights (and MXFP8 tokens) at batch T;
+    weights and router drawn like the fp8 workloads, seed 6."""
+    m = MIXTRAL
+    return Workload(f"mixtral-mxfp4-T{T}", int(T), m["H"], m["I"], m["E"], m["k"], "mxfp4",
+                    1.0, 1.0 / 64.0, 0.02, 6, x_seed=(int(T),))
 
 
 def mxfp8(T: int) -> Workload:
@@ -146,6 +156,33 @@ def quantize_blocks_mx(a: np.ndarray, block: int = 32):
     return q.numpy(), (x + 127).to(torch.uint8).numpy()
 
 
+_E2M1_MID = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)  # between E2M1 values
+
+
+def quantize_blocks_mx4(a: np.ndarray, block: int = 32):
+    """Per-block E2M1 codes (packed two per byte, value 2i in the low nibble of byte i)
+    and E8M0 scale codes along each row (OCP MX storage).
+
+    Block b of row r gets exponent x = floor(log2 amax) - 2 (0 for an all-zero block),
+    clamped to [-127, 127]; codes = nearest E2M1 value of clamp(a / 2^x, -6, 6), ties to
+    the even code (E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 are codes 0..7). Returns
+    (codes uint8 [R, C/2], scale codes uint8 [R, C/block])."""
+    a = np.ascontiguousarray(a, np.float32)
+    R, C = a.shape
+    b = a.reshape(R, C // block, block)
+    amax = np.abs(b).max(2)
+    _, ex = np.frexp(amax)  # amax = m * 2^ex, 0.5 <= m < 1
+    x = np.where(amax > 0, np.clip(ex - 3, -127, 127), 0)
+    v = np.clip(b * np.exp2(-x).astype(np.float32)[:, :, None], -6.0, 6.0).reshape(R, C)
+    mag = np.abs(v)
+    code = np.searchsorted(_E2M1_MID, mag, side="left")  # midpoints below |v|
+    tie = (code < 7) & (mag == _E2M1_MID[np.minimum(code, 6)])
+    code = (code + (tie & (code % 2 == 1))).astype(np.uint8)  # a tie goes to the even code
+    code |= np.signbit(v).astype(np.uint8) << 3
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (x + 127).astype(np.uint8)
+
+
 # ---------------------------------------------------------------------------
 
 @dataclass
@@ -155,9 +192,9 @@ class Inputs:
     x: np.ndarray            # uint16 bf16 [T, H]
     w_router: np.ndarray     # uint16 bf16 [E, H]
     bias: np.ndarray | None  # float32 [E] or None
-    w1: np.ndarray           # bf16 uint16 or e4m3fn uint8, [E, I, H] (gate)
+    w1: np.ndarray           # bf16 uint16 or e4m3fn uint8 [E, I, H] (gate); mxfp4 [E, I, H/2]
     w3: np.ndarray           # same, [E, I, H] (up)
-    w2: np.ndarray           # same, [E, H, I] (down)
+    w2: np.ndarray           # same, [E, H, I] (down); mxfp4 [E, H, I/2]
     s1: np.ndarray | None    # fp8: float32 [E, I]; mxfp8: E8M0 uint8 [E, I, H/32]
     s3: np.ndarray | None    # same as s1
     s2: np.ndarray | None    # fp8: float32 [E, H]; mxfp8: E8M0 uint8 [E, H, I/32]
@@ -210,16 +247,20 @@ def generate(wl: Workload, weights: bool = True, threads: int = 8) -> Inputs:
         if wl.dtype == "mxfp8":
             q, s = quantize_blocks_mx(a)
             return job, q, s
+        if wl.dtype == "mxfp4":
+            q, s = quantize_blocks_mx4(a)
+            return job, q, s
         q, s = quantize_rows_fp8(a)
         return job, q, s
 
     wdt = np.uint16 if wl.dtype == "bf16" else np.uint8
-    w1 = np.empty((E, I, H), wdt)
-    w3 = np.empty((E, I, H), wdt)
-    w2 = np.empty((E, H, I), wdt)
+    per = 2 if wl.dtype == "mxfp4" else 1  # values per stored element
+    w1 = np.empty((E, I, H // per), wdt)
+    w3 = np.empty((E, I, H // per), wdt)
+    w2 = np.empty((E, H, I // per), wdt)
     mats = (w1, w3, w2)
-    fp8 = wl.dtype in ("fp8", "mxfp8")
-    if wl.dtype == "mxfp8":
+    fp8 = wl.dtype in ("fp8", "mxfp8", "mxfp4")
+    if wl.dtype in ("mxfp8", "mxfp4"):
         s1 = np.empty((E, I, H // 32), np.uint8)
         s3 = np.empty((E, I, H // 32), np.uint8)
         s2 = np.empty((E, H, I // 32), np.uint8)
