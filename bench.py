@@ -23,6 +23,9 @@ The same line carries:
   mxfp8         the MXFP8 layer (E8M0 scale per 32 values): prefill T=8192 (whole
                 layer and stage-1 kernel TFLOP/s) and the decode batch T=16 measured
                 like the FP8 sweep;
+  mxfp4         the layer with MXFP4 (E2M1) expert weights and MXFP8 tokens: prefill
+                T=8192 and the decode sweep T = 1 .. 256, weight GB/s over the
+                active experts' codes and scales;
   cpu_baseline  the CPU oracle on the first tokens of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-sweep]
@@ -30,6 +33,7 @@ The same line carries:
                     [--decode-runs 100]
     python bench.py --decode-only T [--decode-runs N]   (one FP8 decode batch)
     python bench.py --mxfp8-only [--steps K]           (the MXFP8 lines only)
+    python bench.py --mxfp4-only [--steps K]           (the MXFP4 lines only)
     python bench.py --traffic-from FETCH.db WRITE.db   (writes the traffic summary)
 """
 from __future__ import annotations
@@ -238,11 +242,14 @@ def timed_steps(layer, x, steps):
     return t0.elapsed_time(t1) / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
-def mxfp8(steps, runs):
-    """The MXFP8 layer at the Mixtral shape: prefill T=8192 and decode T=16."""
+def mx_lines(kind, steps, runs, decode_ts):
+    """A block-scaled layer ("mxfp8" or "mxfp4") at the Mixtral shape: prefill T=8192
+    (whole layer and stage-1 kernel) and the decode batches decode_ts, measured like the
+    FP8 sweep over the active experts' weight bytes (codes plus one E8M0 byte per 32)."""
     import torch
     import workloads
-    wl = workloads.mxfp8(8192)
+    make_wl = getattr(workloads, kind)
+    wl = make_wl(8192)
     inp = workloads.generate(wl, threads=16)
     layer = make_layer(inp)
     x = dev(inp.x)
@@ -257,14 +264,28 @@ def mxfp8(steps, runs):
                "tokens_per_s": round(wl.T / (ms * 1e-3), 1),
                "stage1_ms": round(s1_ms, 4), "stage1_tflops": round(s1_tf, 2),
                "stage1_frac": round(s1_tf / PEAK["fp8"], 4)}
-    wd = workloads.mxfp8(16)
     flush = flush_buffer()
-    dec = decode_line(wd, layer, dev(workloads.generate(wd, weights=False).x), runs, flush,
-                      1.0 + 1.0 / 32.0)  # codes plus one E8M0 byte per 32
-    dec = {"workload": wd.name, **dec}
+    per_weight = (0.5 if kind == "mxfp4" else 1.0) + 1.0 / 32.0
+    dec = []
+    for T in decode_ts:
+        wd = make_wl(T)
+        rec = decode_line(wd, layer, dev(workloads.generate(wd, weights=False).x), runs, flush,
+                          per_weight)
+        dec.append({"workload": wd.name, **rec})
     del layer, flush
     torch.cuda.empty_cache()
-    return {"prefill": prefill, "decode": dec}
+    return {"prefill": prefill, "decode": dec[0] if len(dec) == 1 else dec}
+
+
+def mxfp8(steps, runs):
+    """The MXFP8 layer: prefill T=8192 and decode T=16."""
+    return mx_lines("mxfp8", steps, runs, (16,))
+
+
+def mxfp4(steps, runs):
+    """The MXFP4-weight layer: prefill T=8192 and the decode sweep T = 1 .. 256."""
+    import workloads
+    return mx_lines("mxfp4", steps, runs, workloads.DECODE_SWEEP)
 
 
 def traffic_from(fetch_db, write_db):
@@ -315,6 +336,8 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
     ap.add_argument("--mxfp8-only", action="store_true",
                     help="only the MXFP8 prefill and decode lines (for profiler runs)")
+    ap.add_argument("--mxfp4-only", action="store_true",
+                    help="only the MXFP4 prefill and decode lines (for profiler runs)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
@@ -329,6 +352,9 @@ def main():
 
     if args.mxfp8_only:
         print(json.dumps({"mxfp8": mxfp8(args.steps, args.decode_runs)}), flush=True)
+        return
+    if args.mxfp4_only:
+        print(json.dumps({"mxfp4": mxfp4(args.steps, args.decode_runs)}), flush=True)
         return
 
     if args.decode_only is not None:
@@ -402,6 +428,7 @@ def main():
         rec["bf16_decode"] = bf16_decode(args.decode_runs)
         rec["skewed"] = skewed(max(5, args.steps // 2))
         rec["mxfp8"] = mxfp8(max(5, args.steps // 2), args.decode_runs)
+        rec["mxfp4"] = mxfp4(max(5, args.steps // 2), args.decode_runs)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)

@@ -22,6 +22,12 @@
  * reduction; scale code b means 2^(b-127)). MXFP8 block scales are chosen as in the OCP Microscaling
  * specification: x = floor(log2 max|v|) - 8 (0 for an all-zero block), clamped
  * to [-127, 127], code x + 127; values e4m3fn(clamp(v / 2^x, -448, 448)).
+ * MXFP4 (the same section's "packed FP4-E2M1 operands"): expert weights are
+ * OCP E2M1 codes (1 sign, 2 exponent bits with bias 1, 1 mantissa bit:
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte with value 2i in the
+ * low nibble of byte i, and one E8M0 scale per 32 values along the reduction;
+ * tokens and the intermediate are MXFP8 as above. The weight codes come
+ * quantised from the caller.
  *
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers owned by the caller, allocated
@@ -56,7 +62,7 @@ typedef enum {
     MOE_ERR_HIP = 4          /* a HIP launch reported an error                      */
 } moe_status;
 
-typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3FN = 1, MOE_MXFP8 = 2 } moe_dtype;
+typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3FN = 1, MOE_MXFP8 = 2, MOE_MXFP4 = 3 } moe_dtype;
 
 /* Static string for a status code. */
 const char* moe_status_string(int status);
@@ -150,23 +156,27 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
  * (lane l = 0..63) are row l mod 32, bytes (l/32)*32 + pc*16 .. +15 of the
  * fragment's 64 (MXFP8: bytes pc*32 + (l/32)*16 .. +15, so that each piece
  * pair is one 32-value scale block in the matrix-core instruction's grouping).
+ * MXFP4 fragments are 32 rows x 32 bytes (64 E2M1 values) in one 1 KB piece:
+ * the 16 bytes at l*16 are row l mod 32, bytes (l/32)*16 .. +15 of the
+ * fragment's 32 (the instruction's order for 4-bit operands).
  * Gate and up rows are interleaved in blocks of 32 (W1 block, W3 block, ...),
  * so one wave holds the gate and up value of the same intermediate column.
  *
- * w1, w3   [E,I,H] row-major; w2 [E,H,I] row-major (bf16 or e4m3fn codes)
+ * w1, w3   [E,I,H] row-major; w2 [E,H,I] row-major (bf16 or e4m3fn codes;
+ *          MXFP4: packed E2M1, [E,I,H/2] and [E,H,I/2] bytes)
  * s1, s3   FP8: fp32 [E,I]; s2 FP8: fp32 [E,H] per-output-channel scales.
- *          MXFP8: E8M0 codes, s1, s3 uint8 [E,I,H/32]; s2 uint8 [E,H,I/32]
+ *          MXFP8, MXFP4: E8M0 codes, s1, s3 uint8 [E,I,H/32]; s2 uint8 [E,H,I/32]
  *          (one per row and 32 reduction values). BF16: NULL.
  * w13_out  [moe_preshuffle_bytes(dt,E,H,I,0)] bytes; w2_out [.., 1] bytes
- * s13_out  [.., 2] bytes; s2_out [.., 3] bytes (FP8 and MXFP8, else unused).
+ * s13_out  [.., 2] bytes; s2_out [.., 3] bytes (FP8, MXFP8, MXFP4, else unused).
  *          FP8: fp32 [E,2,I] (gate scales then up scales) and fp32 [E,H].
- *          MXFP8 (4-byte aligned): the codes in the order the kernels read
+ *          MXFP8, MXFP4 (4-byte aligned): the codes in the order the kernels read
  *          them: per expert, groups of four 32-row blocks (composite rows as
  *          above), then reduction fragment kb (64 values), then lane l = 0..63,
  *          then the four blocks: the code of row l mod 32 of the block, value
  *          block 2*kb + l/32.
  * Supported: H % 128 == 0 and I % 128 == 0 (bf16), H % 256 and I % 256 (FP8,
- * MXFP8).
+ * MXFP8, MXFP4).
  */
 int64_t moe_preshuffle_bytes(moe_dtype dt, int E, int H, int I,
                              int which /*0: W1+W3, 1: W2, 2: their scales s13, 3: s2*/);
@@ -181,21 +191,23 @@ moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, con
  * s = sorted_slot[p], token t = s / k, expert e = tile_expert[p / block_m]:
  *   g = W1[e] x_t, u = W3[e] x_t (fp32 accumulation; FP8: x_t = x_q[t]*x_scale[t],
  *   W = code * scale; MXFP8: every value times 2^(code - 127) of its 32-value
- *   block, tokens and weights alike), act[p, i] = bf16(silu(g_i) * u_i),
+ *   block, tokens and weights alike; MXFP4: the same with E2M1 weight values),
+ *   act[p, i] = bf16(silu(g_i) * u_i),
  *   silu(z) = z/(1+e^-z).
  * Pad rows (s == T*k) get act = 0.
  * FP8 also writes act_amax: per row p, partial maxima of |act[p,:]| over column
  * blocks, [capacity][moe_stage1_amax_floats()/capacity] floats (row-major);
  * stage 2 reduces them.
  *
- * x_or_xq  bf16 [T,H] (BF16) or e4m3fn [T,H] (FP8 from moe_route, MXFP8 from
- *          moe_route_mx)
- * x_scale  fp32 [T] (FP8), E8M0 uint8 [T,H/32] (MXFP8, 8-byte aligned) or NULL;
+ * x_or_xq  bf16 [T,H] (BF16) or e4m3fn [T,H] (FP8 from moe_route, MXFP8 and
+ *          MXFP4 from moe_route_mx)
+ * x_scale  fp32 [T] (FP8), E8M0 uint8 [T,H/32] (MXFP8, MXFP4; 8-byte aligned) or NULL;
  * w13, s13 from moe_preshuffle
  * sorted_slot, tile_expert, total_padded from moe_align with the same block_m
  * act      bf16 [capacity, I] (out); act_amax as above (FP8) or NULL (else unused)
  * Supported: block_m in {32, 64, 128, 256}; H, I multiples of 128 (bf16) or 256
- * (FP8, MXFP8); MXFP8 also H <= 8192 and I <= 16384; activations below 2 GiB.
+ * (FP8, MXFP8, MXFP4); MXFP8 and MXFP4 also H <= 8192 and I <= 16384;
+ * activations below 2 GiB.
  */
 int64_t moe_stage1_amax_floats(moe_dtype dt, int T, int k, int E, int H, int I, int block_m);
 moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, const void* w13,
@@ -207,8 +219,8 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, co
  * moe_stage2 - grouped down GEMM + weighted scatter-combine (talk summary 5:56,
  * "Scatter"). For each real row p (slot s, token t = s / k, expert e):
  *   y = W2[e] act_p   (FP8: act_p requantised per row, scale = max|act_p|/448,
- *                      code = e4m3fn(act_p / scale); MXFP8: act_p quantised
- *                      per block of 32 values as moe_route_mx does x;
+ *                      code = e4m3fn(act_p / scale); MXFP8, MXFP4: act_p
+ *                      quantised per block of 32 values as moe_route_mx does x;
  *                      fp32 accumulation)
  *   out[t, :] = bf16( sum_{j=0..k-1} w[t,j] * y_{t,j} ), summed in ascending j
  *   in fp32: a fixed order, no floating-point atomics, so results are
@@ -220,7 +232,7 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, co
  * act, act_amax from moe_stage1 (act_amax unused, may be NULL, unless FP8);
  * w2, s2 from moe_preshuffle; topk_w fp32 [T,k]
  * out bf16 [T,H] (out); workspace [moe_stage2_workspace_bytes()] bytes (device,
- * 256-byte aligned): per-slot weighted partials, for FP8 and MXFP8 the
+ * 256-byte aligned): per-slot weighted partials, for FP8, MXFP8 and MXFP4 the
  * requantised intermediate, and at prefill sizes the partials of those
  * reduction pieces.
  * Calls that use one workspace must be ordered (same stream or synchronised).

@@ -13,7 +13,9 @@ library's HIP kernels; torch provides device memory and streams only.
 
 The MXFP8 path ("mxfp8": e4m3fn values with one E8M0 scale code per 32 values
 along the reduction) is the same sequence with route(..., mx=True), which
-returns the block codes of x as x_scale, and block-scaled weights.
+returns the block codes of x as x_scale, and block-scaled weights. The MXFP4
+path ("mxfp4") takes packed E2M1 expert weights (two per byte, [E, I, H/2] and
+[E, H, I/2]) with the same E8M0 block codes; tokens are MXFP8 as before.
 """
 from __future__ import annotations
 
@@ -21,7 +23,7 @@ from dataclasses import dataclass
 
 import torch
 
-from ._lib import BF16, FP8, MXFP8, MoEError, check, lib
+from ._lib import BF16, FP8, MXFP4, MXFP8, MoEError, check, lib
 
 __all__ = ["route", "align", "preshuffle", "stage1", "stage2", "forward", "Layer",
            "pick_block_m", "align_capacity", "MoEError"]
@@ -34,6 +36,8 @@ def _dt(dtype) -> int:
         return FP8
     if dtype in ("mxfp8", MXFP8):
         return MXFP8
+    if dtype in ("mxfp4", MXFP4):
+        return MXFP4
     raise ValueError(f"dtype {dtype!r}")
 
 
@@ -130,16 +134,22 @@ class Weights:
     s2: torch.Tensor | None
 
 
+def _expert_shape(dt: int, w1) -> tuple[int, int, int]:
+    """(E, I, H) from the gate weights (MXFP4 rows hold H/2 bytes)."""
+    E, I, Hs = w1.shape
+    return E, I, Hs * 2 if dt == MXFP4 else Hs
+
+
 def preshuffle(dtype, w1, w3, w2, s1=None, s3=None, s2=None) -> Weights:
     dt = _dt(dtype)
-    E, I, H = w1.shape
+    E, I, H = _expert_shape(dt, w1)
     L = lib()
     n13 = L.moe_preshuffle_bytes(dt, E, H, I, 0)
     n2 = L.moe_preshuffle_bytes(dt, E, H, I, 1)
     dev = w1.device
     w13p = torch.empty(n13, dtype=torch.uint8, device=dev)
     w2p = torch.empty(n2, dtype=torch.uint8, device=dev)
-    if dt == MXFP8:  # block codes in the kernels' order (opaque bytes)
+    if dt in (MXFP8, MXFP4):  # block codes in the kernels' order (opaque bytes)
         s13p = torch.empty(L.moe_preshuffle_bytes(dt, E, H, I, 2), dtype=torch.uint8, device=dev)
         s2p = torch.empty(L.moe_preshuffle_bytes(dt, E, H, I, 3), dtype=torch.uint8, device=dev)
     else:
@@ -200,8 +210,8 @@ class Layer:
                  k=2, T=None, block_m=None):
         self.dt = _dt(dtype)
         self.fp8 = self.dt == FP8
-        self.mx = self.dt == MXFP8
-        self.E, self.I, self.H = w1.shape
+        self.mx = self.dt in (MXFP8, MXFP4)
+        self.E, self.I, self.H = _expert_shape(self.dt, w1)
         self.k = k
         self.w_router = w_router
         self.bias = bias

@@ -8,7 +8,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
-BF16, FP8, MXFP8 = 0, 1, 2
+BF16, FP8, MXFP8, MXFP4 = 0, 1, 2, 3
 
 # Every symbol the header declares, with (restype, argtypes).
 _P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t

@@ -52,7 +52,12 @@ int64_t capacity(int T, int k, int E, int bm) {
 }
 
 // Checks shared by the two GEMM stages.
-bool valid_dt(int dt) { return dt == MOE_BF16 || dt == MOE_FP8_E4M3FN || dt == MOE_MXFP8; }
+bool valid_dt(int dt) {
+  return dt == MOE_BF16 || dt == MOE_FP8_E4M3FN || dt == MOE_MXFP8 || dt == MOE_MXFP4;
+}
+
+// Block-scaled element types: MXFP8 tokens and E8M0 weight codes per 32 values.
+bool is_mx(int dt) { return dt == MOE_MXFP8 || dt == MOE_MXFP4; }
 
 moe_status check_stage(int dt, int T, int k, int E, int H, int I, int bm) {
   CHECK(valid_dt(dt), MOE_ERR_INVALID_ARG, "dtype %d", dt);
@@ -64,8 +69,8 @@ moe_status check_stage(int dt, int T, int k, int E, int H, int I, int bm) {
   const int q = dt == MOE_BF16 ? 128 : 256;
   CHECK(H % q == 0 && I % q == 0, MOE_ERR_UNSUPPORTED, "H=%d I=%d must be multiples of %d", H, I,
         q);
-  CHECK(dt != MOE_MXFP8 || (H <= moe::kMxMaxH && I <= moe::kMxMaxI), MOE_ERR_UNSUPPORTED,
-        "MXFP8 needs H <= %d and I <= %d (H=%d I=%d)", moe::kMxMaxH, moe::kMxMaxI, H, I);
+  CHECK(!is_mx(dt) || (H <= moe::kMxMaxH && I <= moe::kMxMaxI), MOE_ERR_UNSUPPORTED,
+        "MXFP8/MXFP4 need H <= %d and I <= %d (H=%d I=%d)", moe::kMxMaxH, moe::kMxMaxI, H, I);
   CHECK((int64_t)T * k <= (1 << 30) && capacity(T, k, E, bm) <= (1 << 30), MOE_ERR_UNSUPPORTED,
         "T*k too large");
   // Activation rows are addressed with 32-bit buffer offsets below 2 GiB.
@@ -161,8 +166,9 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
 int64_t moe_preshuffle_bytes(moe_dtype dt, int E, int H, int I, int which) {
   if (!valid_dt(dt) || E < 1 || H < 1 || I < 1) return -1;
   const int64_t es = dt == MOE_BF16 ? 2 : 1;
-  if (which == 0) return 2 * (int64_t)E * I * H * es;
-  if (which == 1) return (int64_t)E * H * I * es;
+  const int64_t d = dt == MOE_MXFP4 ? 2 : 1;  // E2M1: two values per byte
+  if (which == 0) return 2 * (int64_t)E * I * H * es / d;
+  if (which == 1) return (int64_t)E * H * I * es / d;
   if (which == 2 || which == 3) {
     if (dt == MOE_BF16) return 0;
     const int64_t rows = which == 2 ? 2 * (int64_t)E * I : (int64_t)E * H;
@@ -185,19 +191,22 @@ moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, con
   CHECK(aligned(w1, 16) && aligned(w3, 16) && aligned(w2, 16) && aligned(w13_out, 16) &&
             aligned(w2_out, 16),
         MOE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
-  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = dt == MOE_MXFP8;
+  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = is_mx(dt), fp4 = dt == MOE_MXFP4;
   if (fp8 || mx)
     CHECK(s1 && s3 && s2 && s13_out && s2_out, MOE_ERR_INVALID_ARG,
-          "FP8 and MXFP8 need all scale pointers");
+          "FP8, MXFP8 and MXFP4 need all scale pointers");
   if (mx)
     CHECK(aligned(s13_out, 4) && aligned(s2_out, 4), MOE_ERR_INVALID_ARG,
-          "MXFP8 scale outputs must be 4-byte aligned");
-  const int64_t es = dt == MOE_BF16 ? 2 : 1;
+          "MXFP8/MXFP4 scale outputs must be 4-byte aligned");
+  // Row length in bytes of each weight matrix and the fragment order.
+  const int64_t h_bytes = dt == MOE_BF16 ? 2 * (int64_t)H : fp4 ? H / 2 : H;
+  const int64_t i_bytes = dt == MOE_BF16 ? 2 * (int64_t)I : fp4 ? I / 2 : I;
+  const int order = fp4 ? 2 : mx ? 1 : 0;
   moe::PreshuffleArgs a13{(const uint8_t*)w1, (const uint8_t*)w3, (uint8_t*)w13_out, E, 2 * I,
-                          H * es, mx};
+                          h_bytes, order};
   hipError_t err = moe::launch_preshuffle(a13, stream);
   if (err != hipSuccess) return hip_status(err, "preshuffle W1/W3");
-  moe::PreshuffleArgs a2{(const uint8_t*)w2, nullptr, (uint8_t*)w2_out, E, H, I * es, mx};
+  moe::PreshuffleArgs a2{(const uint8_t*)w2, nullptr, (uint8_t*)w2_out, E, H, i_bytes, order};
   err = moe::launch_preshuffle(a2, stream);
   if (err != hipSuccess) return hip_status(err, "preshuffle W2");
   if (fp8) {
@@ -236,17 +245,17 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, co
   moe_status s = check_stage(dt, T, k, E, H, I, block_m);
   if (s != MOE_OK) return s;
   if (T == 0) return ok();
-  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = dt == MOE_MXFP8;
+  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = is_mx(dt);
   CHECK(x_or_xq && w13 && sorted_slot && tile_expert && total_padded && act, MOE_ERR_INVALID_ARG,
         "null pointer argument");
   CHECK(!fp8 || (x_scale && s13 && act_amax), MOE_ERR_INVALID_ARG,
         "FP8 needs x_scale, s13 and act_amax");
-  CHECK(!mx || (x_scale && s13), MOE_ERR_INVALID_ARG, "MXFP8 needs x_scale and s13");
+  CHECK(!mx || (x_scale && s13), MOE_ERR_INVALID_ARG, "MXFP8/MXFP4 need x_scale and s13");
   CHECK(aligned(x_or_xq, 16) && aligned(w13, 16) && aligned(act, 16) &&
             aligned(s13, mx ? 4 : 16) && aligned(x_scale, mx ? 8 : 4),
         MOE_ERR_INVALID_ARG,
-        "x, w13 and act must be 16-byte aligned, s13 16-byte (MXFP8: 4), x_scale 4-byte "
-        "(MXFP8: 8)");
+        "x, w13 and act must be 16-byte aligned, s13 16-byte (MXFP8/MXFP4: 4), x_scale 4-byte "
+        "(MXFP8/MXFP4: 8)");
   moe::GemmCfg c = moe::stage1_cfg(dt, T, k, E, H, I, block_m);
   const int64_t cap = capacity(T, k, E, block_m);
   moe::GemmArgs a{};
@@ -290,7 +299,7 @@ int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int
     const int64_t cap = capacity(T, k, E, block_m);
     bytes += up(cap * I) + up(cap * 4);  // requantised intermediate + row scales
   }
-  if (dt == MOE_MXFP8) {
+  if (is_mx(dt)) {
     const int64_t cap = capacity(T, k, E, block_m);
     bytes += up(cap * I) + up(cap * (I / 32));  // requantised intermediate + block codes
   }
@@ -307,11 +316,11 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
   moe_status s = check_stage(dt, T, k, E, H, I, block_m);
   if (s != MOE_OK) return s;
   if (T == 0) return ok();
-  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = dt == MOE_MXFP8;
+  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = is_mx(dt);
   CHECK(act && w2 && sorted_slot && tile_expert && total_padded && topk_w && out && workspace,
         MOE_ERR_INVALID_ARG, "null pointer argument");
   CHECK(!fp8 || (act_amax && s2), MOE_ERR_INVALID_ARG, "FP8 needs act_amax and s2");
-  CHECK(!mx || s2, MOE_ERR_INVALID_ARG, "MXFP8 needs s2");
+  CHECK(!mx || s2, MOE_ERR_INVALID_ARG, "MXFP8/MXFP4 need s2");
   CHECK(aligned(act, 16) && aligned(w2, 16) && aligned(out, 8) && aligned(workspace, 256) &&
             aligned(s2, mx ? 4 : 16),
         MOE_ERR_INVALID_ARG, "act/w2/s2 16-byte, out 8-byte, workspace 256-byte alignment");

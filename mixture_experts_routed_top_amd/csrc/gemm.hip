@@ -14,7 +14,11 @@
 // instruction itself pairs K differently: lanes r and r+32 together hold its
 // first 32 values in their first pieces. Any order shared by both operands
 // gives the same sums; the MXFP8 path, whose scales follow the instruction's
-// own grouping, stores piece pc of lane l as bytes 32*pc + 16*(l/32).)
+// own grouping, stores piece pc of lane l as bytes 32*pc + 16*(l/32).) The
+// MXFP4 path (E2M1 weights, two per byte, against MXFP8 tokens) has a
+// one-piece weight fragment of 32 rows x 32 bytes: lane l holds row l%32 and
+// the 32 values 32*(l/32) .. +31 of the fragment's 64, in order, which pair
+// with the token values of the MXFP8 order and take lane l's scale.
 //
 // Workgroup = 4 waves. Each wave owns NF weight fragments along the features
 // (NF*32 rows; for stage 1 gate blocks and the matching up blocks, so the
@@ -77,6 +81,19 @@ struct Mma<2> {  // e4m3fn x e4m3fn with E8M0 block scales (MXFP8), 32x32x64
                (int)x[1].x, (int)x[1].y, (int)x[1].z, (int)x[1].w};
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
         a, b, c, 0, 0, 0, (int)((uint32_t)ws >> (8 * OA)), 0, (int)((uint32_t)xs >> (8 * OB)));
+  }
+};
+template <>
+struct Mma<3> {  // E2M1 weights x e4m3fn tokens with E8M0 block scales (MXFP4), 32x32x64
+  template <int OA, int OB>
+  static __device__ __forceinline__ f32x16 run(const uint4 (&w)[1], const uint4 (&x)[2],
+                                               f32x16 c, int ws, int xs) {
+    // The E2M1 operand occupies the first four registers; the rest are unread.
+    i32x8 a = {(int)w[0].x, (int)w[0].y, (int)w[0].z, (int)w[0].w, 0, 0, 0, 0};
+    i32x8 b = {(int)x[0].x, (int)x[0].y, (int)x[0].z, (int)x[0].w,
+               (int)x[1].x, (int)x[1].y, (int)x[1].z, (int)x[1].w};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        a, b, c, 4, 0, 0, (int)((uint32_t)ws >> (8 * OA)), 0, (int)((uint32_t)xs >> (8 * OB)));
   }
 };
 template <>
@@ -192,11 +209,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   static_assert(WN * BMT * 4 <= LDS, "amax space");
   static_assert(NB == 3 || NB == 4, "weight pipeline depth");
 
-  // MXFP8: the E8M0 codes of the tile's token rows over this workgroup's
-  // reduction range sit after the token buffers for the main loop, laid out
-  // [column][token][fragment] (a column covers 32 reduction values), so that
-  // one LDS read gives a lane the codes of all MT fragments in one column.
-  constexpr bool MX = DT == 2;
+  // MXFP8 and MXFP4 (block-scaled tokens): the E8M0 codes of the tile's
+  // token rows over this workgroup's reduction range sit after the token
+  // buffers for the main loop, laid out [column][token][fragment] (a column
+  // covers 32 reduction values), so that one LDS read gives a lane the codes
+  // of all MT fragments in one column.
+  constexpr bool MX = DT == 2 || DT == 3;
+  // Weight fragment: two 1 KB pieces, or one for E2M1 (32 rows x 32 bytes).
+  constexpr int WP = DT == 3 ? 1 : 2;
+  constexpr int WFRAG = WP * kPiece;
   constexpr int XCOLS = MX ? (STAGE == 1 ? kMxMaxH : kMxMaxI) / 32 + 16 : 0;
   constexpr int XST = XCOLS * BMT;
   // Token buffers (reused by the epilogue), then the column scales of this
@@ -301,9 +322,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // reduction blocks from this wave's split on.
   const int64_t RB = a.N / 32, KB = Kb / 64;
   const int rb0 = ntile * (WGN / 32) + wn * NF;
-  const uint8_t* wbase = a.W + (((int64_t)e * RB + rb0) * KB + (kbase + wk * Kw) / 64) * kFrag +
+  const uint8_t* wbase = a.W + (((int64_t)e * RB + rb0) * KB + (kbase + wk * Kw) / 64) * WFRAG +
                          lane * 16;
-  const int64_t wfrag_stride = KB * kFrag;  // next row block
+  const int64_t wfrag_stride = KB * WFRAG;  // next row block
   // MXFP8 weight codes of this wave's row blocks: per fragment one 32-bit
   // (NF = 4) or 16-bit (NF = 2) word per lane whose byte f belongs to row
   // block rb0 + f (rb0 is a multiple of NF).
@@ -321,7 +342,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       for (int i = 0; i < 16; ++i) acc[m][f][i] = 0.0f;
 
   uint4 xr[2][PPT];             // token prefetch, by chunk parity
-  uint4 wbuf[NB][kSub][NF][2];  // weight prefetch: [stage][sub-block][fragment][piece]
+  uint4 wbuf[NB][kSub][NF][WP];  // weight prefetch: [stage][sub-block][fragment][piece]
   uint32_t wsr[NB][kSub];       // MXFP8 weight codes, staged like the weights
   uint32_t xsr[2][kSub];        // MXFP8 token codes, by chunk parity
 
@@ -338,7 +359,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   };
   auto load_w1 = [&](int c, int s, int f, int pc, uint4& w) {
     w = *reinterpret_cast<const uint4*>(wbase + f * wfrag_stride +
-                                        ((int64_t)c * kSub + s) * kFrag + pc * kPiece);
+                                        ((int64_t)c * kSub + s) * WFRAG + pc * kPiece);
   };
   auto load_ws = [&](int c, int sb, uint32_t& r) {
     const uint8_t* p = wsp + ((int64_t)c * kSub + sb) * 256;
@@ -347,13 +368,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     else
       r = *reinterpret_cast<const uint16_t*>(p);
   };
-  auto load_w = [&](int c, uint4 (&w)[kSub][NF][2]) {
+  auto load_w = [&](int c, uint4 (&w)[kSub][NF][WP]) {
 #pragma unroll
     for (int s = 0; s < kSub; ++s)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int pc = 0; pc < 2; ++pc) load_w1(c, s, f, pc, w[s][f][pc]);
+        for (int pc = 0; pc < WP; ++pc) load_w1(c, s, f, pc, w[s][f][pc]);
   };
   // Column whose bytes this lane's piece 0 / piece 1 holds, and their slots.
   const int rc0 = MX ? (lane >> 5) : 2 * (lane >> 5), rc1 = MX ? 2 + (lane >> 5) : 1 + 2 * (lane >> 5);
@@ -395,7 +416,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   uint4 xf[2][2];
   auto step = [&](int c, auto u_const) {
     constexpr int u = decltype(u_const)::value;
-    constexpr int NWL = PPT + kSub * NF * 2;  // token and weight loads
+    constexpr int NWL = PPT + kSub * NF * WP;  // token and weight loads
     constexpr int NLOAD = NWL + (MX ? kSub : 0);
     constexpr int NM = NSTEP * NF;
     const int last = nchunks - 1;
@@ -407,7 +428,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff[j] + (uint32_t)cx * kChunk,
                                                          0, 0));
       } else if constexpr (j < NWL) {
-        constexpr int q = j - PPT, s = q / (NF * 2), f = (q / 2) % NF, pc = q % 2;
+        constexpr int q = j - PPT, s = q / (NF * WP), f = (q / WP) % NF, pc = q % WP;
         load_w1(cw, s, f, pc, wbuf[(u + NB - 1) % NB][s][f][pc]);
       } else {
         load_ws(cw, j - NWL, wsr[(u + NB - 1) % NB][j - NWL]);
@@ -961,6 +982,8 @@ hipError_t dispatch(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipS
     return stage == 1 ? launch_dt_stage<0, 1>(c, a, st, res) : launch_dt_stage<0, 2>(c, a, st, res);
   if (dt == 2)
     return stage == 1 ? launch_dt_stage<2, 1>(c, a, st, res) : launch_dt_stage<2, 2>(c, a, st, res);
+  if (dt == 3)
+    return stage == 1 ? launch_dt_stage<3, 1>(c, a, st, res) : launch_dt_stage<3, 2>(c, a, st, res);
   return stage == 1 ? launch_dt_stage<1, 1>(c, a, st, res) : launch_dt_stage<1, 2>(c, a, st, res);
 }
 

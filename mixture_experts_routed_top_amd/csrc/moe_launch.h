@@ -38,8 +38,8 @@ struct PreshuffleArgs {
   const uint8_t* src1;  // W3, or null for W2
   uint8_t* dst;
   int E, R;             // R: composite rows per expert (2I or H)
-  int64_t K_bytes;      // reduction length in bytes (multiple of 64)
-  int mx_order;         // MXFP8 byte order inside a fragment (see preshuffle_kernel)
+  int64_t K_bytes;      // reduction length in bytes (multiple of 64; E2M1: of 32)
+  int mx_order;         // 0: plain, 1: MXFP8 byte order, 2: E2M1 fragments (see preshuffle_kernel)
 };
 hipError_t launch_preshuffle(const PreshuffleArgs& a, hipStream_t st);
 // The E8M0 block scales of the same matrices ([E][rows][K/32] codes, K_bytes =
@@ -76,8 +76,8 @@ struct GemmArgs {
   const float* x_scale;    // FP8: per-token (stage 1) or per-row (stage 2) activation scale
   const uint8_t* W;        // preshuffled weights
   const float* w_scale;    // FP8: s13 [E][2][I] (stage 1) or s2 [E][H] (stage 2)
-  const uint8_t* x_mx;     // MXFP8: E8M0 codes of X's rows, [rows of X][K/32]
-  const uint8_t* w_mx;     // MXFP8: preshuffled E8M0 weight codes (launch_preshuffle_mx_scales)
+  const uint8_t* x_mx;     // MXFP8/MXFP4: E8M0 codes of X's rows, [rows of X][K/32]
+  const uint8_t* w_mx;     // MXFP8/MXFP4: preshuffled E8M0 weight codes (launch_preshuffle_mx_scales)
   const int32_t* sorted_slot;
   const int32_t* tile_expert;
   const int32_t* total_padded;

@@ -10,7 +10,10 @@
 // MXFP8 uses bytes pc*32 + (l/32)*16 .. +15 instead: the scaled instruction
 // applies the scale of lane r (r < 32) to what lanes r and r+32 hold in their
 // first 16-byte piece and the scale of lane r+32 to their second pieces, so
-// each piece must be one 32-value block of the row.
+// each piece must be one 32-value block of the row. MXFP4 (E2M1 codes, two
+// per byte) has one-piece fragments of 32 rows x 32 bytes (64 values): lane l
+// holds row l%32 and the fragment's bytes (l/32)*16 .. +15, the instruction's
+// own order for a 4-bit operand (lane l's 32 values form its scale block).
 // Fragments are ordered by 32-row block, then by reduction block. For
 // gate/up, composite row c of an expert is row (c/64)*32 + c%32 of W1 when
 // (c/32) is even and of W3 when it is odd.
@@ -20,7 +23,9 @@
 namespace moe {
 
 __global__ __launch_bounds__(256) void preshuffle_kernel(PreshuffleArgs a) {
-  const int64_t kblocks = a.K_bytes / 64;
+  const bool fp4 = a.mx_order == 2;
+  const int fbytes = fp4 ? 1024 : 2048;          // bytes per fragment
+  const int64_t kblocks = a.K_bytes / (fbytes / 32);
   const int64_t per_expert = (int64_t)a.R * a.K_bytes;
   const int64_t n16 = per_expert * a.E / 16;
   const int64_t rows_src = a.src1 ? a.R / 2 : a.R;  // rows of each source matrix
@@ -29,8 +34,8 @@ __global__ __launch_bounds__(256) void preshuffle_kernel(PreshuffleArgs a) {
     const int64_t b = u * 16;
     const int64_t e = b / per_expert;
     const int64_t rem = b % per_expert;
-    const int64_t f = rem / 2048;
-    const int in = (int)(rem % 2048);
+    const int64_t f = rem / fbytes;
+    const int in = (int)(rem % fbytes);
     const int pc = in / 1024, lane = (in % 1024) / 16;
     const int64_t rb = f / kblocks, kb = f % kblocks;
     const int64_t c = rb * 32 + lane % 32;
@@ -40,8 +45,9 @@ __global__ __launch_bounds__(256) void preshuffle_kernel(PreshuffleArgs a) {
       row = (c / 64) * 32 + c % 32;
       if ((c / 32) % 2) src = a.src1;
     }
-    const int64_t kbyte = kb * 64 + (a.mx_order ? pc * 32 + (lane / 32) * 16
-                                                : (lane / 32) * 32 + pc * 16);
+    const int64_t kbyte = fp4 ? kb * 32 + (lane / 32) * 16
+                              : kb * 64 + (a.mx_order ? pc * 32 + (lane / 32) * 16
+                                                      : (lane / 32) * 32 + pc * 16);
     const int64_t sb = (e * rows_src + row) * a.K_bytes + kbyte;
     *reinterpret_cast<uint4*>(a.dst + b) = *reinterpret_cast<const uint4*>(src + sb);
   }

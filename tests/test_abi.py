@@ -169,3 +169,29 @@ def test_mxfp8_size_queries_and_checks():
     assert status("moe_route_mx", *a) == _lib.ERR_UNSUPPORTED         # H % 128
     a = list(r); a[3] = 0; a[10] = None
     assert status("moe_route_mx", *a) == _lib.OK
+
+
+def test_mxfp4_size_queries_and_checks():
+    L = _lib.lib()
+    E, H, I = 8, 4096, 14336
+    assert L.moe_preshuffle_bytes(3, E, H, I, 0) == E * I * H                # two values per byte
+    assert L.moe_preshuffle_bytes(3, E, H, I, 1) == E * H * I // 2
+    assert L.moe_preshuffle_bytes(3, E, H, I, 2) == 2 * E * I * (H // 32)    # one code per 32
+    assert L.moe_preshuffle_bytes(3, E, H, I, 3) == E * H * (I // 32)
+    assert L.moe_preshuffle_bytes(4, E, H, I, 0) == -1                        # no such dtype
+    assert L.moe_stage1_amax_floats(3, 8192, 2, E, H, I, 128) == 0
+    cap = L.moe_align_capacity(16, 2, E, 32)
+    need = L.moe_stage2_workspace_bytes(3, 16, 2, E, H, I, 32)
+    up = lambda b: (b + 255) // 256 * 256
+    assert need >= up(16 * 2 * H * 4) + up(cap * I) + up(cap * I // 32)
+    s1 = [3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 8, 4096, 14336, 32, FAKE, None, None]
+    a = list(s1); a[11] = 8192 + 256
+    assert status("moe_stage1", *a) == _lib.ERR_UNSUPPORTED          # H <= 8192
+    a = list(s1); a[12] = 16384 + 256
+    assert status("moe_stage1", *a) == _lib.ERR_UNSUPPORTED          # I <= 16384
+    a = list(s1); a[4] = None
+    assert status("moe_stage1", *a) == _lib.ERR_INVALID_ARG          # weight codes missing
+    p = [3, 8, 4096, 14336, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    assert status("moe_preshuffle", *p) == _lib.ERR_INVALID_ARG      # scales required
+    a = [4] + s1[1:]
+    assert status("moe_stage1", *a) == _lib.ERR_INVALID_ARG          # unknown dtype

@@ -32,7 +32,7 @@ def check_full(wl, n_sample, inp=None):
     if wl.dtype == "fp8":
         oq, os_ = oracle.quant_tokens(inp.x)
         assert np.array_equal(host(up.layer.xq), oq) and np.array_equal(host(up.layer.xs), os_)
-    if wl.dtype == "mxfp8":
+    if wl.dtype in ("mxfp8", "mxfp4"):
         oq, os_ = oracle.quant_tokens_mx(inp.x)
         assert np.array_equal(host(up.layer.xq), oq) and np.array_equal(host(up.layer.xs), os_)
     toks = sample_tokens(oid, wl.E, n_sample)
@@ -81,3 +81,12 @@ def test_mixtral_mxfp8_prefill_T8192_and_decode_T16():
     inp = workloads.Inputs(wl, xi.x, base.w_router, None, base.w1, base.w3, base.w2, base.s1,
                            base.s3, base.s2)
     check_full(wl, 8, inp)
+
+
+def test_mixtral_mxfp4_decode_T16_and_prefill_T8192():
+    base = check_full(workloads.mxfp4(16), 16)
+    wl = workloads.mxfp4(8192)
+    xi = workloads.generate(wl, weights=False)
+    inp = workloads.Inputs(wl, xi.x, base.w_router, None, base.w1, base.w3, base.w2, base.s1,
+                           base.s3, base.s2)
+    check_full(wl, 32, inp)
