@@ -61,10 +61,11 @@ def log(*a):
 
 
 def kernel_sha() -> str:
-    """Hash of the HIP sources: a traffic figure is only valid for the code it was taken on."""
+    """Hash of the sources the stage-1 kernel is compiled from (the GEMM file and the two
+    headers it includes): a traffic figure is only valid for the code it was taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_routed_top_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
+    for n in ("gemm.hip", "moe_device.h", "moe_launch.h"):
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -190,8 +190,12 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// The E2M1 decode tile of stage 1 (one token fragment, four weight fragments
+// per wave) is held to the 256 registers that two waves per SIMD leave each.
 template <int DT, int STAGE, int MT, int NF, int KSPLIT, int NB, int CK>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(DT == 3 && MT == 1 && NF == 4 ? 2 : 1, 8)))
+void gemm_kernel(GemmArgs a) {
   constexpr int kSub = CK / 64;          // fragments along the reduction per stage
   constexpr int kChunk = CK;             // reduction bytes per pipeline stage
   constexpr int WN = 4 / KSPLIT;         // waves along the features
@@ -873,8 +877,13 @@ GemmCfg stage1_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
   c.ksplit = 1;
   c.kg = 1;
   // Decode shapes (one 32-row fragment per tile): split the reduction over the
-  // waves so that a workgroup covers 64 features and the launch fills the chip.
-  if (c.mt == 1 && (H * (dt == 0 ? 2 : 1)) % (4 * 128) == 0) c.ksplit = 4;
+  // waves so that a workgroup covers 64 features and the launch fills the chip
+  // (E2M1 weights: 128 features, the same weight bytes per workgroup; the
+  // kernel then needs all 256 registers of two waves per SIMD).
+  if (c.mt == 1 && (H * (dt == 0 ? 2 : 1)) % (4 * 128) == 0) {
+    c.ksplit = 4;
+    if (dt == 3) c.nf = 4;
+  }
   set_pipeline(c);
   return c;
 }
@@ -896,7 +905,7 @@ GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
     // Split the reduction over workgroups too until the launch has about
     // 1024 live workgroups (each split g adds a partial, summed in order).
     const int chunks = kbytes / (4 * 128);
-    const int64_t base = live_mtiles(T, k, E, 32) * (H / 64);
+    const int64_t base = live_mtiles(T, k, E, 32) * (H / (32 * c.nf));
     for (int cand = 2; cand <= 16; ++cand) {
       if (chunks % cand) continue;
       if (base * c.kg >= 1024) break;
@@ -913,7 +922,9 @@ GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
 bool gemm_cfg_ok(int dt, int stage, const GemmCfg& c, int N, int K) {
   const int64_t kbytes = (int64_t)K * (dt == 0 ? 2 : 1);
   if (c.mt != 1 && c.mt != 2 && c.mt != 4) return false;
-  if (c.nf != 2 && !(c.nf == 4 && c.mt == 4 && c.ksplit == 1)) return false;
+  if (c.nf != 2 && !(c.nf == 4 && c.mt == 4 && c.ksplit == 1) &&
+      !(dt == 3 && stage == 1 && c.nf == 4 && c.mt == 1 && c.ksplit == 4))
+    return false;
   if (N % c.wg_n) return false;
   if (kbytes % ((int64_t)c.ksplit * c.kg * c.ck)) return false;
   if (stage == 1 && (c.kg != 1 || c.tail_split != 0)) return false;
@@ -963,6 +974,8 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t st, int* resident) {
 
 template <int DT, int STAGE>
 hipError_t launch_dt_stage(const GemmCfg& c, const GemmArgs& a, hipStream_t st, int* res) {
+  if constexpr (DT == 3 && STAGE == 1)
+    if (c.ksplit == 4 && c.nf == 4) return launch_one<DT, STAGE, 1, 4, 4, 3, 128>(a, st, res);
   if (c.ksplit == 4) return launch_one<DT, STAGE, 1, 2, 4, 3, 128>(a, st, res);
   if (c.ksplit == 2)
     return c.mt == 1 ? launch_one<DT, STAGE, 1, 2, 2, 3, 128>(a, st, res)
