@@ -15,8 +15,9 @@
 //  - small batches: one workgroup per token; its four waves split the experts
 //    (expert e on wave e%4) so that all loads of the token are in flight at
 //    once, then wave 0 selects the top-k and quantises the row;
-//  - large batches (E <= 16): one wave per token, W_r staged once per
-//    workgroup in LDS (batched 16-byte copies), several tokens per workgroup.
+//  - large batches (E <= 16): one wave per two tokens (four for H <= 2048),
+//    W_r staged once per workgroup in LDS (batched 16-byte copies), the
+//    experts' logits folded together (fold_many).
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -73,6 +74,8 @@ __device__ __forceinline__ float fold64(float v) {
 // outputs (lane 0 writes).
 __device__ __forceinline__ void select_topk(const RouteArgs& a, int t, int lane, float mine) {
   const int E = a.E, k = a.k;
+  int off0 = 32;
+  while (off0 > 1 && off0 >= E) off0 >>= 1;
   if (a.logits && lane < E) a.logits[(size_t)t * E + lane] = mine;
   bool taken = lane >= E;
   float top_l[8];
@@ -82,8 +85,9 @@ __device__ __forceinline__ void select_topk(const RouteArgs& a, int t, int lane,
     if (j >= k) break;
     float bv = taken ? -__builtin_inff() : mine;
     int bi = taken ? 1 << 20 : lane;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+    // Candidates sit in lanes e < E <= 2*off0, so the butterfly starts at off0:
+    // lanes 0 .. 2*off0-1 then all hold the best pair (lane 0 writes).
+    for (int off = off0; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off, 64);
       const int oi = __shfl_xor(bi, off, 64);
       if (better(ov, oi, bv, bi)) {
@@ -230,10 +234,55 @@ __global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
   }
 }
 
-// One wave per token; W_r in LDS. All experts accumulate together (chunk by
-// chunk, each expert's sum still in ascending h), so the LDS reads and FMAs of
-// different experts overlap.
-template <int NCH, int MAXE>
+// The fixed fold (p[l] += p[l+off], off = 32 .. 1) of M experts' lane partials
+// at once (M a power of two, 2 <= M <= 16). While an expert's partials still
+// span several lanes, each step keeps half of the experts in the lower lanes
+// of a pair and half in the upper ones, so one exchange serves two experts:
+// lower lane l and upper lane l+off both form p[l] + p[l+off] (an fp32 sum is
+// the same either way round), for the experts they keep. After log2(M) steps
+// every lane holds one expert and the last steps are a plain butterfly. Each
+// expert sees exactly the canonical pairs, so its logit is bit-identical to
+// fold64's; the result for expert e sits in lane fold_lane<M>(e).
+template <int M>
+__device__ __forceinline__ int fold_lane(int e) {
+  int l = 0;
+#pragma unroll
+  for (int b = 0; (1 << b) < M; ++b)  // bit b of e (from the top) picks lane bit 5-b
+    if (e & (M >> (b + 1))) l |= 32 >> b;
+  return l;
+}
+
+// One transposed step at distance OFF over the first 2*HALF values.
+template <int HALF, int OFF, int M>
+__device__ __forceinline__ void fold_step(float (&v)[M], int lane) {
+  const bool up = (lane & OFF) != 0;
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const float keep = up ? v[HALF + i] : v[i];
+    const float send = up ? v[i] : v[HALF + i];
+    const float recv = __shfl_xor(send, OFF, 64);
+    v[i] = up ? recv + keep : keep + recv;  // p[lower] + p[upper]
+  }
+  if constexpr (HALF > 1) fold_step<HALF / 2, OFF / 2, M>(v, lane);
+}
+
+template <int M>
+__device__ __forceinline__ float fold_many(float (&v)[M], int lane) {
+  static_assert(M >= 2 && M <= 16 && (M & (M - 1)) == 0, "experts folded together");
+  fold_step<M / 2, 32, M>(v, lane);
+  float r = v[0];
+#pragma unroll
+  for (int off = 32 / M; off >= 1; off >>= 1) {
+    const float o = __shfl_xor(r, off, 64);
+    r = (lane & off) ? o + r : r + o;
+  }
+  return r;
+}
+
+// TPW tokens per wave at once; W_r in LDS. The TPW rows are loaded together,
+// then each W_r chunk is read from LDS and converted once for all TPW tokens;
+// each (token, expert) sum still adds its products in ascending h.
+template <int NCH, int MAXE, int TPW>
 __global__ __launch_bounds__(256) void route_wave_kernel(RouteArgs a) {
   extern __shared__ __align__(16) uint16_t wr_lds[];
   const int lane = threadIdx.x & 63;
@@ -256,42 +305,53 @@ __global__ __launch_bounds__(256) void route_wave_kernel(RouteArgs a) {
     __syncthreads();
   }
   const int waves_total = gridDim.x * (blockDim.x / 64);
-  for (int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); t < a.T; t += waves_total) {
-    uint4 xv[NCH];
-    load_row<NCH>(a.x + (size_t)t * a.H, lane, nchunk, xv);
-    float acc[MAXE];
+  for (int t0 = (blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)) * TPW; t0 < a.T;
+       t0 += waves_total * TPW) {
+    uint4 xv[TPW][NCH];
 #pragma unroll
-    for (int e = 0; e < MAXE; ++e) acc[e] = 0.0f;
+    for (int u = 0; u < TPW; ++u)  // rows past T repeat the last one (not written)
+      load_row<NCH>(a.x + (size_t)min(t0 + u, a.T - 1) * a.H, lane, nchunk, xv[u]);
+    float acc[TPW][MAXE];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int e = 0; e < MAXE; ++e) acc[u][e] = 0.0f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = lane + 64 * i;
       if (c < nchunk) {
-        float xf[8];
-        unpack8(xv[i], xf);
+        float xf[TPW][8];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) unpack8(xv[u][i], xf[u]);
 #pragma unroll
         for (int e = 0; e < MAXE; ++e) {
           if (e < a.E) {
             float wf[8];
             unpack8(*reinterpret_cast<const uint4*>(wr_lds + (size_t)e * a.H + (size_t)c * 8), wf);
-            float s = acc[e];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s = s + xf[j] * wf[j];
-            acc[e] = s;
+            for (int u = 0; u < TPW; ++u) {
+              float s = acc[u][e];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) s = s + xf[u][j] * wf[j];
+              acc[u][e] = s;
+            }
           }
         }
       }
     }
-    float mine = -__builtin_inff();
+    const int src_lane = fold_lane<MAXE>(lane < MAXE ? lane : 0);
 #pragma unroll
-    for (int e = 0; e < MAXE; ++e) {
-      if (e < a.E) {
-        float l = fold64(acc[e]);
-        if (a.bias) l = l + a.bias[e];
-        if (lane == e) mine = l;
+    for (int u = 0; u < TPW; ++u) {
+      const int t = t0 + u;
+      const float folded = fold_many<MAXE>(acc[u], lane);
+      float mine = __shfl(folded, src_lane, 64);  // lane e < E: logit of expert e
+      if (a.bias && lane < a.E) mine = mine + a.bias[lane];
+      if (lane >= a.E) mine = -__builtin_inff();
+      if (t < a.T) {
+        select_topk(a, t, lane, mine);
+        if (a.x_q) quantise<NCH>(a, t, lane, nchunk, xv[u]);
       }
     }
-    select_topk(a, t, lane, mine);
-    if (a.x_q) quantise<NCH>(a, t, lane, nchunk, xv);
   }
 }
 
@@ -301,13 +361,16 @@ template <int NCH>
 hipError_t launch_nch(const RouteArgs& a, hipStream_t st) {
   const size_t wbytes = (size_t)a.E * a.H * 2;
   if (a.T >= 1024 && a.E <= 16 && wbytes <= (size_t)kRouteLdsBytes) {
-    // W_r fits in LDS: about 4 tokens per wave, so staging it is amortised.
-    int blocks = (a.T + 15) / 16;
-    if (blocks > 2048) blocks = 2048;
+    // W_r fits in LDS: TPW tokens per wave per pass, two workgroups per CU
+    // (the LDS limit), so at most 512 workgroups each staging W_r once.
+    constexpr int TPW = NCH <= 4 ? 4 : 2;
+    int blocks = (a.T + 4 * TPW - 1) / (4 * TPW);
+    if (blocks > 512) blocks = 512;
     if (a.E <= 8)
-      hipLaunchKernelGGL((route_wave_kernel<NCH, 8>), dim3(blocks), dim3(256), wbytes, st, a);
+      hipLaunchKernelGGL((route_wave_kernel<NCH, 8, TPW>), dim3(blocks), dim3(256), wbytes, st, a);
     else
-      hipLaunchKernelGGL((route_wave_kernel<NCH, 16>), dim3(blocks), dim3(256), wbytes, st, a);
+      hipLaunchKernelGGL((route_wave_kernel<NCH, 16, TPW>), dim3(blocks), dim3(256), wbytes, st,
+                         a);
   } else {
     const int blocks = a.T < 4096 ? a.T : 4096;
     hipLaunchKernelGGL((route_block_kernel<NCH>), dim3(blocks), dim3(256), 0, st, a);

@@ -67,19 +67,21 @@ def test_align_rejects_out_of_range_ids_on_device():
     assert int(host(g.total)[0]) == 0
 
 
-def test_empty_grouping_gives_zero_output():
+@pytest.mark.parametrize("dtype", ["fp8", "mxfp8", "mxfp4"])
+def test_empty_grouping_gives_zero_output(dtype):
     # stages run on the empty grouping of invalid ids: stage 2's output is all zero
     T, H, I, E, k = 10, 256, 256, 8, 2
-    wl = workloads.Workload("empty", T, H, I, E, k, "fp8", 1.0, 1.0 / 16.0, 0.05, 9)
+    wl = workloads.Workload("empty", T, H, I, E, k, dtype, 1.0, 1.0 / 16.0, 0.05, 9)
     inp = workloads.generate(wl)
     ids = np.zeros((T, k), np.int32)
     ids[0, 0] = E  # out of range
     g = moe.align(dev(ids), E, 32)
-    pw = moe.preshuffle("fp8", dev(inp.w1), dev(inp.w3), dev(inp.w2), dev(inp.s1), dev(inp.s3),
+    pw = moe.preshuffle(dtype, dev(inp.w1), dev(inp.w3), dev(inp.w2), dev(inp.s1), dev(inp.s3),
                         dev(inp.s2))
-    _, _, xq, xs, _ = moe.route(dev(inp.x), dev(inp.w_router), k, fp8=True)
-    act, amax = moe.stage1("fp8", xq, xs, pw, g)
+    mx = dtype != "fp8"
+    _, _, xq, xs, _ = moe.route(dev(inp.x), dev(inp.w_router), k, fp8=not mx, mx=mx)
+    act, amax = moe.stage1(dtype, xq, xs, pw, g)
     w = torch.full((T, k), 0.5, dtype=torch.float32, device="cuda")
-    out = moe.stage2("fp8", act, amax, pw, g, w)
+    out = moe.stage2(dtype, act, amax, pw, g, w)
     torch.cuda.synchronize()
     assert np.all(host(out) == 0)

@@ -1,7 +1,7 @@
 """The layer captured in a HIP graph: every replay, with eager work and host
 synchronisations between replays, equals the eager call on the same tokens,
-bit for bit (decode-size FP8, and a BF16 shape whose stage 2 cuts its last
-round into reduction pieces)."""
+bit for bit (decode-size FP8 and MXFP4, an MXFP8 prefill-tile shape, and a BF16
+shape whose stage 2 cuts its last round into reduction pieces)."""
 import numpy as np
 import pytest
 import torch
@@ -22,6 +22,8 @@ def make(dtype, T, H, I, E, k, seed):
 @pytest.mark.parametrize("dtype,T,H,I,E,k,bm", [
     ("fp8", 16, 1024, 1024, 8, 2, 32),     # decode shape: split reductions, one-wave align
     ("bf16", 700, 512, 768, 8, 2, 256),    # stage 2 tail pieces and their reduction
+    ("mxfp4", 16, 1024, 1024, 8, 2, 32),   # E2M1 decode: MX token codes, 128-feature stage 1
+    ("mxfp8", 300, 512, 512, 8, 2, 128),   # MX prefill tiles with the code tile in LDS
 ])
 def test_graph_replays_match_eager(dtype, T, H, I, E, k, bm):
     inp = make(dtype, T, H, I, E, k, seed=T)

@@ -119,14 +119,15 @@ def test_skew_everything_to_one_pair():
     assert rel_err(r["out"], o64) <= TOL["fp8"]
 
 
-def test_layer_is_deterministic_and_token_order_free():
-    inp = make("fp8", 96, 512, 512, 8, 2, seed=3)
+@pytest.mark.parametrize("dtype", ["fp8", "mxfp8", "mxfp4"])
+def test_layer_is_deterministic_and_token_order_free(dtype):
+    inp = make(dtype, 96, 512, 512, 8, 2, seed=3)
     up = Uploaded(inp, block_m=32)
     a = up.run()
     b = up.run()
     assert np.array_equal(a, b)
     perm = np.random.default_rng(0).permutation(inp.wl.T)
-    inp2 = make("fp8", 96, 512, 512, 8, 2, seed=3)
+    inp2 = make(dtype, 96, 512, 512, 8, 2, seed=3)
     inp2.x = np.ascontiguousarray(inp.x[perm])
     c = Uploaded(inp2, block_m=32).run()
     assert np.array_equal(c, a[perm])
