@@ -50,13 +50,13 @@ def _stream() -> int:
 
 
 def pick_block_m(T: int, k: int, E: int) -> int:
-    """M-tile for a batch: the smallest of 32/64/128 covering the mean expert group
-    (the kernels' largest row tile is 128, so larger groups also use 128)."""
+    """M-tile for a batch: 32-row tiles while the mean expert group is at most 24 slots
+    (three quarters of a tile, so that few groups spill into a second tile, which would
+    stream that expert's weights again), else 128-row tiles. Measured on the Mixtral shape
+    (cold cache, FP8): 32 rows are fastest up to T=96 (mean 24), 128 rows from T=128 (mean
+    32: 313 us against 376 with 32-row and 320 with 64-row tiles) on."""
     mean = T * k / max(E, 1)
-    for bm in (32, 64):
-        if mean <= bm:
-            return bm
-    return 128
+    return 32 if mean <= 24 else 128
 
 
 def align_capacity(T: int, k: int, E: int, block_m: int) -> int:
