@@ -2,7 +2,7 @@
 // sort (the "dynamic expert sizes" of the routed MoE GEMM in the FlyDSL-in-JAX
 // talk summary, 5:56). Integer work only: bit-exact by construction. Three
 // kernels by size, each one workgroup:
-//  - align_small_kernel (S <= 2048 slots, decode): one wave, ids in registers,
+//  - align_small_kernel (S <= 256 slots, decode): one wave, ids in registers,
 //    counts and ranks from ballots, offsets from a shuffle scan;
 //  - align_runs_kernel (S <= 32768, E <= 16): each thread takes a contiguous
 //    run of slots and counts it in packed 16-bit counters; one exclusive scan
@@ -146,8 +146,10 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a) {
 // Small groupings (S <= kSmallSlots, decode batches): the same counting sort
 // on one wave, in registers. Lane l holds slot 64*i + l of each 64-slot chunk
 // i; lane e (< E) keeps expert e's count, offset and running base. No LDS and
-// no barriers: the cost is a few ballots per chunk and expert.
-constexpr int kSmallSlots = 2048;
+// no barriers: the cost is a few ballots per chunk and expert, so it grows
+// with the chunks (measured: 5.1 us at 32 slots, 8.2 at 256, 12.1 at 512, 36
+// at 2048), while align_runs_kernel takes 8.0-8.6 us from 256 to 2048 slots.
+constexpr int kSmallSlots = 256;
 constexpr int kSmallChunks = kSmallSlots / 64;
 
 __global__ __launch_bounds__(64) void align_small_kernel(AlignArgs a) {
