@@ -83,8 +83,20 @@ def test_mixtral_mxfp8_prefill_T8192_and_decode_T16():
     check_full(wl, 8, inp)
 
 
-def test_mixtral_mxfp4_decode_T16_and_prefill_T8192():
-    base = check_full(workloads.mxfp4(16), 16)
+def test_mixtral_mxfp4_decode_sweep_and_prefill_T8192():
+    # every batch the benchmark times: the decode sweep T = 1 .. 256 (32- and 128-row
+    # tiles) and the prefill, on one set of E2M1 weights
+    base = None
+    for T in workloads.DECODE_SWEEP:
+        wl = workloads.mxfp4(T)
+        if base is None:
+            base = workloads.generate(wl, threads=16)
+            inp = base
+        else:
+            xi = workloads.generate(wl, weights=False)
+            inp = workloads.Inputs(wl, xi.x, base.w_router, None, base.w1, base.w3, base.w2,
+                                   base.s1, base.s3, base.s2)
+        check_full(wl, min(T, 16), inp)
     wl = workloads.mxfp4(8192)
     xi = workloads.generate(wl, weights=False)
     inp = workloads.Inputs(wl, xi.x, base.w_router, None, base.w1, base.w3, base.w2, base.s1,
