@@ -524,27 +524,67 @@ void gemm_kernel(GemmArgs a) {
       const int col0 = kbase >> 5, gstart = col0 & ~7;
       const int cend = (kbase + (KSPLIT - 1) * Kw + nchunks * kChunk) >> 5;
       const int ng = (cend - gstart + 7) >> 3;
-      const int r = tid % BMT;
-      const int slot = a.sorted_slot[row0 + r];
-      const uint32_t srow = STAGE == 1 ? div_k(min(slot, S - 1), a.k_magic) : (uint32_t)(row0 + r);
-      const uint32_t sbase = slot < S ? srow * (uint32_t)(Kb >> 5) + (uint32_t)gstart : kPadOffset;
       const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
           (void*)a.x_mx, (short)0, (int)(a.x_bytes >> 5), 0x00020000);
-      uint8_t* dst = lds + LDS + (r & 31) * MT + (r >> 5);
-      constexpr int GS = 256 / BMT, BATCH = 8;
-      for (int g0 = tid / BMT; g0 < ng; g0 += GS * BATCH) {
-        uint2 v[BATCH];
+      auto code_base = [&](int r) {  // buffer offset of tile row r's first code
+        const int slot = a.sorted_slot[row0 + r];
+        const uint32_t srow =
+            STAGE == 1 ? div_k(min(slot, S - 1), a.k_magic) : (uint32_t)(row0 + r);
+        return slot < S ? srow * (uint32_t)(Kb >> 5) + (uint32_t)gstart : kPadOffset;
+      };
+      if constexpr (MT == 4) {
+        // Thread: token t's four rows (t + 32f, fragment f) over 8 columns at a
+        // time; a 4x4 byte transpose in registers makes each column's word
+        // (fragment f in byte f), stored with one 32-bit LDS write.
+        const int t = tid & 31;
+        uint32_t sb[4];
 #pragma unroll
-        for (int j = 0; j < BATCH; ++j)
-          v[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                               srsrc, sbase + 8u * (uint32_t)(g0 + GS * j), 0, 0));
+        for (int f = 0; f < 4; ++f) sb[f] = code_base(32 * f + t);
+        uint32_t* dstw = reinterpret_cast<uint32_t*>(lds + LDS) + t;  // column c: word c*32 + t
+        constexpr int BATCH = 4;  // column groups per thread in flight
+        for (int g0 = tid >> 5; g0 < ng; g0 += 8 * BATCH) {
+          uint2 v[BATCH][4];
 #pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-          const int g = g0 + GS * j;
-          if (g < ng) {
+          for (int j = 0; j < BATCH; ++j)
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-              dst[(8 * g + i) * BMT] = (uint8_t)((i < 4 ? v[j].x : v[j].y) >> (8 * (i & 3)));
+            for (int f = 0; f < 4; ++f)
+              v[j][f] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                      srsrc, sb[f] + 8u * (uint32_t)(g0 + 8 * j), 0, 0));
+#pragma unroll
+          for (int j = 0; j < BATCH; ++j) {
+            const int g = g0 + 8 * j;
+            if (g < ng) {
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const int sh = 8 * (i & 3);
+                uint32_t w = 0;
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                  w |= (((i < 4 ? v[j][f].x : v[j][f].y) >> sh) & 0xffu) << (8 * f);
+                dstw[(8 * g + i) * 32] = w;
+              }
+            }
+          }
+        }
+      } else {
+        const int r = tid % BMT;
+        const uint32_t sbase = code_base(r);
+        uint8_t* dst = lds + LDS + (r & 31) * MT + (r >> 5);
+        constexpr int GS = 256 / BMT, BATCH = 8;
+        for (int g0 = tid / BMT; g0 < ng; g0 += GS * BATCH) {
+          uint2 v[BATCH];
+#pragma unroll
+          for (int j = 0; j < BATCH; ++j)
+            v[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 srsrc, sbase + 8u * (uint32_t)(g0 + GS * j), 0, 0));
+#pragma unroll
+          for (int j = 0; j < BATCH; ++j) {
+            const int g = g0 + GS * j;
+            if (g < ng) {
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                dst[(8 * g + i) * BMT] = (uint8_t)((i < 4 ? v[j].x : v[j].y) >> (8 * (i & 3)));
+            }
           }
         }
       }
