@@ -754,6 +754,17 @@ __global__ __launch_bounds__(256) void quant_act_kernel(QuantArgs a) {
   const int p = blockIdx.x;
   if (p >= *a.total_padded) return;
   const int tid = threadIdx.x, lane = tid & 63;
+  const uint16_t* row = a.act + (size_t)p * a.I;
+  // The row's first chunks are loaded before the row maximum is known, so
+  // that their latency overlaps the maxima's (rows of up to 8 * 2048 values
+  // come entirely from these registers).
+  constexpr int kPre = 8;
+  uint4 pre[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int c = tid + 256 * j;
+    if (c < a.I / 8) pre[j] = *reinterpret_cast<const uint4*>(row + c * 8);
+  }
   float m = 0.0f;
   for (int i = tid; i < a.nparts; i += 256) m = fmaxf(m, a.amax_part[(size_t)p * a.nparts + i]);
 #pragma unroll
@@ -764,11 +775,9 @@ __global__ __launch_bounds__(256) void quant_act_kernel(QuantArgs a) {
   const float s = m > 0.0f ? m / 448.0f : 1.0f;
   const float inv = 1.0f / s;
   if (tid == 0) a.act_scale[p] = s;
-  const uint16_t* row = a.act + (size_t)p * a.I;
   uint8_t* q = a.act_q + (size_t)p * a.I;
-  for (int c = tid; c < a.I / 8; c += 256) {
-    uint4 v = *reinterpret_cast<const uint4*>(row + c * 8);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  auto convert = [&](int c, const uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     float f[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -777,7 +786,14 @@ __global__ __launch_bounds__(256) void quant_act_kernel(QuantArgs a) {
     }
     *reinterpret_cast<uint2*>(q + c * 8) =
         make_uint2(f32x4_to_e4m3(f[0], f[1], f[2], f[3]), f32x4_to_e4m3(f[4], f[5], f[6], f[7]));
+  };
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int c = tid + 256 * j;
+    if (c < a.I / 8) convert(c, pre[j]);
   }
+  for (int c = tid + 256 * kPre; c < a.I / 8; c += 256)
+    convert(c, *reinterpret_cast<const uint4*>(row + c * 8));
 }
 
 // MX block quantisation of the bf16 intermediate (MXFP8 stage 2): one thread
