@@ -845,21 +845,32 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       *reinterpret_cast<uint2*>(a.out + (size_t)i * 4) = make_uint2(0u, 0u);
     return;
   }
+  const int n = a.k * a.kg;  // partials per output, summed in the order u = j*kg + g
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i * 4 / a.H, h = i * 4 % a.H;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < a.k; ++j) {
-      for (int g = 0; g < a.kg; ++g) {
-        const float4 v = *reinterpret_cast<const float4*>(a.part + g * split +
-                                                          ((size_t)t * a.k + j) * a.H + h);
-        if (j == 0 && g == 0) {
-          s = v;
+    // Eight partials are loaded before any is added, so their latencies overlap.
+    constexpr int B = 8;
+    for (int u0 = 0; u0 < n; u0 += B) {
+      float4 v[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int u = u0 + b, j = u / a.kg, g = u % a.kg;
+        if (u < n)
+          v[b] = *reinterpret_cast<const float4*>(a.part + g * split +
+                                                  ((size_t)t * a.k + j) * a.H + h);
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        if (u0 + b >= n) break;
+        if (u0 + b == 0) {
+          s = v[b];
         } else {
-          s.x = s.x + v.x;
-          s.y = s.y + v.y;
-          s.z = s.z + v.z;
-          s.w = s.w + v.w;
+          s.x = s.x + v[b].x;
+          s.y = s.y + v[b].y;
+          s.z = s.z + v[b].z;
+          s.w = s.w + v[b].w;
         }
       }
     }
