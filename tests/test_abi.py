@@ -195,3 +195,13 @@ def test_mxfp4_size_queries_and_checks():
     assert status("moe_preshuffle", *p) == _lib.ERR_INVALID_ARG      # scales required
     a = [4] + s1[1:]
     assert status("moe_stage1", *a) == _lib.ERR_INVALID_ARG          # unknown dtype
+
+
+def test_pick_block_m_rule():
+    # 32-row tiles while the mean expert group is at most 24 slots, else 128-row tiles
+    import mixture_experts_routed_top_amd as moe
+    assert [moe.pick_block_m(T, 2, 8) for T in (1, 16, 64, 96)] == [32] * 4
+    assert [moe.pick_block_m(T, 2, 8) for T in (97, 128, 256, 8192)] == [128] * 4
+    assert moe.pick_block_m(12, 1, 1) == 32 and moe.pick_block_m(25, 1, 1) == 128
+    for T in (1, 96, 97, 8192):  # every choice has a capacity the align call accepts
+        assert moe.align_capacity(T, 2, 8, moe.pick_block_m(T, 2, 8)) > 0
