@@ -929,6 +929,8 @@ int64_t live_mtiles(int T, int k, int E, int tile_rows) {
 // Workgroups of a decode-shaped stage-2 launch that MI355X runs at once (two
 // per CU on 256 CUs): the reduction split aims for one full round of them.
 constexpr int64_t kDecodeRound = 512;
+// The same for the 128 x 512 prefill tile (one workgroup per CU).
+constexpr int64_t kPrefillRound = 256;
 
 // Pipeline shape of a (mt, nf, ksplit) triple: stage bytes (the weight
 // pipeline is always three stages deep).
@@ -991,9 +993,24 @@ GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
     }
   }
   set_pipeline(c);
-  // Prefill tiles are long (the whole reduction of 128 rows x 512 features):
-  // a partial last round is cut into pieces.
-  if (c.mt == 4 && c.nf == 4 && c.ksplit == 1 && c.kg == 1) c.tail_split = 8;
+  if (c.mt == 4 && c.nf == 4 && c.ksplit == 1 && c.kg == 1) {
+    // Prefill tiles are long (the whole reduction of 128 rows x 512 features).
+    // When a quarter round of resident workgroups holds them all (small
+    // batches on 128-row tiles), split the reduction over workgroups until
+    // the round is full, with at least 16 chunks per split; otherwise cut a
+    // partial last round into pieces (tail_split). Measured, FP8 on the
+    // Mixtral shape: T=256 325 -> 319 us and T=512 453 -> 443 us with 4
+    // splits; at T=1024 two splits were slower than the pieces (636 -> 649).
+    const int chunks = kbytes / c.ck;
+    const int64_t tiles = live_mtiles(T, k, E, 128) * (H / c.wg_n);
+    for (int cand = 2; cand <= 64; ++cand) {
+      if (chunks % cand || chunks / cand < 16) continue;
+      if (tiles * cand > kPrefillRound) break;
+      c.kg = cand;
+    }
+    if (c.kg < 4) c.kg = 1;
+    if (c.kg == 1) c.tail_split = 8;
+  }
   return c;
 }
 

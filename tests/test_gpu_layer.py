@@ -64,6 +64,7 @@ def run_stages(inp, bm):
     ("bf16", 200, 256, 384, 8, 2, 128),    # 2I % 512 != 0: stage 1 on 2 fragments per wave
     ("fp8", 17, 256, 256, 4, 1, 32),       # k = 1
     ("fp8", 5, 1024, 1024, 8, 2, 32),      # decode: reduction split over waves and workgroups
+    ("fp8", 256, 512, 4096, 8, 2, 128),    # 128-row tiles, one round: stage 2 split over 4 workgroups
     ("bf16", 9, 256, 256, 1, 1, 32),       # E = 1: a plain SwiGLU MLP
 ])
 def test_stages_match_oracle(dtype, T, H, I, E, k, bm):
