@@ -2,7 +2,7 @@
 // sort (the "dynamic expert sizes" of the routed MoE GEMM in the FlyDSL-in-JAX
 // talk summary, 5:56). Integer work only: bit-exact by construction. Three
 // kernels by size, each one workgroup:
-//  - align_small_kernel (S <= 256 slots, decode): one wave, ids in registers,
+//  - align_small_kernel (S <= 128 slots, decode): one wave, ids in registers,
 //    counts and ranks from ballots, offsets from a shuffle scan;
 //  - align_runs_kernel (S <= 32768, E <= 16): each thread takes a contiguous
 //    run of slots and counts it in packed 16-bit counters; one exclusive scan
@@ -147,9 +147,9 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a) {
 // on one wave, in registers. Lane l holds slot 64*i + l of each 64-slot chunk
 // i; lane e (< E) keeps expert e's count, offset and running base. No LDS and
 // no barriers: the cost is a few ballots per chunk and expert, so it grows
-// with the chunks (measured: 5.1 us at 32 slots, 8.2 at 256, 12.1 at 512, 36
-// at 2048), while align_runs_kernel takes 8.0-8.6 us from 256 to 2048 slots.
-constexpr int kSmallSlots = 256;
+// with the chunks (measured: 5.1 us at 32 slots, 6.1 at 128, 8.2 at 256, 36 at
+// 2048), while align_runs_kernel takes 6.3-6.8 us from 512 to 2048 slots.
+constexpr int kSmallSlots = 128;
 constexpr int kSmallChunks = kSmallSlots / 64;
 
 __global__ __launch_bounds__(64) void align_small_kernel(AlignArgs a) {
@@ -227,21 +227,29 @@ __global__ __launch_bounds__(64) void align_small_kernel(AlignArgs a) {
 // Prefill-size groupings with few experts (S <= kRunSlots * 1024, E <= 16):
 // thread t owns a contiguous run of slots, so one block-wide scan replaces the
 // per-chunk ballots. The ids go through LDS as bytes (coalesced loads, then
-// each thread reads its run); a thread counts its run in packed 16-bit
-// counters (expert e in half e%2 of word e/2: counts stay below 2^16 since
-// S <= 32768); an exclusive scan of those words over the threads gives every
-// thread, for every expert, the number of earlier slots; its slots then go to
-// offset[e] + that number + the rank inside its run, in ascending order, which
-// is the stable order.
+// each thread copies its run into registers); a thread counts its run in
+// packed 16-bit counters (expert e in half e%2 of word e/2: counts stay below
+// 2^16 since S <= 32768); an exclusive scan of those words over the threads
+// gives every thread, for every expert, the number of earlier slots; its
+// slots then go to offset[e] + that number + the rank inside its run, in
+// ascending order, which is the stable order. The grouping is assembled in
+// LDS (over the ids, which are in registers by then) and written out in
+// order: one workgroup's scattered 4-byte global stores touched a cache line
+// each and were the kernel's largest cost.
 constexpr int kRunSlots = 32;                     // slots per thread at most
 constexpr int kRunMaxSlots = kRunSlots * kAlignThreads;
-constexpr int kRunWords = 8;                      // packed counter words (E <= 16)
+constexpr int kRunWords = 8;                      // packed counter words at most (E <= 16)
+constexpr int kRunMaxRows = kRunMaxSlots + 16 * 255;  // capacity at E <= 16, block_m <= 256
 
+// W packed counter words: experts 0 .. 2W-1 (4 words for E <= 8, else 8).
+template <int W>
 __global__ __launch_bounds__(kAlignThreads) void align_runs_kernel(AlignArgs a) {
-  __shared__ __align__(16) uint8_t ids8[kRunMaxSlots];
-  __shared__ uint32_t wtot[kAlignWaves][kRunWords];  // per-wave totals, then wave prefixes
-  __shared__ int cnt[2 * kRunWords];
-  __shared__ int off[2 * kRunWords + 1];
+  // ids as bytes first, then the grouped rows (capacity ints) in the same space
+  __shared__ __align__(16) int rows[kRunMaxRows];
+  uint8_t* const ids8 = reinterpret_cast<uint8_t*>(rows);
+  __shared__ uint32_t wtot[kAlignWaves][W];  // per-wave totals, then wave prefixes
+  __shared__ int cnt[2 * W];
+  __shared__ int off[2 * W + 1];
   __shared__ int bad;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, E = a.E, bm = a.bm;
@@ -252,9 +260,10 @@ __global__ __launch_bounds__(kAlignThreads) void align_runs_kernel(AlignArgs a) 
     bool anybad = false;
 #pragma unroll
     for (int i = 0; i < kRunSlots; ++i) {
-      const int s = i * kAlignThreads + tid;  // clamped load, then select: no branches
+      if (i >= nchunks) break;                // uniform: the chunks present
+      const int s = i * kAlignThreads + tid;  // clamped load, then select
       const int v = a.ids[min(s, S - 1)];
-      if (i < nchunks && s < S) {
+      if (s < S) {
         anybad |= v < 0 || v >= E;
         ids8[s] = (uint8_t)v;
       }
@@ -266,25 +275,31 @@ __global__ __launch_bounds__(kAlignThreads) void align_runs_kernel(AlignArgs a) 
     if (tid == 0) *a.total = 0;
     return;
   }
-  // This thread's run: slots [r0, r0 + n4) clipped to S, n4 a multiple of 4.
+  // This thread's run: slots [r0, r0 + n4) clipped to S, n4 a multiple of 4,
+  // copied into registers four ids per word (slots past S read as 0, unused).
   const int n4 = ((nchunks + 3) / 4) * 4;
   const int r0 = tid * n4;
-  uint32_t cntw[kRunWords];
+  uint32_t idw[kRunSlots / 4];
 #pragma unroll
-  for (int w = 0; w < kRunWords; ++w) cntw[w] = 0;
-  auto run_id = [&](int i) { return (int)ids8[r0 + i]; };
-  for (int i = 0; i < n4; ++i) {
-    if (r0 + i >= S) break;
+  for (int q = 0; q < kRunSlots / 4; ++q)
+    idw[q] = 4 * q < n4 ? *reinterpret_cast<const uint32_t*>(ids8 + r0 + 4 * q) : 0u;
+  auto run_id = [&](int i) { return (int)((idw[i / 4] >> (8 * (i % 4))) & 0xffu); };
+  uint32_t cntw[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) cntw[w] = 0;
+#pragma unroll
+  for (int i = 0; i < kRunSlots; ++i) {
+    if (i >= n4 || r0 + i >= S) break;
     const int e = run_id(i);
     const uint32_t inc = (e & 1) ? 0x10000u : 1u;
 #pragma unroll
-    for (int w = 0; w < kRunWords; ++w) cntw[w] += (e >> 1) == w ? inc : 0u;
+    for (int w = 0; w < W; ++w) cntw[w] += (e >> 1) == w ? inc : 0u;
   }
   // Exclusive scan of the packed words over the threads (thread order = slot
   // order): inside each wave with shuffles, then over the 16 wave totals.
-  uint32_t excl[kRunWords];
+  uint32_t excl[W];
 #pragma unroll
-  for (int w = 0; w < kRunWords; ++w) {
+  for (int w = 0; w < W; ++w) {
     uint32_t x = cntw[w];
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -294,8 +309,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_runs_kernel(AlignArgs a) 
     excl[w] = x - cntw[w];
     if (lane == 63) wtot[wave][w] = x;
   }
-  __syncthreads();
-  if (tid < kRunWords) {  // wave prefixes in place, and the expert counts from the grand total
+  __syncthreads();  // also: every run is in registers, so the id bytes may be overwritten
+  if (tid < W) {  // wave prefixes in place, and the expert counts from the grand total
     uint32_t acc = 0;
     for (int w = 0; w < kAlignWaves; ++w) {
       const uint32_t t = wtot[w][tid];
@@ -307,7 +322,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_runs_kernel(AlignArgs a) 
   }
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < kRunWords; ++w) excl[w] += wtot[wave][w];
+  for (int w = 0; w < W; ++w) excl[w] += wtot[wave][w];
   if (tid == 0) {  // padded offsets
     int pos = 0;
     for (int e = 0; e < E; ++e) {
@@ -320,34 +335,42 @@ __global__ __launch_bounds__(kAlignThreads) void align_runs_kernel(AlignArgs a) 
   __syncthreads();
   if (tid < E) a.count[tid] = cnt[tid];
   if (tid <= E) a.offset[tid] = off[tid];
-  // Tile experts and pad sentinels (fewer than block_m pad rows per expert).
+  // Tile experts (global) and pad sentinels (fewer than block_m pad rows per
+  // expert, in LDS).
   for (int e = 0; e < E; ++e) {
     const int o0 = off[e], o1 = off[e + 1];
     for (int i = o0 / bm + tid; i < o1 / bm; i += kAlignThreads) a.tile_expert[i] = e;
     const int p = o0 + cnt[e] + tid;
-    if (p < o1) a.sorted_slot[p] = S;
+    if (p < o1) rows[p] = S;
   }
-  // Stable scatter of this thread's run.
-  for (int i = 0; i < n4; ++i) {
-    const int s = r0 + i;
-    if (s >= S) break;
+  // Stable scatter of this thread's run into LDS.
+#pragma unroll
+  for (int i = 0; i < kRunSlots; ++i) {
+    const int sl = r0 + i;
+    if (i >= n4 || sl >= S) break;
     const int e = run_id(i);
     uint32_t word = 0;
 #pragma unroll
-    for (int w = 0; w < kRunWords; ++w) word = (e >> 1) == w ? excl[w] : word;
+    for (int w = 0; w < W; ++w) word = (e >> 1) == w ? excl[w] : word;
     const int rank = (int)((e & 1) ? (word >> 16) : (word & 0xffffu));
-    a.sorted_slot[off[e] + rank] = s;
+    rows[off[e] + rank] = sl;
     const uint32_t inc = (e & 1) ? 0x10000u : 1u;
 #pragma unroll
-    for (int w = 0; w < kRunWords; ++w) excl[w] += (e >> 1) == w ? inc : 0u;
+    for (int w = 0; w < W; ++w) excl[w] += (e >> 1) == w ? inc : 0u;
   }
+  __syncthreads();
+  // The grouping in order: consecutive threads write consecutive rows.
+  const int total = off[E];
+  for (int p = tid; p < total; p += kAlignThreads) a.sorted_slot[p] = rows[p];
 }
 
 hipError_t launch_align(const AlignArgs& a, hipStream_t st) {
   if (a.S <= kSmallSlots)
     hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(64), 0, st, a);
+  else if (a.S <= kRunMaxSlots && a.E <= 8)
+    hipLaunchKernelGGL(align_runs_kernel<4>, dim3(1), dim3(kAlignThreads), 0, st, a);
   else if (a.S <= kRunMaxSlots && a.E <= 2 * kRunWords)
-    hipLaunchKernelGGL(align_runs_kernel, dim3(1), dim3(kAlignThreads), 0, st, a);
+    hipLaunchKernelGGL(align_runs_kernel<kRunWords>, dim3(1), dim3(kAlignThreads), 0, st, a);
   else
     hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, st, a);
   return hipGetLastError();

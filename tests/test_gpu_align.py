@@ -40,10 +40,11 @@ def check(ids, E, bm):
                                       (8192, 2, 8, 128), (8192, 2, 8, 256), (16384, 2, 8, 256),
                                       (257, 3, 64, 64), (1000, 1, 4, 32), (2049, 8, 8, 32),
                                       (64, 2, 8, 128),
-                                      # around the one-wave path's limit of 256 slots
-                                      (128, 2, 8, 32), (257, 1, 8, 64), (32, 2, 64, 32),
-                                      (33, 1, 1, 256), (65, 1, 8, 32), (256, 1, 8, 32),
-                                      # the per-thread-run path (256 < S <= 32768, E <= 16)
+                                      # around the one-wave path's limit of 128 slots
+                                      (64, 2, 8, 32), (129, 1, 8, 64), (32, 2, 64, 32),
+                                      (33, 1, 1, 256), (65, 1, 8, 32), (128, 1, 8, 32),
+                                      (256, 1, 8, 32), (100, 2, 12, 32),
+                                      # the per-thread-run path (128 < S <= 32768, E <= 16)
                                       # and the chunked path beyond it
                                       (1024, 2, 8, 32), (2049, 1, 8, 64),
                                       (1025, 2, 16, 64), (3000, 2, 64, 64),
