@@ -121,6 +121,29 @@ moe_status moe_route_mx(const void* x, const void* w_router, const float* bias, 
                         void* x_scale_e8m0, hipStream_t stream);
 
 /*
+ * moe_route_align - moe_route (quant 0: no token quantisation, 1: the per-token
+ * FP8 quantisation, x_scale fp32 [T]; 2: the MXFP8 block quantisation of
+ * moe_route_mx, x_scale E8M0 uint8 [T, H/32]) followed by moe_align of its ids
+ * with block_m, in one launch where the batch allows: the router's workgroups
+ * each take an integer ticket after writing their tokens, and the last one to
+ * arrive builds the grouping (the talk summary, 5:56, fuses the routed GEMM's
+ * steps into a single kernel; this fuses the two cheap steps before it).
+ * Results are exactly those of the two calls. One launch when T < 1024,
+ * T*k <= 2048 and E <= 16; otherwise the two kernels run back to back.
+ *
+ * ticket   int32 [1], device memory that is zero before the first call; every
+ *          call leaves it zero again. Calls that share a ticket must be
+ *          ordered (same stream or synchronised).
+ * Other arguments as moe_route / moe_route_mx (logits are not produced) and
+ * moe_align; the same checks (plus block_m), before any launch.
+ */
+moe_status moe_route_align(const void* x, const void* w_router, const float* bias, int T, int H,
+                           int E, int k, int quant, int32_t* topk_ids, float* topk_w, void* x_q,
+                           void* x_scale, int block_m, int32_t* sorted_slot,
+                           int32_t* tile_expert, int32_t* expert_count, int32_t* expert_offset,
+                           int32_t* total_padded, int32_t* ticket, hipStream_t stream);
+
+/*
  * moe_align - groups the T*k token-slots by expert and pads each group to the
  * M-tile (the "dynamic expert sizes" of the talk summary, 5:56).
  *
@@ -195,9 +218,10 @@ moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, con
  *   act[p, i] = bf16(silu(g_i) * u_i),
  *   silu(z) = z/(1+e^-z).
  * Pad rows (s == T*k) get act = 0.
- * FP8 also writes act_amax: per row p, partial maxima of |act[p,:]| over column
- * blocks, [capacity][moe_stage1_amax_floats()/capacity] floats (row-major);
- * stage 2 reduces them.
+ * FP8 also writes act_amax: per row p, partial maxima of |silu(g_i) * u_i| (the
+ * fp32 values, before their bf16 rounding) over column blocks,
+ * [capacity][moe_stage1_amax_floats()/capacity] floats (row-major, 16-byte
+ * aligned); stage 2 reduces them to the row's requantisation scale.
  *
  * x_or_xq  bf16 [T,H] (BF16) or e4m3fn [T,H] (FP8 from moe_route, MXFP8 and
  *          MXFP4 from moe_route_mx)
@@ -218,23 +242,32 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, co
 /*
  * moe_stage2 - grouped down GEMM + weighted scatter-combine (talk summary 5:56,
  * "Scatter"). For each real row p (slot s, token t = s / k, expert e):
- *   y = W2[e] act_p   (FP8: act_p requantised per row, scale = max|act_p|/448,
- *                      code = e4m3fn(act_p / scale); MXFP8, MXFP4: act_p
- *                      quantised per block of 32 values as moe_route_mx does x;
- *                      fp32 accumulation)
+ *   y = W2[e] act_p   (FP8: act_p requantised per row, scale = max|act_p|/448
+ *                      from stage 1's partial maxima, code = e4m3fn(act_p /
+ *                      scale) with a correctly rounded fp32 quotient, done as
+ *                      the GEMM loads the row; MXFP8, MXFP4: act_p quantised per
+ *                      block of 32 values as moe_route_mx does x, in a pass
+ *                      before the GEMM; fp32 accumulation)
  *   out[t, :] = bf16( sum_{j=0..k-1} w[t,j] * y_{t,j} ), summed in ascending j
  *   in fp32: a fixed order, no floating-point atomics, so results are
- *   reproducible bit for bit on a given device. (At prefill sizes the tiles
- *   of a partial last round of workgroups are cut into pieces along the
- *   reduction whose partials are summed in piece order; the cut follows from
- *   the number of workgroups the device runs at once.)
+ *   reproducible bit for bit. The sum is taken inside the GEMM launch: the
+ *   workgroup that writes the last of a token's partials for a block of
+ *   output columns (an integer ticket per token and block) adds them in that
+ *   order. (At prefill sizes the tiles of a partial last round of workgroups
+ *   are cut into pieces along the reduction whose partials are summed in
+ *   piece order; the cut follows from the shapes and the device-side padded
+ *   total only, with a fixed round of 256 workgroups, never from a property
+ *   queried from the device. Decode sizes split the reduction over
+ *   workgroups the same way: partial g of slot j is added at u = j*kg + g.)
  *
  * act, act_amax from moe_stage1 (act_amax unused, may be NULL, unless FP8);
  * w2, s2 from moe_preshuffle; topk_w fp32 [T,k]
  * out bf16 [T,H] (out); workspace [moe_stage2_workspace_bytes()] bytes (device,
- * 256-byte aligned): per-slot weighted partials, for FP8, MXFP8 and MXFP4 the
- * requantised intermediate, and at prefill sizes the partials of those
- * reduction pieces.
+ * 256-byte aligned): per-slot weighted partials, for MXFP8 and MXFP4 the
+ * block-quantised intermediate, at prefill sizes the partials of those
+ * reduction pieces, and the integer tickets. The workspace must be zero-filled
+ * once before its first use (the tickets); every call leaves the tickets zero,
+ * so a workspace is reused without clearing it again.
  * Calls that use one workspace must be ordered (same stream or synchronised).
  */
 int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int I, int block_m);

@@ -43,6 +43,17 @@ __device__ __forceinline__ float clamp448(float v) {
   return fminf(fmaxf(v, -448.0f), 448.0f);
 }
 
+// e4m3fn input of a per-row quantisation: clamp(RN(x / s), -448, 448), the
+// quotient correctly rounded in fp32, from r = RN(1 / s) computed once per row
+// (Markstein's correction): q0 = RN(x * r) is within one ulp of x / s, the
+// remainder x - s * q0 is exact in one fma, and RN(q0 + rem * r) = RN(x / s)
+// whenever the quotient is a normal number. Smaller quotients encode to a
+// (signed) zero code either way; copysign keeps the sign of a zero x.
+__device__ __forceinline__ float quant_div(float x, float s, float r) {
+  const float q0 = x * r;
+  return clamp448(copysignf(fmaf(fmaf(-q0, s, x), r, q0), x));
+}
+
 // Shared exponent of an MX block with E4M3 elements (OCP Microscaling): the
 // largest magnitude amax sets x = floor(log2 amax) - 8, 8 being the exponent
 // of E4M3's largest normal (448 = 1.75 * 2^8), clamped to the E8M0 range
@@ -60,6 +71,44 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 // float; smaller products encode to a zero e4m3fn code either way.
 __device__ __forceinline__ float mx_inv_scale(int x) {
   return __uint_as_float((uint32_t)(127 - x) << 23);
+}
+
+// Release of this thread's earlier global writes to every workgroup of the
+// device (agent scope), and the matching acquire. Workgroups that hand results
+// to each other through a ticket (an integer counter, no floating-point
+// atomics) use them around it: the writers release before taking the ticket,
+// and the workgroup that finds itself last acquires before reading.
+__device__ __forceinline__ void release_device() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+}
+__device__ __forceinline__ void acquire_device() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+__device__ __forceinline__ int ticket_add(int32_t* t, int v) {
+  return __hip_atomic_fetch_add(t, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ticket_reset(int32_t* t) {
+  __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whether this workgroup is the last of n to arrive at `ticket` (the same
+// answer in every thread). Every thread's global writes made before the call
+// are visible to the last workgroup after it; the last workgroup resets the
+// ticket to zero, so the next launch finds it as this one did. `flag` is one
+// int of LDS.
+__device__ __forceinline__ bool last_workgroup(int32_t* ticket, int n, int* flag) {
+  release_device();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const bool last = ticket_add(ticket, 1) == n - 1;
+    if (last) {
+      acquire_device();
+      ticket_reset(ticket);
+    }
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
 }
 
 // Physical workgroup id -> logical tile id so that each XCD (workgroups are

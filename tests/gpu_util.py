@@ -1,7 +1,10 @@
 """Helpers of the GPU parity tests: upload workloads, run the library, compare."""
 from __future__ import annotations
 
+import json
+import os
 import sys
+import time
 
 import numpy as np
 import torch
@@ -76,3 +79,50 @@ def sample_tokens(ids: np.ndarray, E: int, n: int, seed: int = 0) -> np.ndarray:
     rest = [t for t in rng.permutation(T) if t not in pick]
     pick.update(int(t) for t in rest[: max(0, n - len(pick))])
     return np.array(sorted(pick), np.int32)
+
+
+def tile_rows(block_m: int) -> int:
+    """Rows of one GEMM row tile for a grouping with M-tile block_m (both stages tile the
+    grouped rows in 32-, 64- or 128-row tiles that never straddle two experts)."""
+    return min(block_m, 128)
+
+
+def cover_tokens(ids: np.ndarray, E: int, block_m: int, seed: int = 0) -> np.ndarray:
+    """Tokens whose layer outputs, compared element by element, touch every live row tile of
+    both GEMM stages: one real slot drawn from each row tile of the grouping (a slot's output
+    row spans every feature tile of stage 2, and its intermediate row every feature tile of
+    stage 1), plus the first and the last token. The grouping is the oracle's."""
+    import oracle
+    T, k = ids.shape
+    g = oracle.align(ids, E, block_m)
+    ss, tr = g["sorted_slot"], tile_rows(block_m)
+    rng = np.random.default_rng(seed)
+    pick = {0, T - 1}
+    for r0 in range(0, g["total"], tr):
+        real = ss[r0:r0 + tr]
+        real = real[real < T * k]
+        if real.size:
+            pick.add(int(real[rng.integers(real.size)]) // k)
+    return np.array(sorted(pick), np.int32)
+
+
+def live_row_tiles(ids: np.ndarray, E: int, block_m: int) -> int:
+    import oracle
+    return oracle.align(ids, E, block_m)["total"] // tile_rows(block_m)
+
+
+ERROR_LOG = os.environ.get("MOE_PARITY_LOG", os.path.join(
+    os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
+    "parity_errors.jsonl"))
+
+
+def record_error(case: str, err: float, tol: float, tokens: int, total_tokens: int, **extra):
+    """Append one parity figure (max|err|/max|ref| of the layer output) to the JSONL log."""
+    rec = {"case": case, "rel_err": err, "tolerance": tol, "tokens_checked": tokens,
+           "tokens": total_tokens, "time": time.strftime("%Y-%m-%d %H:%M:%S"), **extra}
+    try:
+        os.makedirs(os.path.dirname(ERROR_LOG), exist_ok=True)
+        with open(ERROR_LOG, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    except OSError as e:  # a read-only tree must not fail the parity test itself
+        say(f"(parity log not written: {e})")

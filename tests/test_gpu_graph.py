@@ -1,14 +1,16 @@
 """The layer captured in a HIP graph: every replay, with eager work and host
-synchronisations between replays, equals the eager call on the same tokens,
-bit for bit (decode-size FP8 and MXFP4, an MXFP8 prefill-tile shape, and a BF16
-shape whose stage 2 cuts its last round into reduction pieces)."""
+synchronisations between replays, matches the CPU oracle on that replay's
+tokens within the layer's tolerance, and equals the eager call on the same
+tokens bit for bit (decode-size FP8 and MXFP4, an MXFP8 prefill-tile shape, and
+a BF16 shape whose stage 2 cuts its last round into reduction pieces)."""
 import numpy as np
 import pytest
 import torch
 
 import mixture_experts_routed_top_amd as moe
+import oracle
 import workloads
-from gpu_util import dev, host, say
+from gpu_util import TOL, dev, host, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +46,12 @@ def test_graph_replays_match_eager(dtype, T, H, I, E, k, bm):
         graph.replay()
         torch.cuda.synchronize()
         got = host(layer.out)
+        batch = workloads.Inputs(inp.wl, workloads.to_bf16_bits(xb), inp.w_router, None, inp.w1,
+                                 inp.w3, inp.w2, inp.s1, inp.s3, inp.s2)
+        _, o64 = oracle.forward(batch)
+        err = rel_err(got, o64)
+        say(f"  replay {rep}: max|err|/max|ref| = {err:.3e}")
+        assert err <= TOL[dtype], f"replay {rep}: error {err} against the oracle"
         assert np.array_equal(got, ref), f"replay {rep} differs from the eager call"
         # eager work of the program's own between replays
         _ = (new.float() * 2).sum().item()
