@@ -65,6 +65,8 @@ def lib():
         L.oracle_store_intermediate.argtypes = [i, P, i, i]
         L.oracle_preshuffle_w13.argtypes = [i, i, i, i, P, P, P]
         L.oracle_preshuffle_w2.argtypes = [i, i, i, i, P, P]
+        L.oracle_forward_f64.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P]
+        L.oracle_backward.argtypes = [P, P, P, P, P, P, i, i, i, i, i, P, P, P, P, P, P, P]
         L.oracle_threads.restype = ctypes.c_int
         for name in ("oracle_f32_to_e4m3fn_n", "oracle_e4m3fn_to_f64_n",
                      "oracle_f32_to_bf16_n", "oracle_bf16_to_f64_n", "oracle_e8m0_to_f64_n",
@@ -246,6 +248,40 @@ def forward(inp, tokens=None):
                          _p(inp.w1), _p(inp.w3), _p(inp.w2), _p(inp.s1), _p(inp.s3), _p(inp.s2),
                          wl.T, wl.H, wl.I, wl.E, wl.k, _p(tokens), n, _p(out), _p(o64))
     return out, o64
+
+
+# --- backward pass (bf16 layer) -------------------------------------------
+
+def forward_f64(x, w_router, bias, w1, w3, w2, ids):
+    """fp64 layer output for fp64 parameters and a fixed selection ids [T,k] (no storage
+    roundings): the function whose gradients backward() returns."""
+    x, w_router, w1, w3, w2 = (np.ascontiguousarray(a, np.float64)
+                               for a in (x, w_router, w1, w3, w2))
+    b = None if bias is None else np.ascontiguousarray(bias, np.float64)
+    ids = np.ascontiguousarray(ids, np.int32)
+    T, H = x.shape
+    E, I = w1.shape[0], w1.shape[1]
+    out = np.empty((T, H), np.float64)
+    lib().oracle_forward_f64(_p(x), _p(w_router), _p(b), _p(w1), _p(w3), _p(w2), _p(ids), T, H,
+                             I, E, ids.shape[1], _p(out))
+    return out
+
+
+def backward(inp, dout):
+    """Gradients of sum <dout, out> for a bf16 workloads.Inputs and a bf16 dout [T,H]:
+    dict(dx [T,H], dw1 [E,I,H], dw3 [E,I,H], dw2 [E,H,I], dw_router [E,H], dbias [E]),
+    all fp64, the selection held at the forward's."""
+    wl = inp.wl
+    assert wl.dtype == "bf16", "the backward is defined for the bf16 layer"
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    dout = np.ascontiguousarray(dout, np.uint16)
+    r = dict(dx=np.empty((T, H)), dw1=np.empty((E, I, H)), dw3=np.empty((E, I, H)),
+             dw2=np.empty((E, H, I)), dw_router=np.empty((E, H)), dbias=np.empty(E))
+    b = None if inp.bias is None else np.ascontiguousarray(inp.bias, np.float32)
+    lib().oracle_backward(_p(inp.x), _p(inp.w_router), _p(b), _p(inp.w1), _p(inp.w3),
+                          _p(inp.w2), T, H, I, E, k, _p(dout), _p(r["dx"]), _p(r["dw1"]),
+                          _p(r["dw3"]), _p(r["dw2"]), _p(r["dw_router"]), _p(r["dbias"]))
+    return r
 
 
 # --- preshuffle layout -----------------------------------------------------

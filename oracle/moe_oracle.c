@@ -660,3 +660,211 @@ void oracle_bf16_to_f64_n(const uint16_t* b, long n, double* v)
     for (long i = 0; i < n; ++i)
         v[i] = oracle_bf16_to_f64(b[i]);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass of the bf16 layer (the custom VJP the FlyDSL-in-JAX talk     */
+/* summary lists as its next step, "Ausblick und Roadmap" 10:07; "broader    */
+/* backward coverage" in the glance summary's "What's Next?")                 */
+/*                                                                            */
+/* The pages give no formula. The plainest reading, adopted here: the exact   */
+/* gradient of the layer function                                             */
+/*   out_t = sum_j w_tj * W2[e_j] (silu(W1[e_j] x_t) * W3[e_j] x_t),          */
+/*   w_t = softmax over the k selected logits l_tj = W_r[e_j] . x_t (+ b),    */
+/* with the selection e_tj held fixed (top-k is piecewise constant), taken in */
+/* fp64 on the bf16 input values, for a given output gradient dout. Storage   */
+/* roundings of the forward (the bf16 intermediate and output) are not part of*/
+/* the function being differentiated.                                         */
+
+/* fp64 forward of that function for given (perturbable) fp64 parameters and a
+ * fixed selection ids[T,k]: out[T,H]. Used to pin the gradients by finite
+ * differences. */
+void oracle_forward_f64(const double* x, const double* wr, const double* bias,
+                        const double* w1, const double* w3, const double* w2,
+                        const int32_t* ids, int T, int H, int I, int E, int k, double* out)
+{
+    (void)E;
+    for (int t = 0; t < T; ++t) {
+        const double* xt = x + (size_t)t * H;
+        double l[64], w[64], m = -INFINITY, den = 0.0;
+        for (int j = 0; j < k; ++j) {
+            int e = ids[(size_t)t * k + j];
+            double s = bias ? bias[e] : 0.0;
+            for (int h = 0; h < H; ++h)
+                s += wr[(size_t)e * H + h] * xt[h];
+            l[j] = s;
+            if (s > m)
+                m = s;
+        }
+        for (int j = 0; j < k; ++j) {
+            w[j] = exp(l[j] - m);
+            den += w[j];
+        }
+        double* o = out + (size_t)t * H;
+        for (int h = 0; h < H; ++h)
+            o[h] = 0.0;
+        double* a = (double*)malloc(sizeof(double) * (size_t)I);
+        for (int j = 0; j < k; ++j) {
+            int e = ids[(size_t)t * k + j];
+            double wj = w[j] / den;
+#pragma omp parallel for schedule(static)
+            for (int i = 0; i < I; ++i) {
+                size_t r = ((size_t)e * I + i) * H;
+                double g = 0.0, u = 0.0;
+                for (int c = 0; c < H; ++c) {
+                    g += w1[r + c] * xt[c];
+                    u += w3[r + c] * xt[c];
+                }
+                a[i] = silu(g) * u;
+            }
+#pragma omp parallel for schedule(static)
+            for (int h = 0; h < H; ++h) {
+                double y = 0.0;
+                for (int i = 0; i < I; ++i)
+                    y += w2[((size_t)e * H + h) * I + i] * a[i];
+                o[h] += wj * y;
+            }
+        }
+        free(a);
+    }
+}
+
+/* Gradients of sum_t <dout_t, out_t> with respect to x, W1, W3, W2, W_r and the
+ * bias, for the bf16 layer (inputs as bf16 bit patterns, dout bf16 [T,H]).
+ * The selection is the forward's (fixed-order fp32 logits, oracle_route); the
+ * routing weights and everything else are fp64. Per token and selected expert
+ * e (rank j):
+ *   g = W1 x, u = W3 x, a = silu(g) u, y = W2 a        (the forward values)
+ *   dw_j = <dout, y>                                   (gradient of w_j)
+ *   z = W2^T dout, da = w_j z                          (gradient of a)
+ *   dg = da u silu'(g), du = da silu(g),  silu'(g) = s (1 + g (1 - s)), s = sigmoid(g)
+ *   dW2[e] += (w_j dout) a^T,  dW1[e] += dg x^T,  dW3[e] += du x^T
+ *   dx += W1^T dg + W3^T du
+ * then the softmax over the selected logits: dl_j = w_j (dw_j - sum_i w_i dw_i),
+ *   dW_r[e_j] += dl_j x,  db[e_j] += dl_j,  dx += sum_j dl_j W_r[e_j].
+ * Outputs are fp64 and overwritten: dx [T,H], dw1 and dw3 [E,I,H], dw2 [E,H,I],
+ * dwr [E,H], dbias [E] (may be NULL). Tokens are taken one after another (the
+ * weight gradients accumulate in token order); OpenMP splits rows inside. */
+void oracle_backward(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                     const uint16_t* w1, const uint16_t* w3, const uint16_t* w2, int T, int H,
+                     int I, int E, int k, const uint16_t* dout, double* dx, double* dw1,
+                     double* dw3, double* dw2, double* dwr, double* dbias)
+{
+    memset(dx, 0, sizeof(double) * (size_t)T * H);
+    memset(dw1, 0, sizeof(double) * (size_t)E * I * H);
+    memset(dw3, 0, sizeof(double) * (size_t)E * I * H);
+    memset(dw2, 0, sizeof(double) * (size_t)E * H * I);
+    memset(dwr, 0, sizeof(double) * (size_t)E * H);
+    if (dbias)
+        memset(dbias, 0, sizeof(double) * (size_t)E);
+    double* xt = (double*)malloc(sizeof(double) * (size_t)H);
+    double* dy = (double*)malloc(sizeof(double) * (size_t)H);
+    double* g = (double*)malloc(sizeof(double) * (size_t)I);
+    double* u = (double*)malloc(sizeof(double) * (size_t)I);
+    double* a = (double*)malloc(sizeof(double) * (size_t)I);
+    double* z = (double*)malloc(sizeof(double) * (size_t)I);
+    double* dg = (double*)malloc(sizeof(double) * (size_t)I);
+    double* du = (double*)malloc(sizeof(double) * (size_t)I);
+    for (int t = 0; t < T; ++t) {
+        int32_t ids[64];
+        float wf[64];
+        oracle_route(x + (size_t)t * H, w_router, bias, 1, H, E, k, ids, wf, NULL);
+        for (int h = 0; h < H; ++h) {
+            xt[h] = oracle_bf16_to_f64(x[(size_t)t * H + h]);
+            dy[h] = oracle_bf16_to_f64(dout[(size_t)t * H + h]);
+        }
+        /* routing weights in fp64 from fp64 logits */
+        double l[64], w[64], m = -INFINITY, den = 0.0, dwj[64];
+        for (int j = 0; j < k; ++j) {
+            double s = bias ? (double)bias[ids[j]] : 0.0;
+            for (int h = 0; h < H; ++h)
+                s += oracle_bf16_to_f64(w_router[(size_t)ids[j] * H + h]) * xt[h];
+            l[j] = s;
+            if (s > m)
+                m = s;
+        }
+        for (int j = 0; j < k; ++j) {
+            w[j] = exp(l[j] - m);
+            den += w[j];
+        }
+        for (int j = 0; j < k; ++j)
+            w[j] /= den;
+        for (int j = 0; j < k; ++j) {
+            const int e = ids[j];
+#pragma omp parallel for schedule(static)
+            for (int i = 0; i < I; ++i) {
+                size_t r = ((size_t)e * I + i) * H;
+                double gg = 0.0, uu = 0.0;
+                for (int h = 0; h < H; ++h) {
+                    gg += oracle_bf16_to_f64(w1[r + h]) * xt[h];
+                    uu += oracle_bf16_to_f64(w3[r + h]) * xt[h];
+                }
+                g[i] = gg;
+                u[i] = uu;
+                a[i] = silu(gg) * uu;
+            }
+            /* z = W2^T dout and dw_j = <dout, W2 a> = <z, a> */
+#pragma omp parallel for schedule(static)
+            for (int i = 0; i < I; ++i) {
+                double s = 0.0;
+                for (int h = 0; h < H; ++h)
+                    s += oracle_bf16_to_f64(w2[((size_t)e * H + h) * I + i]) * dy[h];
+                z[i] = s;
+            }
+            double d = 0.0;
+            for (int i = 0; i < I; ++i)
+                d += z[i] * a[i];
+            dwj[j] = d;
+            for (int i = 0; i < I; ++i) {
+                double sg = 1.0 / (1.0 + exp(-g[i]));
+                double da = w[j] * z[i];
+                dg[i] = da * u[i] * sg * (1.0 + g[i] * (1.0 - sg));
+                du[i] = da * g[i] * sg;
+            }
+#pragma omp parallel for schedule(static)
+            for (int h = 0; h < H; ++h) {
+                double* row = dw2 + ((size_t)e * H + h) * I;
+                for (int i = 0; i < I; ++i)
+                    row[i] += w[j] * dy[h] * a[i];
+            }
+#pragma omp parallel for schedule(static)
+            for (int i = 0; i < I; ++i) {
+                double* r1 = dw1 + ((size_t)e * I + i) * H;
+                double* r3 = dw3 + ((size_t)e * I + i) * H;
+                for (int h = 0; h < H; ++h) {
+                    r1[h] += dg[i] * xt[h];
+                    r3[h] += du[i] * xt[h];
+                }
+            }
+#pragma omp parallel for schedule(static)
+            for (int h = 0; h < H; ++h) {
+                double s = 0.0;
+                for (int i = 0; i < I; ++i) {
+                    size_t r = ((size_t)e * I + i) * H + h;
+                    s += oracle_bf16_to_f64(w1[r]) * dg[i] + oracle_bf16_to_f64(w3[r]) * du[i];
+                }
+                dx[(size_t)t * H + h] += s;
+            }
+        }
+        double sw = 0.0;
+        for (int j = 0; j < k; ++j)
+            sw += w[j] * dwj[j];
+        for (int j = 0; j < k; ++j) {
+            const int e = ids[j];
+            const double dl = w[j] * (dwj[j] - sw);
+            for (int h = 0; h < H; ++h) {
+                dwr[(size_t)e * H + h] += dl * xt[h];
+                dx[(size_t)t * H + h] += dl * oracle_bf16_to_f64(w_router[(size_t)e * H + h]);
+            }
+            if (dbias)
+                dbias[e] += dl;
+        }
+    }
+    free(xt);
+    free(dy);
+    free(g);
+    free(u);
+    free(a);
+    free(z);
+    free(dg);
+    free(du);
+}
