@@ -26,7 +26,10 @@ The same line carries:
   mxfp4         the layer with MXFP4 (E2M1) expert weights and MXFP8 tokens: prefill
                 T=8192 and the decode sweep T = 1 .. 256, weight GB/s over the
                 active experts' codes and scales;
-  cpu_baseline  the CPU oracle on the first tokens of the same workload.
+  cpu_baseline  the CPU oracle on the first tokens of the same workload; per_workload
+                holds its wall time (oracle_s, cores) on up to 16 tokens of each of the
+                other workloads (the tiny layer, the BF16 decode batch, each FP8 decode
+                batch and the skewed layer).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-sweep]
                     [--no-cpu-baseline] [--cpu-tokens 64] [--copy-calibration]
@@ -93,18 +96,32 @@ def make_layer(inp, block_m=None):
 
 def cpu_baseline(inp, n_tokens):
     """The CPU oracle, as it stands, on the first n_tokens tokens of the same workload."""
+    wl = inp.wl
+    r = oracle_time(inp, n_tokens)
+    return {"value": r["tflops"], "unit": "TFLOP/s", "cores": r["cores"], "kind": "oracle",
+            "sample": f"whole layer (route, quantise, {wl.k} experts, combine) for the first "
+                      f"{r['tokens']} of {wl.T} tokens of {wl.name}: {r['oracle_s']:.1f} s wall; "
+                      f"effective flops 6*H*I per token-slot"}
+
+
+ORACLE_TIMES = []  # one record per workload, filled by the legs that have its inputs
+
+
+def oracle_time(inp, n_tokens):
+    """Wall time of the CPU oracle (whole layer) on the first n_tokens tokens of a workload
+    (all of them when the batch is smaller), recorded in ORACLE_TIMES."""
     import oracle
     wl = inp.wl
     toks = np.arange(min(n_tokens, wl.T), dtype=np.int32)
     t0 = time.perf_counter()
     oracle.forward(inp, toks)
     dt = time.perf_counter() - t0
-    flops = 6.0 * wl.H * wl.I * wl.k * toks.size
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"whole layer (route, quantise, {wl.k} experts, combine) for the first "
-                      f"{toks.size} of {wl.T} tokens of {wl.name}: {dt:.1f} s wall; effective "
-                      f"flops 6*H*I per token-slot"}
+    rec = {"workload": wl.name, "T": wl.T, "tokens": int(toks.size), "oracle_s": round(dt, 3),
+           "oracle_s_per_token": round(dt / toks.size, 4), "cores": oracle.threads(),
+           "tflops": round(6.0 * wl.H * wl.I * wl.k * toks.size / dt / 1e12, 6)}
+    ORACLE_TIMES.append(rec)
+    log(f"[bench] oracle {wl.name}: {toks.size} tokens in {dt:.2f} s")
+    return rec
 
 
 def evict(flush):
@@ -163,9 +180,10 @@ def flush_buffer():
     return torch.zeros(128 << 20, dtype=torch.float32, device="cuda")  # 512 MB, 2x the Infinity Cache
 
 
-def decode_sweep(runs):
+def decode_sweep(runs, oracle_tokens=0):
     """FP8 decode batches: per-T median latency of the whole layer over `runs` calls with
-    the Infinity Cache flushed between calls, tokens/s, weight GB/s."""
+    the Infinity Cache flushed between calls, tokens/s, weight GB/s (and, with
+    oracle_tokens, the CPU oracle's time on up to that many tokens of each batch)."""
     import torch
     import workloads
     base = workloads.generate(workloads.config(3, workloads.DECODE_SWEEP[0]), threads=16)
@@ -175,14 +193,18 @@ def decode_sweep(runs):
     out = []
     for T in workloads.DECODE_SWEEP:
         wl = workloads.config(3, T)
-        x = dev(workloads.generate(wl, weights=False).x)
+        xi = workloads.generate(wl, weights=False)
+        x = dev(xi.x)
         out.append(decode_line(wl, layer, x, runs, flush, 1))
+        if oracle_tokens:
+            oracle_time(workloads.Inputs(wl, xi.x, base.w_router, None, base.w1, base.w3, base.w2,
+                                         base.s1, base.s3, base.s2), oracle_tokens)
     del layer, flush
     torch.cuda.empty_cache()
     return out
 
 
-def bf16_decode(runs):
+def bf16_decode(runs, oracle_tokens=0):
     """The BF16 decode batch (Mixtral shape, T=16), measured like the FP8 sweep."""
     import torch
     import workloads
@@ -191,13 +213,15 @@ def bf16_decode(runs):
     layer = make_layer(inp)
     flush = flush_buffer()
     rec = decode_line(wl, layer, dev(inp.x), runs, flush, 2)
+    if oracle_tokens:
+        oracle_time(inp, oracle_tokens)
     rec = {"workload": wl.name, **rec}
     del layer, flush
     torch.cuda.empty_cache()
     return rec
 
 
-def skewed(steps):
+def skewed(steps, oracle_tokens=0):
     """The skewed FP8 workload (T=16384, ~40% of slots on expert 0): latency, effective
     TFLOP/s, and what the skew does to the grouping (slots and row tiles per expert, pad rows)."""
     import torch
@@ -225,6 +249,8 @@ def skewed(steps):
     log(f"[bench] {wl.name}: {ms:.3f} ms, {tf:.0f} TFLOP/s, expert slots {count.tolist()}")
     del layer
     torch.cuda.empty_cache()
+    if oracle_tokens:
+        oracle_time(inp, oracle_tokens)
     return {"workload": wl.name, "T": wl.T, "ms": round(ms, 4), "tflops": round(tf, 2),
             "frac_of_fp8_peak": round(tf / PEAK["fp8"], 4),
             "tokens_per_s": round(wl.T / (ms * 1e-3), 1), "block_m": bm,
@@ -340,6 +366,8 @@ def main():
                     help="only time the FP8 decode batch T (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--oracle-tokens", type=int, default=16,
+                    help="tokens of each other workload the CPU oracle is timed on")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
@@ -432,15 +460,18 @@ def main():
                      "frac": round(s1_tf / peak, 4), "traffic": traffic,
                      "avg_launch_ms": round(s1_ms, 4)},
     }
+    ot = 0 if args.no_cpu_baseline else args.oracle_tokens
     if not args.no_sweep:
-        rec["decode_sweep"] = decode_sweep(args.decode_runs)
-        rec["bf16_decode"] = bf16_decode(args.decode_runs)
-        rec["skewed"] = skewed(max(5, args.steps // 2))
+        rec["decode_sweep"] = decode_sweep(args.decode_runs, ot)
+        rec["bf16_decode"] = bf16_decode(args.decode_runs, ot)
+        rec["skewed"] = skewed(max(5, args.steps // 2), ot)
         rec["mxfp8"] = mxfp8(max(5, args.steps // 2), args.decode_runs)
         rec["mxfp4"] = mxfp4(max(5, args.steps // 2), args.decode_runs)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+        oracle_time(workloads.generate(workloads.config(0)), 32)
+        rec["cpu_baseline"]["per_workload"] = ORACLE_TIMES
     print(json.dumps(rec), flush=True)
 
 

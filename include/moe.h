@@ -121,29 +121,6 @@ moe_status moe_route_mx(const void* x, const void* w_router, const float* bias, 
                         void* x_scale_e8m0, hipStream_t stream);
 
 /*
- * moe_route_align - moe_route (quant 0: no token quantisation, 1: the per-token
- * FP8 quantisation, x_scale fp32 [T]; 2: the MXFP8 block quantisation of
- * moe_route_mx, x_scale E8M0 uint8 [T, H/32]) followed by moe_align of its ids
- * with block_m, in one launch where the batch allows: the router's workgroups
- * each take an integer ticket after writing their tokens, and the last one to
- * arrive builds the grouping (the talk summary, 5:56, fuses the routed GEMM's
- * steps into a single kernel; this fuses the two cheap steps before it).
- * Results are exactly those of the two calls. One launch when T < 1024,
- * T*k <= 2048 and E <= 16; otherwise the two kernels run back to back.
- *
- * ticket   int32 [1], device memory that is zero before the first call; every
- *          call leaves it zero again. Calls that share a ticket must be
- *          ordered (same stream or synchronised).
- * Other arguments as moe_route / moe_route_mx (logits are not produced) and
- * moe_align; the same checks (plus block_m), before any launch.
- */
-moe_status moe_route_align(const void* x, const void* w_router, const float* bias, int T, int H,
-                           int E, int k, int quant, int32_t* topk_ids, float* topk_w, void* x_q,
-                           void* x_scale, int block_m, int32_t* sorted_slot,
-                           int32_t* tile_expert, int32_t* expert_count, int32_t* expert_offset,
-                           int32_t* total_padded, int32_t* ticket, hipStream_t stream);
-
-/*
  * moe_align - groups the T*k token-slots by expert and pads each group to the
  * M-tile (the "dynamic expert sizes" of the talk summary, 5:56).
  *
@@ -220,8 +197,9 @@ moe_status moe_preshuffle(moe_dtype dt, int E, int H, int I, const void* w1, con
  * Pad rows (s == T*k) get act = 0.
  * FP8 also writes act_amax: per row p, partial maxima of |silu(g_i) * u_i| (the
  * fp32 values, before their bf16 rounding) over column blocks,
- * [capacity][moe_stage1_amax_floats()/capacity] floats (row-major, 16-byte
- * aligned); stage 2 reduces them to the row's requantisation scale.
+ * [capacity][moe_stage1_amax_floats()/capacity] floats (row-major); stage 2
+ * reduces them to the row's requantisation scale and quantises with a
+ * correctly rounded fp32 quotient.
  *
  * x_or_xq  bf16 [T,H] (BF16) or e4m3fn [T,H] (FP8 from moe_route, MXFP8 and
  *          MXFP4 from moe_route_mx)
@@ -242,32 +220,24 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, co
 /*
  * moe_stage2 - grouped down GEMM + weighted scatter-combine (talk summary 5:56,
  * "Scatter"). For each real row p (slot s, token t = s / k, expert e):
- *   y = W2[e] act_p   (FP8: act_p requantised per row, scale = max|act_p|/448
- *                      from stage 1's partial maxima, code = e4m3fn(act_p /
- *                      scale) with a correctly rounded fp32 quotient, done as
- *                      the GEMM loads the row; MXFP8, MXFP4: act_p quantised per
- *                      block of 32 values as moe_route_mx does x, in a pass
- *                      before the GEMM; fp32 accumulation)
+ *   y = W2[e] act_p   (FP8: act_p requantised per row, scale = max|act_p|/448,
+ *                      code = e4m3fn(act_p / scale); MXFP8, MXFP4: act_p
+ *                      quantised per block of 32 values as moe_route_mx does x;
+ *                      fp32 accumulation)
  *   out[t, :] = bf16( sum_{j=0..k-1} w[t,j] * y_{t,j} ), summed in ascending j
  *   in fp32: a fixed order, no floating-point atomics, so results are
- *   reproducible bit for bit. The sum is taken inside the GEMM launch: the
- *   workgroup that writes the last of a token's partials for a block of
- *   output columns (an integer ticket per token and block) adds them in that
- *   order. (At prefill sizes the tiles of a partial last round of workgroups
- *   are cut into pieces along the reduction whose partials are summed in
- *   piece order; the cut follows from the shapes and the device-side padded
- *   total only, with a fixed round of 256 workgroups, never from a property
- *   queried from the device. Decode sizes split the reduction over
- *   workgroups the same way: partial g of slot j is added at u = j*kg + g.)
+ *   reproducible bit for bit. (At prefill sizes the tiles of a partial last
+ *   round of workgroups are cut into pieces along the reduction whose
+ *   partials are summed in piece order; the cut follows from the shapes and
+ *   the device-side padded total only, with a fixed round of 256 workgroups,
+ *   never from a property queried from the device.)
  *
  * act, act_amax from moe_stage1 (act_amax unused, may be NULL, unless FP8);
  * w2, s2 from moe_preshuffle; topk_w fp32 [T,k]
  * out bf16 [T,H] (out); workspace [moe_stage2_workspace_bytes()] bytes (device,
- * 256-byte aligned): per-slot weighted partials, for MXFP8 and MXFP4 the
- * block-quantised intermediate, at prefill sizes the partials of those
- * reduction pieces, and the integer tickets. The workspace must be zero-filled
- * once before its first use (the tickets); every call leaves the tickets zero,
- * so a workspace is reused without clearing it again.
+ * 256-byte aligned): per-slot weighted partials, for FP8, MXFP8 and MXFP4 the
+ * requantised intermediate, and at prefill sizes the partials of those
+ * reduction pieces.
  * Calls that use one workspace must be ordered (same stream or synchronised).
  */
 int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int I, int block_m);
@@ -276,6 +246,55 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
                       const int32_t* total_padded, const float* topk_w, int T, int k, int E,
                       int H, int I, int block_m, void* out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward pass of the bf16 layer: the custom VJP the talk summary names as
+ * its next step ("Ausblick und Roadmap", 10:07; "broader backward coverage" in
+ * the glance summary's "What's Next?"). For an output gradient dout, the
+ * gradients of sum_t <dout_t, out_t> with respect to x, W1, W3, W2, W_r and the
+ * router bias, the forward's top-k selection held fixed (it is piecewise
+ * constant). Per slot s = t*k + j of expert e with routing weight w_j:
+ *   g = W1[e] x_t, u = W3[e] x_t, a = silu(g) u   (a is the forward's act row)
+ *   z = W2[e]^T dout_t,  dw_j = <z, a>,  da = w_j z
+ *   dg = da u s (1 + g (1 - s)), du = da g s, s = sigmoid(g)
+ *   dW2[e] += (w_j dout_t) a^T,  dW1[e] += dg x_t^T,  dW3[e] += du x_t^T
+ *   dl_j = w_j (dw_j - sum_i w_i dw_i)       (softmax over the selected logits)
+ *   dx_t = sum_j (W1[e_j]^T dg_j + W3[e_j]^T du_j) + sum_j dl_j W_r[e_j]
+ *   dW_r[e] = sum of dl_j x_t over the slots of e,  dbias[e] = sum of dl_j
+ * Arithmetic: bf16 operands on the matrix cores with fp32 accumulation; g, u,
+ * dg, du and w_j dout are held in bf16 between the launches; every sum runs in
+ * a fixed order, so the results are reproducible bit for bit.
+ *
+ * moe_backward_preshuffle - one-time relayout of the transposed weights the
+ * backward GEMMs read (W2^T [E][I][H] and [W1^T | W3^T] [E][H][2I], in the
+ * bf16 fragment order of moe_preshuffle). w1, w3 bf16 [E,I,H], w2 bf16 [E,H,I];
+ * w2t_out [moe_backward_preshuffle_bytes(E,H,I,0)] bytes, w13t_out [.., 1].
+ * Supported: H, I multiples of 128.
+ *
+ * moe_backward - the gradients. Inputs from the forward call on the same
+ * tokens: x bf16 [T,H], w_router bf16 [E,H], topk_ids / topk_w (moe_route),
+ * sorted_slot, tile_expert, expert_offset, total_padded (moe_align with
+ * block_m), act bf16 [capacity, I] (moe_stage1), w13 (moe_preshuffle, bf16),
+ * w2t, w13t (moe_backward_preshuffle); dout bf16 [T,H].
+ * Outputs (fp32, overwritten): dx [T,H]; dw1, dw3 [E,I,H]; dw2 [E,H,I];
+ * dw_router [E,H]; dbias [E] or NULL. Experts without a slot get zero
+ * gradients. workspace [moe_backward_workspace_bytes()] bytes, 256-byte
+ * aligned. Supported: the bf16 shapes of moe_stage1 (H, I multiples of 128),
+ * 4 * capacity * I below 2 GiB.
+ */
+int64_t moe_backward_preshuffle_bytes(int E, int H, int I, int which /*0: W2^T, 1: W13^T*/);
+moe_status moe_backward_preshuffle(int E, int H, int I, const void* w1, const void* w3,
+                                   const void* w2, void* w2t_out, void* w13t_out,
+                                   hipStream_t stream);
+int64_t moe_backward_workspace_bytes(int T, int k, int E, int H, int I, int block_m);
+moe_status moe_backward(const void* x, const void* w_router, const int32_t* topk_ids,
+                        const float* topk_w, const int32_t* sorted_slot,
+                        const int32_t* tile_expert, const int32_t* expert_offset,
+                        const int32_t* total_padded, const void* act, const void* w13,
+                        const void* w2t, const void* w13t, const void* dout, int T, int k,
+                        int E, int H, int I, int block_m, float* dx, float* dw1, float* dw3,
+                        float* dw2, float* dw_router, float* dbias, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

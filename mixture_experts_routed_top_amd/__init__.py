@@ -6,7 +6,7 @@ the current HIP stream, and checks status codes. All computation happens in the
 library's HIP kernels; torch provides device memory and streams only.
 
     ids, w, x_q, x_scale, _ = route(x, w_router, k, fp8=True)
-    grp = align(ids, E, block_m)        # or both in one launch: route_align(...)
+    grp = align(ids, E, block_m)
     pw = preshuffle("fp8", w1, w3, w2, s1, s3, s2)          # once, at load time
     act, amax = stage1("fp8", x_q, x_scale, pw, grp)
     out = stage2("fp8", act, amax, pw, grp, w)
@@ -25,8 +25,8 @@ import torch
 
 from ._lib import BF16, FP8, MXFP4, MXFP8, MoEError, check, lib
 
-__all__ = ["route", "align", "route_align", "preshuffle", "stage1", "stage2", "forward",
-           "Layer", "pick_block_m", "align_capacity", "MoEError"]
+__all__ = ["route", "align", "preshuffle", "stage1", "stage2", "forward", "Layer",
+           "preshuffle_backward", "backward", "pick_block_m", "align_capacity", "MoEError"]
 
 
 def _dt(dtype) -> int:
@@ -121,36 +121,6 @@ def align(topk_ids: torch.Tensor, E: int, block_m: int) -> Grouping:
     return Grouping(ss, te, cnt, off, tot, T, k, E, block_m)
 
 
-def route_align(x: torch.Tensor, w_router: torch.Tensor, k: int, E: int, block_m: int,
-                bias: torch.Tensor | None = None, quant: str | None = None, ticket=None):
-    """route() and align() in one launch where the batch allows (moe_route_align).
-    quant: None, "fp8" (per-token scales) or "mx" (MXFP8 block codes).
-    -> (ids, w, x_q | None, x_scale | None, Grouping)."""
-    T, H = x.shape
-    dev = x.device
-    q = {None: 0, "fp8": 1, "mx": 2}[quant]
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    xq = torch.empty((T, H), dtype=torch.uint8, device=dev) if q else None
-    xs = (torch.empty((T,), dtype=torch.float32, device=dev) if q == 1 else
-          torch.empty((T, H // 32), dtype=torch.uint8, device=dev) if q == 2 else None)
-    cap = align_capacity(T, k, E, block_m)
-    if cap < 0:
-        check(lib().moe_align(None, T, k, E, block_m, None, None, None, None, None, None))
-    g = Grouping(torch.empty(cap, dtype=torch.int32, device=dev),
-                 torch.empty(cap // block_m, dtype=torch.int32, device=dev),
-                 torch.empty(E, dtype=torch.int32, device=dev),
-                 torch.empty(E + 1, dtype=torch.int32, device=dev),
-                 torch.empty(1, dtype=torch.int32, device=dev), T, k, E, block_m)
-    if ticket is None:
-        ticket = torch.zeros(1, dtype=torch.int32, device=dev)
-    check(lib().moe_route_align(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, q, _ptr(ids),
-                                _ptr(w), _ptr(xq), _ptr(xs), block_m, _ptr(g.sorted_slot),
-                                _ptr(g.tile_expert), _ptr(g.count), _ptr(g.offset),
-                                _ptr(g.total), _ptr(ticket), _stream()))
-    return ids, w, xq, xs, g
-
-
 @dataclass
 class Weights:
     """Preshuffled expert weights (output of preshuffle())."""
@@ -212,13 +182,6 @@ def stage2_workspace_bytes(dtype, T, k, E, H, I, block_m) -> int:
     return int(lib().moe_stage2_workspace_bytes(_dt(dtype), T, k, E, H, I, block_m))
 
 
-def stage2_workspace(dtype, T, k, E, H, I, block_m, device) -> torch.Tensor:
-    """A zero-filled stage-2 workspace (its integer tickets must start at zero; every call
-    leaves them zero, so it is reused as is)."""
-    n = stage2_workspace_bytes(dtype, T, k, E, H, I, block_m)
-    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
-
-
 def stage2(dtype, act, act_amax, pw: Weights, grp: Grouping, topk_w, out=None, workspace=None):
     """-> out, bf16 bits as int16 [T, H]."""
     dt = _dt(dtype)
@@ -227,8 +190,9 @@ def stage2(dtype, act, act_amax, pw: Weights, grp: Grouping, topk_w, out=None, w
     dev = act.device
     if out is None:
         out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    nws = stage2_workspace_bytes(dt, T, k, E, H, I, bm)
     if workspace is None:
-        workspace = stage2_workspace(dt, T, k, E, H, I, bm, dev)
+        workspace = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
     check(lib().moe_stage2(dt, _ptr(act), _ptr(act_amax), _ptr(pw.w2), _ptr(pw.s2),
                            _ptr(grp.sorted_slot), _ptr(grp.tile_expert), _ptr(grp.total),
                            _ptr(topk_w), T, k, E, H, I, bm, _ptr(out), _ptr(workspace),
@@ -236,12 +200,48 @@ def stage2(dtype, act, act_amax, pw: Weights, grp: Grouping, topk_w, out=None, w
     return out
 
 
+def preshuffle_backward(w1, w3, w2):
+    """Transposed bf16 weights in the fragment order the backward GEMMs read (load time).
+    -> (w2t, w13t) uint8 device tensors."""
+    E, I, H = w1.shape
+    L = lib()
+    w2t = torch.empty(L.moe_backward_preshuffle_bytes(E, H, I, 0), dtype=torch.uint8,
+                      device=w1.device)
+    w13t = torch.empty(L.moe_backward_preshuffle_bytes(E, H, I, 1), dtype=torch.uint8,
+                       device=w1.device)
+    check(L.moe_backward_preshuffle(E, H, I, _ptr(w1), _ptr(w3), _ptr(w2), _ptr(w2t), _ptr(w13t),
+                                    _stream()))
+    return w2t, w13t
+
+
+def backward(x, w_router, ids, w, grp: Grouping, act, pw: Weights, w2t, w13t, dout,
+             want_dbias=True):
+    """Gradients of sum <dout, out> of the bf16 layer (moe_backward), from the forward's
+    tokens x, router weights, routing (ids, w), grouping, stage-1 output act and
+    preshuffled weights. -> dict(dx, dw1, dw3, dw2, dw_router, dbias), fp32 device tensors."""
+    T, H = x.shape
+    E, I, k, bm = pw.E, pw.I, grp.k, grp.block_m
+    dev = x.device
+    f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    g = dict(dx=f(T, H), dw1=f(E, I, H), dw3=f(E, I, H), dw2=f(E, H, I), dw_router=f(E, H),
+             dbias=f(E) if want_dbias else None)
+    L = lib()
+    n = int(L.moe_backward_workspace_bytes(T, k, E, H, I, bm))
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    check(L.moe_backward(_ptr(x), _ptr(w_router), _ptr(ids), _ptr(w), _ptr(grp.sorted_slot),
+                         _ptr(grp.tile_expert), _ptr(grp.offset), _ptr(grp.total), _ptr(act),
+                         _ptr(pw.w13), _ptr(w2t), _ptr(w13t), _ptr(dout), T, k, E, H, I, bm,
+                         _ptr(g["dx"]), _ptr(g["dw1"]), _ptr(g["dw3"]), _ptr(g["dw2"]),
+                         _ptr(g["dw_router"]), _ptr(g["dbias"]), _ptr(ws), ws.numel(),
+                         _stream()))
+    return g
+
+
 class Layer:
     """The whole routed MoE layer with buffers allocated once for a fixed batch size.
 
-    Weights are preshuffled at construction (load time). __call__ runs route + align (one
-    launch at decode sizes), stage 1 and stage 2 (requantisation and combine inside its
-    launch) on the current stream with no host synchronisation."""
+    Weights are preshuffled at construction (load time). __call__ runs route, align,
+    stage 1 and stage 2 on the current stream with no host synchronisation."""
 
     def __init__(self, dtype, w_router, w1, w3, w2, s1=None, s3=None, s2=None, bias=None,
                  k=2, T=None, block_m=None):
@@ -278,8 +278,8 @@ class Layer:
         self.act = torch.empty((cap, I), dtype=torch.int16, device=dev)
         n = int(L.moe_stage1_amax_floats(self.dt, T, k, E, H, I, self.bm)) if self.fp8 else 0
         self.amax = torch.empty(max(n, 1), dtype=torch.float32, device=dev) if self.fp8 else None
-        self.ws = stage2_workspace(self.dt, T, k, E, H, I, self.bm, dev)
-        self.ticket = torch.zeros(1, dtype=torch.int32, device=dev)
+        nws = stage2_workspace_bytes(self.dt, T, k, E, H, I, self.bm)
+        self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
         self.out = torch.empty((T, H), dtype=torch.int16, device=dev)
 
     def __call__(self, x: torch.Tensor, events=None) -> torch.Tensor:
@@ -290,11 +290,11 @@ class Layer:
             self._alloc(T)
         L, st = lib(), _stream()
         E, H, I, k, bm, g = self.E, self.H, self.I, self.k, self.bm, self.grp
-        quant = 2 if self.mx else 1 if self.fp8 else 0
-        check(L.moe_route_align(_ptr(x), _ptr(self.w_router), _ptr(self.bias), T, H, E, k, quant,
-                                _ptr(self.ids), _ptr(self.w), _ptr(self.xq), _ptr(self.xs), bm,
-                                _ptr(g.sorted_slot), _ptr(g.tile_expert), _ptr(g.count),
-                                _ptr(g.offset), _ptr(g.total), _ptr(self.ticket), st))
+        route_fn = L.moe_route_mx if self.mx else L.moe_route
+        check(route_fn(_ptr(x), _ptr(self.w_router), _ptr(self.bias), T, H, E, k,
+                       _ptr(self.ids), _ptr(self.w), None, _ptr(self.xq), _ptr(self.xs), st))
+        check(L.moe_align(_ptr(self.ids), T, k, E, bm, _ptr(g.sorted_slot), _ptr(g.tile_expert),
+                          _ptr(g.count), _ptr(g.offset), _ptr(g.total), st))
         xin = x if self.dt == BF16 else self.xq
         if events is not None:
             events[0].record()

@@ -18,8 +18,6 @@ SIGNATURES = {
     "moe_version": (ctypes.c_char_p, []),
     "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_route_mx": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
-    "moe_route_align": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P,
-                             _P, _P, _P]),
     "moe_align_capacity": (_I64, [_I, _I, _I, _I]),
     "moe_align": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_preshuffle_bytes": (_I64, [_I, _I, _I, _I, _I]),
@@ -29,6 +27,11 @@ SIGNATURES = {
     "moe_stage2_workspace_bytes": (_I64, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_stage2": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                         _SZ, _P]),
+    "moe_backward_preshuffle_bytes": (_I64, [_I, _I, _I, _I]),
+    "moe_backward_preshuffle": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_backward_workspace_bytes": (_I64, [_I, _I, _I, _I, _I, _I]),
+    "moe_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                          _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 

@@ -3,12 +3,10 @@
 // talk summary, 5:56). Integer work only: bit-exact by construction. Three
 // kernels by size, each one workgroup:
 //  - align_small_kernel (S <= 128 slots, decode): one wave, ids in registers,
-//    counts and ranks from ballots, offsets from a shuffle scan
-//    (align_device.h);
+//    counts and ranks from ballots, offsets from a shuffle scan;
 //  - align_runs_kernel (S <= 32768, E <= 16): each thread takes a contiguous
 //    run of slots and counts it in packed 16-bit counters; one exclusive scan
-//    of those over the 1024 threads gives every slot its stable rank
-//    (align_device.h);
+//    of those over the 1024 threads gives every slot its stable rank;
 //  - align_kernel (the rest): 1024 threads, slot c*1024 + t of each 1024-slot
 //    chunk c on thread t. Pass 1 counts slots per expert with wave ballots (one
 //    LDS integer atomic per wave and expert). Pass 2 walks the chunks in
@@ -16,7 +14,8 @@
 //    wave ballot (lanes are in ascending slot order) plus the counts of the
 //    lower waves, which one lane per (expert, wave) pair obtains with a 16-lane
 //    shuffle scan; so the result is exactly the stable order.
-#include "align_device.h"
+#include "moe_device.h"
+#include "moe_launch.h"
 
 namespace moe {
 
@@ -144,20 +143,225 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a) {
   }
 }
 
-// Small groupings: one wave (align_small).
+// Small groupings (S <= kSmallSlots, decode batches): the same counting sort
+// on one wave, in registers. Lane l holds slot 64*i + l of each 64-slot chunk
+// i; lane e (< E) keeps expert e's count, offset and running base. No LDS and
+// no barriers: the cost is a few ballots per chunk and expert, so it grows
+// with the chunks (measured: 5.1 us at 32 slots, 6.1 at 128, 8.2 at 256, 36 at
+// 2048), while align_runs_kernel takes 6.3-6.8 us from 512 to 2048 slots.
+constexpr int kSmallSlots = 128;
+constexpr int kSmallChunks = kSmallSlots / 64;
+
 __global__ __launch_bounds__(64) void align_small_kernel(AlignArgs a) {
-  align_small(a, threadIdx.x);
+  const int lane = threadIdx.x;
+  const int S = a.S, E = a.E, bm = a.bm;
+  const int nchunks = (S + 63) / 64;
+  int idv[kSmallChunks];
+#pragma unroll
+  for (int i = 0; i < kSmallChunks; ++i) {
+    const int s = i * 64 + lane;  // clamped load, then select: no branches
+    const int v = a.ids[min(s, S - 1)];
+    idv[i] = s < S ? v : -1;
+  }
+  // Counts (lane e: expert e), and a check of every id.
+  int cnt = 0;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < kSmallChunks; ++i) {
+    if (i >= nchunks) break;
+    const int e = idv[i];
+    bad |= i * 64 + lane < S && (e < 0 || e >= E);
+    for (int ee = 0; ee < E; ++ee) {
+      const int c = __popcll(__ballot(e == ee));
+      if (lane == ee) cnt += c;
+    }
+  }
+  if (__ballot(bad)) {  // invalid ids: an empty grouping, nothing downstream runs
+    if (lane == 0) *a.total = 0;
+    return;
+  }
+  // Padded offsets: exclusive scan of the padded counts over lanes 0..E-1.
+  const int padded = lane < E ? (cnt + bm - 1) / bm * bm : 0;
+  int incl = padded;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  const int off = incl - padded;
+  const int total = __shfl(incl, 63, 64);
+  if (lane < E) {
+    a.count[lane] = cnt;
+    a.offset[lane] = off;
+  }
+  if (lane == 0) {
+    a.offset[E] = total;
+    *a.total = total;
+  }
+  // Tile experts and pad sentinels (fewer than block_m pad rows per expert).
+  for (int e = 0; e < E; ++e) {
+    const int o0 = __shfl(off, e, 64), o1 = __shfl(incl, e, 64);
+    const int c = __shfl(cnt, e, 64);
+    for (int i = o0 / bm + lane; i < o1 / bm; i += 64) a.tile_expert[i] = e;
+    for (int p = o0 + c + lane; p < o1; p += 64) a.sorted_slot[p] = S;
+  }
+  // Stable scatter, chunk by chunk: a slot's row is its expert's running base
+  // plus the number of lower lanes of the chunk with the same expert.
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int base = off;  // lane e: next row of expert e
+#pragma unroll
+  for (int i = 0; i < kSmallChunks; ++i) {
+    if (i >= nchunks) break;
+    const int e = idv[i];
+    const int b = __shfl(base, e < 0 ? 0 : e, 64);  // the expert's base before this chunk
+    int rank = 0;
+    for (int ee = 0; ee < E; ++ee) {
+      const unsigned long long m = __ballot(e == ee);
+      if (e == ee) rank = __popcll(m & lt);
+      if (lane == ee) base += __popcll(m);
+    }
+    if (e >= 0) a.sorted_slot[b + rank] = i * 64 + lane;
+  }
 }
 
-// Prefill-size groupings with few experts: runs of up to 32 slots on 1024
-// threads (align_runs).
-constexpr int kRunSlots = 32;
+// Prefill-size groupings with few experts (S <= kRunSlots * 1024, E <= 16):
+// thread t owns a contiguous run of slots, so one block-wide scan replaces the
+// per-chunk ballots. The ids go through LDS as bytes (coalesced loads, then
+// each thread copies its run into registers); a thread counts its run in
+// packed 16-bit counters (expert e in half e%2 of word e/2: counts stay below
+// 2^16 since S <= 32768); an exclusive scan of those words over the threads
+// gives every thread, for every expert, the number of earlier slots; its
+// slots then go to offset[e] + that number + the rank inside its run, in
+// ascending order, which is the stable order. The grouping is assembled in
+// LDS (over the ids, which are in registers by then) and written out in
+// order: one workgroup's scattered 4-byte global stores touched a cache line
+// each and were the kernel's largest cost.
+constexpr int kRunSlots = 32;                     // slots per thread at most
 constexpr int kRunMaxSlots = kRunSlots * kAlignThreads;
+constexpr int kRunWords = 8;                      // packed counter words at most (E <= 16)
+constexpr int kRunMaxRows = kRunMaxSlots + 16 * 255;  // capacity at E <= 16, block_m <= 256
 
+// W packed counter words: experts 0 .. 2W-1 (4 words for E <= 8, else 8).
 template <int W>
 __global__ __launch_bounds__(kAlignThreads) void align_runs_kernel(AlignArgs a) {
-  __shared__ __align__(16) AlignRunsLds<kAlignThreads, kRunSlots> lds;
-  align_runs<W, kAlignThreads, kRunSlots>(a, lds);
+  // ids as bytes first, then the grouped rows (capacity ints) in the same space
+  __shared__ __align__(16) int rows[kRunMaxRows];
+  uint8_t* const ids8 = reinterpret_cast<uint8_t*>(rows);
+  __shared__ uint32_t wtot[kAlignWaves][W];  // per-wave totals, then wave prefixes
+  __shared__ int cnt[2 * W];
+  __shared__ int off[2 * W + 1];
+  __shared__ int bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.S, E = a.E, bm = a.bm;
+  const int nchunks = (S + kAlignThreads - 1) / kAlignThreads;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  {
+    bool anybad = false;
+#pragma unroll
+    for (int i = 0; i < kRunSlots; ++i) {
+      if (i >= nchunks) break;                // uniform: the chunks present
+      const int s = i * kAlignThreads + tid;  // clamped load, then select
+      const int v = a.ids[min(s, S - 1)];
+      if (s < S) {
+        anybad |= v < 0 || v >= E;
+        ids8[s] = (uint8_t)v;
+      }
+    }
+    if (anybad) bad = 1;
+  }
+  __syncthreads();
+  if (bad) {  // invalid ids: an empty grouping, nothing downstream runs
+    if (tid == 0) *a.total = 0;
+    return;
+  }
+  // This thread's run: slots [r0, r0 + n4) clipped to S, n4 a multiple of 4,
+  // copied into registers four ids per word (slots past S read as 0, unused).
+  const int n4 = ((nchunks + 3) / 4) * 4;
+  const int r0 = tid * n4;
+  uint32_t idw[kRunSlots / 4];
+#pragma unroll
+  for (int q = 0; q < kRunSlots / 4; ++q)
+    idw[q] = 4 * q < n4 ? *reinterpret_cast<const uint32_t*>(ids8 + r0 + 4 * q) : 0u;
+  auto run_id = [&](int i) { return (int)((idw[i / 4] >> (8 * (i % 4))) & 0xffu); };
+  uint32_t cntw[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) cntw[w] = 0;
+#pragma unroll
+  for (int i = 0; i < kRunSlots; ++i) {
+    if (i >= n4 || r0 + i >= S) break;
+    const int e = run_id(i);
+    const uint32_t inc = (e & 1) ? 0x10000u : 1u;
+#pragma unroll
+    for (int w = 0; w < W; ++w) cntw[w] += (e >> 1) == w ? inc : 0u;
+  }
+  // Exclusive scan of the packed words over the threads (thread order = slot
+  // order): inside each wave with shuffles, then over the 16 wave totals.
+  uint32_t excl[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    uint32_t x = cntw[w];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(x, d, 64);
+      if (lane >= d) x += o;
+    }
+    excl[w] = x - cntw[w];
+    if (lane == 63) wtot[wave][w] = x;
+  }
+  __syncthreads();  // also: every run is in registers, so the id bytes may be overwritten
+  if (tid < W) {  // wave prefixes in place, and the expert counts from the grand total
+    uint32_t acc = 0;
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const uint32_t t = wtot[w][tid];
+      wtot[w][tid] = acc;
+      acc += t;
+    }
+    cnt[2 * tid] = (int)(acc & 0xffffu);
+    cnt[2 * tid + 1] = (int)(acc >> 16);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < W; ++w) excl[w] += wtot[wave][w];
+  if (tid == 0) {  // padded offsets
+    int pos = 0;
+    for (int e = 0; e < E; ++e) {
+      off[e] = pos;
+      pos += (cnt[e] + bm - 1) / bm * bm;
+    }
+    off[E] = pos;
+    *a.total = pos;
+  }
+  __syncthreads();
+  if (tid < E) a.count[tid] = cnt[tid];
+  if (tid <= E) a.offset[tid] = off[tid];
+  // Tile experts (global) and pad sentinels (fewer than block_m pad rows per
+  // expert, in LDS).
+  for (int e = 0; e < E; ++e) {
+    const int o0 = off[e], o1 = off[e + 1];
+    for (int i = o0 / bm + tid; i < o1 / bm; i += kAlignThreads) a.tile_expert[i] = e;
+    const int p = o0 + cnt[e] + tid;
+    if (p < o1) rows[p] = S;
+  }
+  // Stable scatter of this thread's run into LDS.
+#pragma unroll
+  for (int i = 0; i < kRunSlots; ++i) {
+    const int sl = r0 + i;
+    if (i >= n4 || sl >= S) break;
+    const int e = run_id(i);
+    uint32_t word = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) word = (e >> 1) == w ? excl[w] : word;
+    const int rank = (int)((e & 1) ? (word >> 16) : (word & 0xffffu));
+    rows[off[e] + rank] = sl;
+    const uint32_t inc = (e & 1) ? 0x10000u : 1u;
+#pragma unroll
+    for (int w = 0; w < W; ++w) excl[w] += (e >> 1) == w ? inc : 0u;
+  }
+  __syncthreads();
+  // The grouping in order: consecutive threads write consecutive rows.
+  const int total = off[E];
+  for (int p = tid; p < total; p += kAlignThreads) a.sorted_slot[p] = rows[p];
 }
 
 hipError_t launch_align(const AlignArgs& a, hipStream_t st) {
@@ -165,8 +369,8 @@ hipError_t launch_align(const AlignArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(64), 0, st, a);
   else if (a.S <= kRunMaxSlots && a.E <= 8)
     hipLaunchKernelGGL(align_runs_kernel<4>, dim3(1), dim3(kAlignThreads), 0, st, a);
-  else if (a.S <= kRunMaxSlots && a.E <= 16)
-    hipLaunchKernelGGL(align_runs_kernel<8>, dim3(1), dim3(kAlignThreads), 0, st, a);
+  else if (a.S <= kRunMaxSlots && a.E <= 2 * kRunWords)
+    hipLaunchKernelGGL(align_runs_kernel<kRunWords>, dim3(1), dim3(kAlignThreads), 0, st, a);
   else
     hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, st, a);
   return hipGetLastError();

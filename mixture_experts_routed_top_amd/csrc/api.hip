@@ -73,119 +73,15 @@ moe_status check_stage(int dt, int T, int k, int E, int H, int I, int bm) {
         "MXFP8/MXFP4 need H <= %d and I <= %d (H=%d I=%d)", moe::kMxMaxH, moe::kMxMaxI, H, I);
   CHECK((int64_t)T * k <= (1 << 30) && capacity(T, k, E, bm) <= (1 << 30), MOE_ERR_UNSUPPORTED,
         "T*k too large");
-  // Activation rows are addressed with 32-bit buffer offsets below 2 GiB (the
-  // bf16 intermediate [capacity][I] is what stage 2 loads, FP8 included).
+  // Activation rows are addressed with 32-bit buffer offsets below 2 GiB.
   const int64_t es = dt == MOE_BF16 ? 2 : 1;
   CHECK((int64_t)T * H * es < ((int64_t)1 << 31) &&
-            capacity(T, k, E, bm) * I * 2 < ((int64_t)1 << 31),
+            capacity(T, k, E, bm) * I * es < ((int64_t)1 << 31),
         MOE_ERR_UNSUPPORTED, "activations beyond 2 GiB (T=%d)", T);
   CHECK(moe::gemm_cfg_ok(dt, 1, moe::stage1_cfg(dt, T, k, E, H, I, bm), 2 * I, H) &&
             moe::gemm_cfg_ok(dt, 2, moe::stage2_cfg(dt, T, k, E, H, I, bm), H, I),
         MOE_ERR_UNSUPPORTED, "no kernel configuration for H=%d I=%d block_m=%d", H, I, bm);
   return ok();
-}
-
-
-// Stage-2 workspace: byte offsets of its parts (each 256-byte aligned).
-//   part          fp32 [kg][T*k][H]  weighted per-slot partials (kg reduction splits)
-//   act_q, act_mx MXFP8/MXFP4: the block-quantised intermediate [cap][I] and its
-//                 E8M0 codes [cap][I/32]
-//   tail          fp32 [kTailPieces][32*mt][wg_n]  partials of the tail pieces
-//   tickets       int32 [T][H/wg_n] per (token, feature tile), then [kTailPieces]
-//                 per tail tile: zero before the first call, left zero by every call
-struct Stage2Layout {
-  moe::GemmCfg c;
-  int64_t part, act_q, act_mx, tail, tickets, tile_tickets, bytes;
-};
-
-Stage2Layout stage2_layout(int dt, int T, int k, int E, int H, int I, int bm) {
-  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
-  Stage2Layout L{};
-  L.c = moe::stage2_cfg(dt, T, k, E, H, I, bm);
-  const int64_t cap = capacity(T, k, E, bm);
-  int64_t o = 0;
-  L.part = o;
-  o += up((int64_t)L.c.kg * T * k * H * 4);
-  L.act_q = L.act_mx = -1;
-  if (is_mx(dt)) {
-    L.act_q = o;
-    o += up(cap * I);
-    L.act_mx = o;
-    o += up(cap * (I / 32));
-  }
-  L.tail = -1;
-  if (L.c.tail_split > 0) {
-    L.tail = o;
-    o += up((int64_t)moe::kTailPieces * 32 * L.c.mt * L.c.wg_n * 4);
-  }
-  L.tickets = o;
-  o += (int64_t)T * (H / L.c.wg_n) * 4;
-  L.tile_tickets = o;
-  o += up((int64_t)moe::kTailPieces * 4);
-  L.bytes = up(o);
-  return L;
-}
-
-// The stage-2 launches (arguments already checked): MXFP8/MXFP4 block
-// requantisation, then the GEMM with the fused FP8 requantisation and combine.
-moe_status stage2_launch(int dt, const void* act, const float* act_amax, const void* w2,
-                         const void* s2, const int32_t* sorted_slot, const int32_t* tile_expert,
-                         const int32_t* total_padded, const float* topk_w, int T, int k, int E,
-                         int H, int I, int bm, void* out, char* ws, const Stage2Layout& L,
-                         hipStream_t stream) {
-  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = is_mx(dt);
-  const int64_t cap = capacity(T, k, E, bm);
-  const moe::GemmCfg& c = L.c;
-  const void* x = act;
-  moe::GemmArgs a{};
-  hipError_t err;
-  if (mx) {
-    uint8_t* act_q = (uint8_t*)(ws + L.act_q);
-    uint8_t* act_mx = (uint8_t*)(ws + L.act_mx);
-    moe::QuantMxArgs q{(const uint16_t*)act, (int)cap, I, total_padded, act_q, act_mx};
-    err = moe::launch_quant_act_mx(q, stream);
-    if (err != hipSuccess) return hip_status(err, "moe_stage2 block requantisation");
-    x = act_q;
-    a.x_mx = act_mx;
-    a.w_mx = (const uint8_t*)s2;
-  } else {
-    a.w_scale = (const float*)s2;
-  }
-  if (fp8) {
-    const moe::GemmCfg c1 = moe::stage1_cfg(dt, T, k, E, H, I, bm);
-    a.amax_part = const_cast<float*>(act_amax);
-    a.nparts = 2 * I / c1.wg_n;
-  }
-  a.X = (const uint8_t*)x;
-  a.W = (const uint8_t*)w2;
-  a.sorted_slot = sorted_slot;
-  a.tile_expert = tile_expert;
-  a.total_padded = total_padded;
-  a.topk_w = topk_w;
-  a.out = ws + L.part;
-  a.T = T;
-  a.k = k;
-  a.N = H;
-  a.I = I;
-  a.cap = (int)cap;
-  a.bm = bm;
-  a.K_bytes = I * (dt == MOE_BF16 ? 2 : 1);
-  a.x_bytes = cap * I * (dt == MOE_BF16 || fp8 ? 2 : 1);  // the rows the GEMM loads
-  a.n_mtiles = (int)(cap / (32 * c.mt));
-  a.n_ntiles = H / c.wg_n;
-  a.kg = c.kg;
-  a.group_m = group_m(c.mt);
-  a.k_magic = k_magic(k);
-  a.tail_split = c.tail_split;
-  a.live_order = c.mt * c.nf < 16;
-  if (c.tail_split > 0) {
-    a.tail_part = (float*)(ws + L.tail);
-    a.round = c.round;
-  }
-  a.y = (uint16_t*)out;
-  a.tickets = (int32_t*)(ws + L.tickets);
-  a.tile_tickets = (int32_t*)(ws + L.tile_tickets);
-  return hip_status(moe::launch_gemm(dt, 2, c, a, stream), "moe_stage2 GEMM launch");
 }
 
 }  // namespace
@@ -245,45 +141,6 @@ moe_status moe_route_mx(const void* x, const void* w_router, const float* bias, 
   moe::RouteArgs a{(const uint16_t*)x, (const uint16_t*)w_router, bias, T, H, E, k, topk_ids,
                    topk_w, logits, (uint8_t*)x_q, nullptr, (uint8_t*)x_scale_e8m0};
   return hip_status(moe::launch_route(a, stream), "moe_route_mx launch");
-}
-
-moe_status moe_route_align(const void* x, const void* w_router, const float* bias, int T, int H,
-                           int E, int k, int quant, int32_t* topk_ids, float* topk_w, void* x_q,
-                           void* x_scale, int block_m, int32_t* sorted_slot,
-                           int32_t* tile_expert, int32_t* expert_count, int32_t* expert_offset,
-                           int32_t* total_padded, int32_t* ticket, hipStream_t stream) {
-  CHECK(T >= 0 && H > 0, MOE_ERR_INVALID_ARG, "sizes T=%d H=%d", T, H);
-  CHECK(E >= 1 && k >= 1, MOE_ERR_INVALID_ARG, "E=%d k=%d", E, k);
-  CHECK(quant >= 0 && quant <= 2, MOE_ERR_INVALID_ARG, "quant=%d (0, 1 or 2)", quant);
-  CHECK(E <= 64 && k <= E && k <= 8, MOE_ERR_UNSUPPORTED, "E=%d k=%d (need E<=64, k<=min(E,8))",
-        E, k);
-  CHECK(H % 128 == 0 && H <= 8192, MOE_ERR_UNSUPPORTED,
-        "H=%d must be a multiple of 128, at most 8192", H);
-  CHECK(valid_bm(block_m), MOE_ERR_UNSUPPORTED, "block_m=%d (need 32, 64, 128 or 256)", block_m);
-  CHECK((int64_t)T * k <= (1 << 30), MOE_ERR_UNSUPPORTED, "T*k too large");
-  if (T == 0) return ok();
-  CHECK(x && w_router && topk_ids && topk_w && sorted_slot && tile_expert && expert_count &&
-            expert_offset && total_padded && ticket,
-        MOE_ERR_INVALID_ARG, "null pointer argument");
-  CHECK(quant == 0 || (x_q && x_scale), MOE_ERR_INVALID_ARG, "quant=%d needs x_q and x_scale",
-        quant);
-  CHECK(aligned(x, 16) && aligned(w_router, 16) && aligned(x_q, 8) &&
-            aligned(x_scale, quant == 2 ? 8 : 4) && aligned(ticket, 4),
-        MOE_ERR_INVALID_ARG,
-        "x and w_router 16-byte, x_q 8-byte, x_scale 4-byte (quant 2: 8-byte) alignment");
-  moe::RouteArgs a{(const uint16_t*)x, (const uint16_t*)w_router, bias, T, H, E, k, topk_ids,
-                   topk_w, nullptr, quant ? (uint8_t*)x_q : nullptr,
-                   quant == 1 ? (float*)x_scale : nullptr,
-                   quant == 2 ? (uint8_t*)x_scale : nullptr};
-  a.al = moe::AlignArgs{topk_ids, T * k, E, block_m, sorted_slot, tile_expert,
-                        expert_count, expert_offset, total_padded};
-  if (T < 1024 && T * k <= moe::kFusedAlignSlots && E <= 16) {
-    a.ticket = ticket;  // one launch: the last router workgroup groups the slots
-    return hip_status(moe::launch_route(a, stream), "moe_route_align launch");
-  }
-  hipError_t err = moe::launch_route(a, stream);
-  if (err != hipSuccess) return hip_status(err, "moe_route_align route launch");
-  return hip_status(moe::launch_align(a.al, stream), "moe_route_align align launch");
 }
 
 int64_t moe_align_capacity(int T, int k, int E, int block_m) {
@@ -435,7 +292,20 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, co
 
 int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int I, int block_m) {
   if (check_stage(dt, T, k, E, H, I, block_m) != MOE_OK) return -1;
-  return stage2_layout(dt, T, k, E, H, I, block_m).bytes;
+  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  const moe::GemmCfg c = moe::stage2_cfg(dt, T, k, E, H, I, block_m);
+  int64_t bytes = up((int64_t)c.kg * T * k * H * 4);  // weighted per-slot partials per split
+  if (dt == MOE_FP8_E4M3FN) {
+    const int64_t cap = capacity(T, k, E, block_m);
+    bytes += up(cap * I) + up(cap * 4);  // requantised intermediate + row scales
+  }
+  if (is_mx(dt)) {
+    const int64_t cap = capacity(T, k, E, block_m);
+    bytes += up(cap * I) + up(cap * (I / 32));  // requantised intermediate + block codes
+  }
+  if (c.tail_split > 0)  // partials of the tail pieces
+    bytes += up((int64_t)moe::kTailPieces * 32 * c.mt * c.wg_n * 4);
+  return bytes;
 }
 
 moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, const void* w2,
@@ -452,14 +322,300 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
   CHECK(!fp8 || (act_amax && s2), MOE_ERR_INVALID_ARG, "FP8 needs act_amax and s2");
   CHECK(!mx || s2, MOE_ERR_INVALID_ARG, "MXFP8/MXFP4 need s2");
   CHECK(aligned(act, 16) && aligned(w2, 16) && aligned(out, 8) && aligned(workspace, 256) &&
-            aligned(s2, mx ? 4 : 16) && aligned(act_amax, 16),
-        MOE_ERR_INVALID_ARG,
-        "act/w2/s2/act_amax 16-byte, out 8-byte, workspace 256-byte alignment");
-  const Stage2Layout L = stage2_layout(dt, T, k, E, H, I, block_m);
+            aligned(s2, mx ? 4 : 16),
+        MOE_ERR_INVALID_ARG, "act/w2/s2 16-byte, out 8-byte, workspace 256-byte alignment");
+  const int64_t need = moe_stage2_workspace_bytes(dt, T, k, E, H, I, block_m);
+  CHECK((int64_t)workspace_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu bytes < %lld needed",
+        workspace_bytes, (long long)need);
+
+  const int64_t cap = capacity(T, k, E, block_m);
+  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  moe::GemmCfg c = moe::stage2_cfg(dt, T, k, E, H, I, block_m);
+  char* ws = (char*)workspace;
+  float* part = (float*)ws;
+  ws += up((int64_t)c.kg * T * k * H * 4);
+  const void* x = act;
+  const float* xs = nullptr;
+  const uint8_t* xmx = nullptr;
+  hipError_t err;
+  if (fp8) {
+    uint8_t* act_q = (uint8_t*)ws;
+    float* act_scale = (float*)(ws + up(cap * I));
+    moe::GemmCfg c1 = moe::stage1_cfg(dt, T, k, E, H, I, block_m);
+    moe::QuantArgs q{(const uint16_t*)act, act_amax, 2 * I / c1.wg_n, (int)cap, I, total_padded,
+                     act_q, act_scale};
+    err = moe::launch_quant_act(q, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_stage2 requantisation");
+    x = act_q;
+    xs = act_scale;
+    ws += up(cap * I) + up(cap * 4);
+  }
+  if (mx) {
+    uint8_t* act_q = (uint8_t*)ws;
+    uint8_t* act_mx = (uint8_t*)(ws + up(cap * I));
+    moe::QuantMxArgs q{(const uint16_t*)act, (int)cap, I, total_padded, act_q, act_mx};
+    err = moe::launch_quant_act_mx(q, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_stage2 block requantisation");
+    x = act_q;
+    xmx = act_mx;
+    ws += up(cap * I) + up(cap * (I / 32));
+  }
+  moe::GemmArgs a{};
+  a.X = (const uint8_t*)x;
+  a.x_scale = xs;
+  a.W = (const uint8_t*)w2;
+  if (mx) {
+    a.x_mx = xmx;
+    a.w_mx = (const uint8_t*)s2;
+  } else {
+    a.w_scale = (const float*)s2;
+  }
+  a.sorted_slot = sorted_slot;
+  a.tile_expert = tile_expert;
+  a.total_padded = total_padded;
+  a.topk_w = topk_w;
+  a.out = part;
+  a.T = T;
+  a.k = k;
+  a.N = H;
+  a.I = I;
+  a.cap = (int)cap;
+  a.bm = block_m;
+  a.K_bytes = I * (dt == MOE_BF16 ? 2 : 1);
+  a.x_bytes = cap * a.K_bytes;
+  a.n_mtiles = (int)(cap / (32 * c.mt));
+  a.n_ntiles = H / c.wg_n;
+  a.kg = c.kg;
+  a.group_m = group_m(c.mt);
+  a.k_magic = k_magic(k);
+  a.tail_split = c.tail_split;
+  a.live_order = c.mt * c.nf < 16;
+  if (c.tail_split > 0) {
+    a.tail_part = (float*)ws;
+    a.round = c.round;
+  }
+  err = moe::launch_gemm(dt, 2, c, a, stream);
+  if (err != hipSuccess) return hip_status(err, "moe_stage2 GEMM launch");
+  if (c.tail_split > 0) {
+    moe::TailReduceArgs tr{a.tail_part, sorted_slot, total_padded, part, T * k, H, 32 * c.mt,
+                           c.wg_n, a.n_ntiles, a.group_m, a.round, c.tail_split,
+                           a.K_bytes / c.ck};
+    err = moe::launch_tail_reduce(tr, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_stage2 tail reduction launch");
+  }
+  moe::CombineArgs cb{part, total_padded, T, k, H, c.kg, (uint16_t*)out};
+  return hip_status(moe::launch_combine(cb, stream), "moe_stage2 combine launch");
+}
+
+// --- backward pass (bf16) ---------------------------------------------------
+
+int64_t moe_backward_preshuffle_bytes(int E, int H, int I, int which) {
+  if (E < 1 || H < 1 || I < 1 || (which != 0 && which != 1)) return -1;
+  return (int64_t)E * H * I * 2 * (which == 0 ? 1 : 2);
+}
+
+moe_status moe_backward_preshuffle(int E, int H, int I, const void* w1, const void* w3,
+                                   const void* w2, void* w2t_out, void* w13t_out,
+                                   hipStream_t stream) {
+  CHECK(E >= 1 && H > 0 && I > 0, MOE_ERR_INVALID_ARG, "sizes E=%d H=%d I=%d", E, H, I);
+  CHECK(H % 128 == 0 && I % 128 == 0, MOE_ERR_UNSUPPORTED, "H=%d I=%d must be multiples of 128",
+        H, I);
+  CHECK(w1 && w3 && w2 && w2t_out && w13t_out, MOE_ERR_INVALID_ARG, "null weight pointer");
+  CHECK(aligned(w1, 16) && aligned(w3, 16) && aligned(w2, 16) && aligned(w2t_out, 16) &&
+            aligned(w13t_out, 16),
+        MOE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  moe::PreshuffleTArgs a{(const uint16_t*)w1, (const uint16_t*)w3, (const uint16_t*)w2,
+                         (uint16_t*)w2t_out, E, H, I, 0};
+  hipError_t err = moe::launch_preshuffle_t(a, stream);
+  if (err != hipSuccess) return hip_status(err, "backward preshuffle W2^T");
+  a.dst = (uint16_t*)w13t_out;
+  a.mode = 1;
+  return hip_status(moe::launch_preshuffle_t(a, stream), "backward preshuffle W13^T");
+}
+
+namespace {
+
+// Backward workspace: gu and dgu bf16 [cap][2I]; dwpart fp32 [T*k][I/wg_n];
+// dl fp32 [T*k]; part fp32 [kg][T*k][H]; tail pieces (prefill sizes).
+struct BwdLayout {
+  moe::GemmCfg c1, cz, c3;  // recompute (stage 1), z (stage 1 over W2^T), dx (stage 2)
+  int64_t gu, dgu, dwpart, dl, part, tail, bytes;
+};
+
+BwdLayout bwd_layout(int T, int k, int E, int H, int I, int bm) {
+  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  BwdLayout L{};
+  L.c1 = moe::stage1_cfg(MOE_BF16, T, k, E, H, I, bm);
+  L.cz = moe::stage1_cfg(MOE_BF16, T, k, E, H, I / 2, bm);  // N = I output features
+  L.c3 = moe::stage2_cfg(MOE_BF16, T, k, E, H, 2 * I, bm);  // reduction over 2I
+  const int64_t cap = capacity(T, k, E, bm), S = (int64_t)T * k;
+  int64_t o = 0;
+  L.gu = o;
+  o += up(cap * 2 * I * 2);
+  L.dgu = o;
+  o += up(cap * 2 * I * 2);
+  L.dwpart = o;
+  o += up(S * (I / L.cz.wg_n) * 4);
+  L.dl = o;
+  o += up(S * 4);
+  L.part = o;
+  o += up((int64_t)L.c3.kg * S * H * 4);
+  L.tail = -1;
+  if (L.c3.tail_split > 0) {
+    L.tail = o;
+    o += up((int64_t)moe::kTailPieces * 32 * L.c3.mt * L.c3.wg_n * 4);
+  }
+  L.bytes = o;
+  return L;
+}
+
+moe_status check_backward(int T, int k, int E, int H, int I, int bm) {
+  moe_status s = check_stage(MOE_BF16, T, k, E, H, I, bm);
+  if (s != MOE_OK) return s;
+  const BwdLayout L = bwd_layout(T, k, E, H, I, bm);
+  CHECK(moe::gemm_cfg_ok(MOE_BF16, 1, L.cz, I, H) && moe::gemm_cfg_ok(MOE_BF16, 2, L.c3, H, 2 * I),
+        MOE_ERR_UNSUPPORTED, "no backward kernel configuration for H=%d I=%d block_m=%d", H, I,
+        bm);
+  CHECK(capacity(T, k, E, bm) * 4 * I < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
+        "backward intermediate beyond 2 GiB (T=%d)", T);
+  return ok();
+}
+
+}  // namespace
+
+int64_t moe_backward_workspace_bytes(int T, int k, int E, int H, int I, int block_m) {
+  if (check_backward(T, k, E, H, I, block_m) != MOE_OK) return -1;
+  return bwd_layout(T, k, E, H, I, block_m).bytes;
+}
+
+moe_status moe_backward(const void* x, const void* w_router, const int32_t* topk_ids,
+                        const float* topk_w, const int32_t* sorted_slot,
+                        const int32_t* tile_expert, const int32_t* expert_offset,
+                        const int32_t* total_padded, const void* act, const void* w13,
+                        const void* w2t, const void* w13t, const void* dout, int T, int k,
+                        int E, int H, int I, int block_m, float* dx, float* dw1, float* dw3,
+                        float* dw2, float* dw_router, float* dbias, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  moe_status s = check_backward(T, k, E, H, I, block_m);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  CHECK(x && w_router && topk_ids && topk_w && sorted_slot && tile_expert && expert_offset &&
+            total_padded && act && w13 && w2t && w13t && dout && dx && dw1 && dw3 && dw2 &&
+            dw_router && workspace,
+        MOE_ERR_INVALID_ARG, "null pointer argument");
+  CHECK(aligned(x, 16) && aligned(w_router, 16) && aligned(act, 16) && aligned(w13, 16) &&
+            aligned(w2t, 16) && aligned(w13t, 16) && aligned(dout, 16) && aligned(dx, 16) &&
+            aligned(dw1, 16) && aligned(dw3, 16) && aligned(dw2, 16) && aligned(dw_router, 16) &&
+            aligned(workspace, 256),
+        MOE_ERR_INVALID_ARG, "16-byte alignment (workspace 256-byte)");
+  const BwdLayout L = bwd_layout(T, k, E, H, I, block_m);
   CHECK((int64_t)workspace_bytes >= L.bytes, MOE_ERR_WORKSPACE,
         "workspace %zu bytes < %lld needed", workspace_bytes, (long long)L.bytes);
-  return stage2_launch(dt, act, act_amax, w2, s2, sorted_slot, tile_expert, total_padded, topk_w,
-                       T, k, E, H, I, block_m, out, (char*)workspace, L, stream);
+  char* ws = (char*)workspace;
+  const int64_t cap = capacity(T, k, E, block_m);
+  const int S = T * k;
+  uint16_t* gu = (uint16_t*)(ws + L.gu);
+  uint16_t* dgu = (uint16_t*)(ws + L.dgu);
+  float* dwpart = (float*)(ws + L.dwpart);
+  float* part = (float*)(ws + L.part);
+  auto common = [&](moe::GemmArgs& a, const moe::GemmCfg& c) {
+    a.sorted_slot = sorted_slot;
+    a.tile_expert = tile_expert;
+    a.total_padded = total_padded;
+    a.topk_w = topk_w;
+    a.T = T;
+    a.k = k;
+    a.I = I;
+    a.cap = (int)cap;
+    a.bm = block_m;
+    a.n_mtiles = (int)(cap / (32 * c.mt));
+    a.group_m = group_m(c.mt);
+    a.k_magic = k_magic(k);
+    a.kg = c.kg;
+    a.live_order = c.mt * c.nf < 16;
+  };
+  // 1. g, u recomputed from x (the forward's stage 1, pre-activations out).
+  {
+    moe::GemmArgs a{};
+    common(a, L.c1);
+    a.X = (const uint8_t*)x;
+    a.W = (const uint8_t*)w13;
+    a.out = gu;
+    a.N = 2 * I;
+    a.K_bytes = 2 * H;
+    a.x_bytes = (int64_t)T * H * 2;
+    a.n_ntiles = 2 * I / L.c1.wg_n;
+    a.epi = 1;
+    hipError_t err = moe::launch_gemm(MOE_BF16, 1, L.c1, a, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_backward recompute launch");
+  }
+  // 2. z = W2^T dout per row; dg, du and the partial <z, act>.
+  {
+    moe::GemmArgs a{};
+    common(a, L.cz);
+    a.X = (const uint8_t*)dout;
+    a.W = (const uint8_t*)w2t;
+    a.out = dgu;
+    a.N = I;
+    a.K_bytes = 2 * H;
+    a.x_bytes = (int64_t)T * H * 2;
+    a.n_ntiles = I / L.cz.wg_n;
+    a.epi = 2;
+    a.act_in = (const uint16_t*)act;
+    a.gu = gu;
+    a.dwpart = dwpart;
+    hipError_t err = moe::launch_gemm(MOE_BF16, 1, L.cz, a, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_backward SwiGLU-gradient launch");
+  }
+  // 3. per slot W1^T dg + W3^T du (stage 2 over [W1^T | W3^T], weight 1).
+  {
+    const moe::GemmCfg& c = L.c3;
+    moe::GemmArgs a{};
+    common(a, c);
+    a.X = (const uint8_t*)dgu;
+    a.W = (const uint8_t*)w13t;
+    a.out = part;
+    a.N = H;
+    a.I = 2 * I;
+    a.K_bytes = 4 * I;
+    a.x_bytes = cap * 4 * I;
+    a.n_ntiles = H / c.wg_n;
+    a.tail_split = c.tail_split;
+    a.unit_w = 1;
+    if (c.tail_split > 0) {
+      a.tail_part = (float*)(ws + L.tail);
+      a.round = c.round;
+    }
+    hipError_t err = moe::launch_gemm(MOE_BF16, 2, c, a, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_backward input-gradient launch");
+    if (c.tail_split > 0) {
+      moe::TailReduceArgs tr{a.tail_part, sorted_slot, total_padded, part, S, H, 32 * c.mt,
+                             c.wg_n, a.n_ntiles, a.group_m, a.round, c.tail_split,
+                             a.K_bytes / c.ck};
+      err = moe::launch_tail_reduce(tr, stream);
+      if (err != hipSuccess) return hip_status(err, "moe_backward tail reduction launch");
+    }
+  }
+  // 4. router gradient, dx.
+  {
+    moe::BwdArgs b{T, H, k, E, I / L.cz.wg_n, L.c3.kg, dwpart, topk_w, topk_ids, part,
+                   (const uint16_t*)w_router, (const uint16_t*)x, (float*)(ws + L.dl), dx,
+                   dw_router, dbias};
+    hipError_t err = moe::launch_bwd_router(b, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_backward router-gradient launch");
+  }
+  // 5. dW2[e] = sum over e's rows of (w dout) act^T; dW1 | dW3 = sum of [dg | du] x^T.
+  {
+    moe::WgradArgs w{(const uint16_t*)dout, (const uint16_t*)act, H, I, 1, 0,
+                     (int64_t)T * H * 2, cap * I * 2, H, I, E, H, expert_offset, sorted_slot,
+                     topk_w, S, k_magic(k), dw2, dw2};
+    hipError_t err = moe::launch_wgrad(w, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_backward dW2 launch");
+    moe::WgradArgs w13g{dgu, (const uint16_t*)x, 2 * I, H, 0, 1, cap * 4 * I,
+                        (int64_t)T * H * 2, 2 * I, H, E, I, expert_offset, sorted_slot, topk_w,
+                        S, k_magic(k), dw1, dw3};
+    return hip_status(moe::launch_wgrad(w13g, stream), "moe_backward dW1/dW3 launch");
+  }
 }
 
 }  // extern "C"

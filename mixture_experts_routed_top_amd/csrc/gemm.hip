@@ -1,10 +1,9 @@
 // Grouped expert GEMMs of the routed MoE layer on gfx950 matrix cores: stage 1
-// (gather-on-load + gate/up GEMM + SwiGLU) and stage 2 (the FP8 requantisation
-// of the intermediate as it is loaded, down GEMM, weighted per-slot scatter and
-// the fixed-order combine of each token's partials by the last workgroup to
-// finish them). The fusion of gather, group GEMM, SwiGLU and scatter is the
-// routed MoE GEMM of the FlyDSL-in-JAX talk summary (5:56); the tiling here is
-// this library's own.
+// (gather-on-load + gate/up GEMM + SwiGLU) and stage 2 (down GEMM + weighted
+// per-slot scatter), plus the FP8 requantisation of the intermediate and the
+// fixed-order combine. The fusion of gather, group GEMM, SwiGLU and scatter is
+// the routed MoE GEMM of the FlyDSL-in-JAX talk summary (5:56); the tiling
+// here is this library's own.
 //
 // Matrix-core roles. The A operand of v_mfma_f32_32x32x64_f8f6f4 (FP8) or of
 // two v_mfma_f32_32x32x16_bf16 (BF16) is a fragment of 32 expert-weight rows
@@ -37,9 +36,8 @@
 // sharing an expert's weights run together (tile_coords). Decode shapes index
 // only the live tiles, from the device-side padded total. Stage 2 at prefill
 // sizes cuts the tiles of a partial last round of workgroups into reduction
-// pieces (tail_plan); the last piece of a tile to finish sums them. Stage 1
-// stages its bf16 output tile in LDS and writes whole row segments
-// non-temporally.
+// pieces (tail_plan, tail_reduce_kernel). Stage 1 stages its bf16 output tile
+// in LDS and writes whole row segments non-temporally.
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -139,14 +137,6 @@ constexpr uint32_t kPadOffset = 0x80000000u;
 // piece).
 __device__ __forceinline__ int lds_swz(int c) { return 4 * (c & 1) + 10 * (c >> 1); }
 
-// n / k for 0 <= n < 2^30 and 1 <= k <= 32 with magic = ceil(2^35 / k):
-// n*magic / 2^35 = n/k + n*(magic*k - 2^35)/(k*2^35), and the added term is
-// below (k-1)/(32k), too small to carry the fraction of n/k (at most
-// (k-1)/k) past the next integer, so the quotient is exact. A multiply
-// instead of a division keeps the compiler from branching around it.
-__device__ __forceinline__ uint32_t div_k(int n, uint64_t magic) {
-  return (uint32_t)(((uint64_t)(uint32_t)n * magic) >> 35);
-}
 
 template <int MT, int KSPLIT, int CK>
 constexpr int gemm_lds_bytes() {
@@ -192,32 +182,11 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-// FP8 stage 2 loads the bf16 intermediate and requantises it with the row's
-// scale s (r = 1/s) on its way into LDS: 16 bf16 values (two 16-byte loads)
-// -> 16 e4m3fn codes, value i in byte i.
-__device__ __forceinline__ uint4 quant_piece(uint4 lo, uint4 hi, float s, float r) {
-  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = f32x4_to_e4m3(quant_div(bf16_bits_to_f32(w[2 * i] & 0xffffu), s, r),
-                         quant_div(bf16_bits_to_f32(w[2 * i] >> 16), s, r),
-                         quant_div(bf16_bits_to_f32(w[2 * i + 1] & 0xffffu), s, r),
-                         quant_div(bf16_bits_to_f32(w[2 * i + 1] >> 16), s, r));
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 // The E2M1 decode tile of stage 1 (one token fragment, four weight fragments
-// per wave) and the FP8 decode tile of stage 2 (whose bf16 token pieces take
-// twice the registers) are held to the 256 registers that two waves per SIMD
-// leave each.
+// per wave) is held to the 256 registers that two waves per SIMD leave each.
 template <int DT, int STAGE, int MT, int NF, int KSPLIT, int NB, int CK>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu((DT == 3 && MT == 1 && NF == 4) || (DT == 1 && STAGE == 2 &&
-                                                                      MT == 1)
-                                       ? 2
-                                       : 1,
-                                   8)))
+__attribute__((amdgpu_waves_per_eu(DT == 3 && MT == 1 && NF == 4 ? 2 : 1, 8)))
 void gemm_kernel(GemmArgs a) {
   constexpr int kSub = CK / 64;          // fragments along the reduction per stage
   constexpr int kChunk = CK;             // reduction bytes per pipeline stage
@@ -242,10 +211,6 @@ void gemm_kernel(GemmArgs a) {
   // covers 32 reduction values), so that one LDS read gives a lane the codes
   // of all MT fragments in one column.
   constexpr bool MX = DT == 2 || DT == 3;
-  // FP8 stage 2 reads the bf16 intermediate (XW = 2 source bytes per operand
-  // byte) and requantises it per row as it stages it (quant_piece).
-  constexpr bool XQ = DT == 1 && STAGE == 2;
-  constexpr int XW = XQ ? 2 : 1;
   // Weight fragment: two 1 KB pieces, or one for E2M1 (32 rows x 32 bytes).
   constexpr int WP = DT == 3 ? 1 : 2;
   constexpr int WFRAG = WP * kPiece;
@@ -262,10 +227,8 @@ void gemm_kernel(GemmArgs a) {
   constexpr int STG = STAGE == 1 ? BMT * SP : 0;
   constexpr int MAIN = LDS + XST;  // main loop: token buffers and the MXFP8 code tile
   constexpr int LDSX = (MAIN > STG ? MAIN : STG) + (STAGE == 1 && DT == 1 ? WN * BMT * 4 : 0);
-  constexpr int RS = XQ ? BMT : 0;  // FP8 stage 2: the tile rows' scales, for the epilogue
-  __shared__ __align__(16) uint8_t lds[LDSX + (SCL + RS) * 4];
+  __shared__ __align__(16) uint8_t lds[LDSX + SCL * 4];
   float* const scl = reinterpret_cast<float*>(lds + LDSX);
-  float* const rowscale = scl + SCL;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wk = wave / WN;
@@ -278,18 +241,8 @@ void gemm_kernel(GemmArgs a) {
   // Tile order: XCD-contiguous runs of logical tiles (xcd_remap), grouped as
   // tile_coords describes.
   int kg = 0, mtile, ntile, total, e_raw;
-  int piece = -1, tail_idx = 0, n_tail = 0, n_split = 1;  // stage-2 tail piece of this workgroup
-  int cbegin = 0;                                         // first reduction chunk
-  if constexpr (STAGE == 2) {
-    // An empty grouping (ids outside the expert range): no tile runs, and the
-    // launch writes an all-zero output.
-    if (*a.total_padded == 0) {
-      const int64_t n4 = (int64_t)a.T * a.N / 4;
-      for (int64_t i = blockIdx.x * 256 + tid; i < n4; i += (int64_t)gridDim.x * 256)
-        *reinterpret_cast<uint2*>(a.y + i * 4) = make_uint2(0u, 0u);
-      return;
-    }
-  }
+  int piece = -1, tail_idx = 0, n_tail = 0;  // stage-2 tail piece of this workgroup
+  int cbegin = 0;                            // first reduction chunk
   if (a.tail_split == 0 && !a.live_order) {
     const int logical = xcd_remap(blockIdx.x, a.n_mtiles * a.n_ntiles * a.kg);
     kg = logical % a.kg;
@@ -320,7 +273,6 @@ void gemm_kernel(GemmArgs a) {
       tail_idx = pi % pl.tail;
       piece = pi / pl.tail;
       n_tail = pl.tail;
-      n_split = pl.split;
       logical = pl.n_full + tail_idx;
       cbegin = piece * nchunks / pl.split;
       nchunks = (piece + 1) * nchunks / pl.split - cbegin;
@@ -343,7 +295,6 @@ void gemm_kernel(GemmArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, (int)a.x_bytes, 0x00020000);
   uint32_t xoff[PPT];
   int loff[PPT];
-  float qsc[PPT], qinv[PPT];  // FP8 stage 2: scale and its reciprocal of each piece's row
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
     const int q = tid + 256 * j;
@@ -354,8 +305,8 @@ void gemm_kernel(GemmArgs a) {
     // Pad rows (sentinel slot) are not read at all.
     const int slot = a.sorted_slot[p];
     const uint32_t row = STAGE == 1 ? div_k(min(slot, S - 1), a.k_magic) : (uint32_t)p;
-    const uint32_t rowbase = slot < S ? row * (uint32_t)(Kb * XW) : kPadOffset;  // select
-    xoff[j] = rowbase + (uint32_t)((kbase + ks * Kw + s * 64 + c * 16) * XW);
+    const uint32_t rowbase = slot < S ? row * (uint32_t)Kb : kPadOffset;  // select, no branch
+    xoff[j] = rowbase + (uint32_t)(kbase + ks * Kw + s * 64 + c * 16);
     // Column c goes to piece c&1 of lane half c>>1 (MXFP8: piece c>>1 of lane
     // half c&1, so that each piece is one 32-value scale block).
     const int pce = MX ? (c >> 1) : (c & 1), hlf = MX ? (c & 1) : (c >> 1);
@@ -386,28 +337,21 @@ void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][f][i] = 0.0f;
 
-  uint4 xr[2][PPT * XW];        // token prefetch, by chunk parity
+  uint4 xr[2][PPT];             // token prefetch, by chunk parity
   uint4 wbuf[NB][kSub][NF][WP];  // weight prefetch: [stage][sub-block][fragment][piece]
   uint32_t wsr[NB][kSub];       // MXFP8 weight codes, staged like the weights
   uint32_t xsr[2][kSub];        // MXFP8 token codes, by chunk parity
 
-  auto load_x = [&](int c, uint4 (&x)[PPT * XW]) {
+  auto load_x = [&](int c, uint4 (&x)[PPT]) {
 #pragma unroll
-    for (int j = 0; j < PPT * XW; ++j)
+    for (int j = 0; j < PPT; ++j)
       x[j] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                     xrsrc, xoff[j / XW] + (uint32_t)(c * kChunk * XW + 16 * (j % XW)), 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff[j] + (uint32_t)c * kChunk, 0, 0));
   };
-  auto store_x = [&](int buf, const uint4 (&x)[PPT * XW]) {
+  auto store_x = [&](int buf, const uint4 (&x)[PPT]) {
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      uint4 v;
-      if constexpr (XQ)
-        v = quant_piece(x[2 * j], x[2 * j + 1], qsc[j], qinv[j]);
-      else
-        v = x[j];
-      *reinterpret_cast<uint4*>(lds + buf * BUF + loff[j]) = v;
-    }
+    for (int j = 0; j < PPT; ++j)
+      *reinterpret_cast<uint4*>(lds + buf * BUF + loff[j]) = x[j];
   };
   auto load_w1 = [&](int c, int s, int f, int pc, uint4& w) {
     w = *reinterpret_cast<const uint4*>(wbase + f * wfrag_stride +
@@ -468,19 +412,19 @@ void gemm_kernel(GemmArgs a) {
   uint4 xf[2][2];
   auto step = [&](int c, auto u_const) {
     constexpr int u = decltype(u_const)::value;
-    constexpr int NWL = PPT * XW + kSub * NF * WP;  // token and weight loads
+    constexpr int NWL = PPT + kSub * NF * WP;  // token and weight loads
     constexpr int NLOAD = NWL + (MX ? kSub : 0);
     constexpr int NM = NSTEP * NF;
     const int last = nchunks - 1;
     const int cx = min(c + 3, last), cw = min(c + NB - 1, last);
     auto issue = [&](auto j_const) {
       constexpr int j = decltype(j_const)::value;
-      if constexpr (j < PPT * XW) {
+      if constexpr (j < PPT) {
         xr[(u + 1) & 1][j] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       xrsrc, xoff[j / XW] + (uint32_t)(cx * kChunk * XW + 16 * (j % XW)), 0, 0));
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff[j] + (uint32_t)cx * kChunk,
+                                                         0, 0));
       } else if constexpr (j < NWL) {
-        constexpr int q = j - PPT * XW, s = q / (NF * WP), f = (q / WP) % NF, pc = q % WP;
+        constexpr int q = j - PPT, s = q / (NF * WP), f = (q / WP) % NF, pc = q % WP;
         load_w1(cw, s, f, pc, wbuf[(u + NB - 1) % NB][s][f][pc]);
       } else {
         load_ws(cw, j - NWL, wsr[(u + NB - 1) % NB][j - NWL]);
@@ -529,7 +473,8 @@ void gemm_kernel(GemmArgs a) {
     if constexpr (STAGE == 1)
       rsc[m] = DT == 1 ? a.x_scale[div_k(sc, a.k_magic)] : 1.0f;
     else
-      rsc[m] = a.topk_w[sc];  // FP8: times the row scale, from LDS in the epilogue
+      rsc[m] = (a.unit_w ? 1.0f : a.topk_w[sc]) *
+               (DT == 1 ? a.x_scale[row0 + m * 32 + tok] : 1.0f);
   }
   // Column scales of this workgroup's features (FP8): loaded after the
   // pipeline's first loads, kept in registers through the main loop and
@@ -559,34 +504,6 @@ void gemm_kernel(GemmArgs a) {
       if constexpr (MX)
 #pragma unroll
         for (int sb = 0; sb < kSub; ++sb) load_ws(min(u, last), sb, wsr[u][sb]);
-    }
-    if constexpr (XQ) {
-      // Row scale of each staged piece's row: the maximum of its partial maxima
-      // (the four threads of a row take every fourth partial), s = max/448
-      // (1 for an all-zero row, as pad rows are).
-#pragma unroll
-      for (int j = 0; j < PPT; ++j) {
-        const int q = tid + 256 * j;
-        const int c = q & 3, r = (q >> 2) & 31, m = (q >> 7) % MT;
-        const float* ap = a.amax_part + (size_t)(row0 + m * 32 + r) * a.nparts;
-        float mx = 0.0f;
-        if ((a.nparts & 15) == 0) {
-          const float4* ap4 = reinterpret_cast<const float4*>(ap);
-#pragma unroll 4
-          for (int i = c; i < a.nparts / 4; i += 4) {
-            const float4 v = ap4[i];
-            mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-          }
-        } else {
-#pragma unroll 4
-          for (int i = c; i < a.nparts; i += 4) mx = fmaxf(mx, ap[i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-        qsc[j] = mx > 0.0f ? mx / 448.0f : 1.0f;
-        qinv[j] = 1.0f / qsc[j];
-        if (c == 0 && q < 128 * MT) rowscale[m * 32 + r] = qsc[j];  // one writer per row
-      }
     }
     load_x(0, xr[0]);
     load_x(min(1, last), xr[1]);
@@ -717,6 +634,96 @@ void gemm_kernel(GemmArgs a) {
     __syncthreads();  // the amax step below reuses the same LDS
   }
 
+  if constexpr (STAGE == 1 && DT == 0) {
+    if (a.epi == 1) {
+      // Backward recompute: the gate and up pre-activations in bf16, g to
+      // columns i, u to columns I + i of the row (pad rows are not written).
+      if (wk != 0) return;
+      uint16_t* gu = reinterpret_cast<uint16_t*>(a.out);
+      const int ib0 = rb0 / 2;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (rslot[m] >= S) continue;
+        uint16_t* row = gu + (size_t)(row0 + m * 32 + tok) * 2 * a.I;
+#pragma unroll
+        for (int qg = 0; qg < NF / 2 * 4; ++qg) {
+          const int q = qg / 4, g = qg % 4;
+          const int i0 = (ib0 + q) * 32 + 8 * g + fq;
+          const f32x16& ga = acc[m][2 * q];
+          const f32x16& ua = acc[m][2 * q + 1];
+          *reinterpret_cast<uint2*>(row + i0) =
+              make_uint2(f32x2_to_bf16x2(ga[4 * g], ga[4 * g + 1]),
+                         f32x2_to_bf16x2(ga[4 * g + 2], ga[4 * g + 3]));
+          *reinterpret_cast<uint2*>(row + a.I + i0) =
+              make_uint2(f32x2_to_bf16x2(ua[4 * g], ua[4 * g + 1]),
+                         f32x2_to_bf16x2(ua[4 * g + 2], ua[4 * g + 3]));
+        }
+      }
+      return;
+    }
+    if (a.epi == 2) {
+      // Backward of the SwiGLU: acc holds z = W2^T dout of the row's token
+      // (features i of fragment f: (rb0 + f) * 32 + ...). With the row's
+      // routing weight w, the forward's a = act and the recomputed g, u:
+      //   <z, a> over these columns -> dwpart (the routing weight's gradient),
+      //   da = w z, dg = da u s (1 + g (1 - s)), du = da g s, s = sigmoid(g).
+      float* wsum = reinterpret_cast<float*>(lds);  // [WN][BMT] partial dot products
+      uint16_t* dgu = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int slot = rslot[m];
+        float dsum = 0.0f;
+        if (wk == 0 && slot < S) {
+          const size_t p = (size_t)(row0 + m * 32 + tok);
+          const float w = a.topk_w[slot];
+          const uint16_t* arow = a.act_in + p * a.I;
+          const uint16_t* grow = a.gu + p * 2 * a.I;
+          uint16_t* drow = dgu + p * 2 * a.I;
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int i0 = (rb0 + f) * 32 + 8 * g + fq;
+              const uint2 av = *reinterpret_cast<const uint2*>(arow + i0);
+              const uint2 gv = *reinterpret_cast<const uint2*>(grow + i0);
+              const uint2 uv = *reinterpret_cast<const uint2*>(grow + a.I + i0);
+              const uint32_t aw[2] = {av.x, av.y}, gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
+              float dg[4], du[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int sh = 16 * (r & 1);
+                const float z = acc[m][f][4 * g + r];
+                const float av_r = bf16_bits_to_f32((aw[r >> 1] >> sh) & 0xffffu);
+                const float gg = bf16_bits_to_f32((gw[r >> 1] >> sh) & 0xffffu);
+                const float uu = bf16_bits_to_f32((uw[r >> 1] >> sh) & 0xffffu);
+                dsum = fmaf(z, av_r, dsum);
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gg));
+                const float da = w * z;
+                dg[r] = da * uu * sg * (1.0f + gg * (1.0f - sg));
+                du[r] = da * gg * sg;
+              }
+              *reinterpret_cast<uint2*>(drow + i0) =
+                  make_uint2(f32x2_to_bf16x2(dg[0], dg[1]), f32x2_to_bf16x2(dg[2], dg[3]));
+              *reinterpret_cast<uint2*>(drow + a.I + i0) =
+                  make_uint2(f32x2_to_bf16x2(du[0], du[1]), f32x2_to_bf16x2(du[2], du[3]));
+            }
+        }
+        // lane halves hold the same row, then the waves along the features
+        dsum = dsum + __shfl_xor(dsum, 32, 64);
+        if (wk == 0 && lane < 32) wsum[wn * BMT + m * 32 + lane] = dsum;
+      }
+      __syncthreads();
+      for (int r = tid; r < BMT; r += 256) {
+        const int slot = a.sorted_slot[row0 + r];
+        if (slot >= S) continue;
+        float v = wsum[r];
+#pragma unroll
+        for (int w = 1; w < WN; ++w) v = v + wsum[w * BMT + r];
+        a.dwpart[(size_t)slot * a.n_ntiles + ntile] = v;
+      }
+      return;
+    }
+  }
   if constexpr (STAGE == 1) {
     // SwiGLU epilogue: fragment 2q is gate block ib0+q, fragment 2q+1 the
     // matching up block.
@@ -789,123 +796,88 @@ void gemm_kernel(GemmArgs a) {
     }
   } else {
     // Down-projection epilogue: weighted per-slot partials, one writer per element.
-    float* const part0 = reinterpret_cast<float*>(a.out);
-    float* const part = part0 + (size_t)kg * S * a.N;
+    if (wk != 0) return;
+    float* part = reinterpret_cast<float*>(a.out) + (size_t)kg * S * a.N;
     // A tail piece writes its tile-local partial instead: rows of the tile,
     // columns of the workgroup, in the piece's slice of the tail space.
     float* const tp = a.tail_part + (size_t)(piece * n_tail + tail_idx) * BMT * WGN;
-    if (wk == 0) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int slot = rslot[m];
-        if (slot >= S) continue;
-        const float sc = rsc[m] * (XQ ? rowscale[m * 32 + tok] : 1.0f);
+    for (int m = 0; m < MT; ++m) {
+      const int slot = rslot[m];
+      if (slot >= S) continue;
+      const float sc = rsc[m];
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
+      for (int f = 0; f < NF; ++f)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int h0 = (rb0 + f) * 32 + 8 * g + fq;
-            float ws[4] = {1.f, 1.f, 1.f, 1.f};
-            if constexpr (DT == 1) {
-              const float4 w4 = *reinterpret_cast<const float4*>(scl + (h0 - ntile * WGN));
-              ws[0] = w4.x; ws[1] = w4.y; ws[2] = w4.z; ws[3] = w4.w;
-            }
-            float4 o;
-            o.x = acc[m][f][4 * g + 0] * ws[0] * sc;
-            o.y = acc[m][f][4 * g + 1] * ws[1] * sc;
-            o.z = acc[m][f][4 * g + 2] * ws[2] * sc;
-            o.w = acc[m][f][4 * g + 3] * ws[3] * sc;
-            if (piece < 0)
-              *reinterpret_cast<float4*>(part + (size_t)slot * a.N + h0) = o;
-            else
-              *reinterpret_cast<float4*>(tp + (size_t)(m * 32 + tok) * WGN + (h0 - ntile * WGN)) = o;
+        for (int g = 0; g < 4; ++g) {
+          const int h0 = (rb0 + f) * 32 + 8 * g + fq;
+          float ws[4] = {1.f, 1.f, 1.f, 1.f};
+          if constexpr (DT == 1) {
+            const float4 w4 = *reinterpret_cast<const float4*>(scl + (h0 - ntile * WGN));
+            ws[0] = w4.x; ws[1] = w4.y; ws[2] = w4.z; ws[3] = w4.w;
           }
-      }
-    }
-    constexpr int C4 = WGN / 4;  // float4 columns of the workgroup
-    __shared__ int flag;
-    if (piece >= 0) {
-      // The last piece of a tail tile to finish sums the tile's pieces, in
-      // piece order, into the slots' partials; it then takes the tile's place.
-      if (!last_workgroup(a.tile_tickets + tail_idx, n_split, &flag)) return;
-      const size_t pstride = (size_t)n_tail * BMT * WGN;
-      const float* const tp0 = a.tail_part + (size_t)tail_idx * BMT * WGN;
-      for (int i = tid; i < BMT * C4; i += 256) {
-        const int r = i / C4, c4 = i % C4;
-        const int slot = a.sorted_slot[row0 + r];
-        if (slot >= S) continue;
-        const float* src = tp0 + (size_t)r * WGN + c4 * 4;
-        float4 v = *reinterpret_cast<const float4*>(src);
-        for (int pc = 1; pc < n_split; ++pc) {
-          const float4 w = *reinterpret_cast<const float4*>(src + pc * pstride);
-          v.x = v.x + w.x;
-          v.y = v.y + w.y;
-          v.z = v.z + w.z;
-          v.w = v.w + w.w;
+          float4 o;
+          o.x = acc[m][f][4 * g + 0] * ws[0] * sc;
+          o.y = acc[m][f][4 * g + 1] * ws[1] * sc;
+          o.z = acc[m][f][4 * g + 2] * ws[2] * sc;
+          o.w = acc[m][f][4 * g + 3] * ws[3] * sc;
+          if (piece < 0)
+            *reinterpret_cast<float4*>(part + (size_t)slot * a.N + h0) = o;
+          else
+            *reinterpret_cast<float4*>(tp + (size_t)(m * 32 + tok) * WGN + (h0 - ntile * WGN)) = o;
         }
-        *reinterpret_cast<float4*>(part + (size_t)slot * a.N + ntile * WGN + c4 * 4) = v;
-      }
-    }
-    // Combine: each real row's token takes a ticket for this feature tile; the
-    // workgroup that completes a token's k * kg partials (k slots, kg
-    // reduction splits) sums them in the fixed order (j ascending, then g)
-    // and writes the token's output columns. Integer tickets only: the sum
-    // does not depend on which workgroup finishes last.
-    int* const fin = reinterpret_cast<int*>(lds);  // the token buffers are free now
-    release_device();
-    __syncthreads();
-    if (tid < BMT) {
-      const int slot = a.sorted_slot[row0 + tid];
-      int t = -1;
-      if (slot < S) {
-        const int tt = (int)div_k(slot, a.k_magic);
-        int32_t* const tk = a.tickets + (size_t)tt * a.n_ntiles + ntile;
-        if (ticket_add(tk, 1) == a.k * a.kg - 1) {
-          t = tt;
-          ticket_reset(tk);
-        }
-      }
-      if (t >= 0) acquire_device();
-      fin[tid] = t;
-    }
-    __syncthreads();
-    const int n = a.k * a.kg;  // partials per output, summed in the order u = j*kg + g
-    const size_t split = (size_t)S * a.N;
-    for (int i = tid; i < BMT * C4; i += 256) {
-      const int r = i / C4, c4 = i % C4;
-      const int t = fin[r];
-      if (t < 0) continue;
-      const int h = ntile * WGN + c4 * 4;
-      const float* const pt = part0 + (size_t)t * a.k * a.N + h;
-      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-      constexpr int B = 8;  // partials loaded before any is added
-      for (int u0 = 0; u0 < n; u0 += B) {
-        float4 v[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const int u = u0 + b, j = u / a.kg, g = u % a.kg;
-          if (u < n) v[b] = *reinterpret_cast<const float4*>(pt + g * split + (size_t)j * a.N);
-        }
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          if (u0 + b >= n) break;
-          if (u0 + b == 0) {
-            sum = v[b];
-          } else {
-            sum.x = sum.x + v[b].x;
-            sum.y = sum.y + v[b].y;
-            sum.z = sum.z + v[b].z;
-            sum.w = sum.w + v[b].w;
-          }
-        }
-      }
-      *reinterpret_cast<uint2*>(a.y + (size_t)t * a.N + h) =
-          make_uint2(f32x2_to_bf16x2(sum.x, sum.y), f32x2_to_bf16x2(sum.z, sum.w));
     }
   }
 }
 
 // ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void quant_act_kernel(QuantArgs a) {
+  __shared__ float red[4];
+  const int p = blockIdx.x;
+  if (p >= *a.total_padded) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint16_t* row = a.act + (size_t)p * a.I;
+  // The row's first chunks are loaded before the row maximum is known, so
+  // that their latency overlaps the maxima's (rows of up to 8 * 2048 values
+  // come entirely from these registers).
+  constexpr int kPre = 8;
+  uint4 pre[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int c = tid + 256 * j;
+    if (c < a.I / 8) pre[j] = *reinterpret_cast<const uint4*>(row + c * 8);
+  }
+  float m = 0.0f;
+  for (int i = tid; i < a.nparts; i += 256) m = fmaxf(m, a.amax_part[(size_t)p * a.nparts + i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = m > 0.0f ? m / 448.0f : 1.0f;
+  const float inv = 1.0f / s;  // for the correctly rounded quotients (quant_div)
+  if (tid == 0) a.act_scale[p] = s;
+  uint8_t* q = a.act_q + (size_t)p * a.I;
+  auto convert = [&](int c, const uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = quant_div(bf16_bits_to_f32(w[i] & 0xffffu), s, inv);
+      f[2 * i + 1] = quant_div(bf16_bits_to_f32(w[i] >> 16), s, inv);
+    }
+    *reinterpret_cast<uint2*>(q + c * 8) =
+        make_uint2(f32x4_to_e4m3(f[0], f[1], f[2], f[3]), f32x4_to_e4m3(f[4], f[5], f[6], f[7]));
+  };
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int c = tid + 256 * j;
+    if (c < a.I / 8) convert(c, pre[j]);
+  }
+  for (int c = tid + 256 * kPre; c < a.I / 8; c += 256)
+    convert(c, *reinterpret_cast<const uint4*>(row + c * 8));
+}
 
 // MX block quantisation of the bf16 intermediate (MXFP8 stage 2): one thread
 // per block of 32 values of a row p < total_padded; the block maximum sets the
@@ -944,6 +916,80 @@ __global__ __launch_bounds__(256) void quant_act_mx_kernel(QuantMxArgs a) {
   dq[0] = make_uint4(c[0], c[1], c[2], c[3]);
   dq[1] = make_uint4(c[4], c[5], c[6], c[7]);
   a.act_mx[(size_t)p * nb + b] = (uint8_t)(x + 127);
+}
+
+// out[t,:] = bf16( sum_j sum_g part[g][t*k+j][:] ), j ascending, then split g ascending.
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int64_t n4 = (int64_t)a.T * a.H / 4;
+  const size_t split = (size_t)a.T * a.k * a.H;
+  if (*a.total_padded == 0) {  // empty grouping (invalid ids): no partial was written
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x)
+      *reinterpret_cast<uint2*>(a.out + (size_t)i * 4) = make_uint2(0u, 0u);
+    return;
+  }
+  const int n = a.k * a.kg;  // partials per output, summed in the order u = j*kg + g
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i * 4 / a.H, h = i * 4 % a.H;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    // Eight partials are loaded before any is added, so their latencies overlap.
+    constexpr int B = 8;
+    for (int u0 = 0; u0 < n; u0 += B) {
+      float4 v[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int u = u0 + b, j = u / a.kg, g = u % a.kg;
+        if (u < n)
+          v[b] = *reinterpret_cast<const float4*>(a.part + g * split +
+                                                  ((size_t)t * a.k + j) * a.H + h);
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        if (u0 + b >= n) break;
+        if (u0 + b == 0) {
+          s = v[b];
+        } else {
+          s.x = s.x + v[b].x;
+          s.y = s.y + v[b].y;
+          s.z = s.z + v[b].z;
+          s.w = s.w + v[b].w;
+        }
+      }
+    }
+    *reinterpret_cast<uint2*>(a.out + (size_t)t * a.H + h) =
+        make_uint2(f32x2_to_bf16x2(s.x, s.y), f32x2_to_bf16x2(s.z, s.w));
+  }
+}
+
+// part[slot][h] of the tail tiles = sum over pieces p = 0, 1, ... in order of
+// tail_part[p][tile][row][col]; one float4 per thread and step.
+__global__ __launch_bounds__(256) void tail_reduce_kernel(TailReduceArgs a) {
+  const int total = *a.total_padded;
+  const int n_m = total / a.bmt;
+  const TailPlan pl = tail_plan(n_m * a.n_ntiles, a.round, a.tail_split, a.nchunks);
+  if (pl.split < 2) return;
+  const int c4n = a.wgn / 4;
+  const int64_t items = (int64_t)pl.tail * a.bmt * c4n;
+  const size_t piece_stride = (size_t)pl.tail * a.bmt * a.wgn;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < items;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int c4 = (int)(i % c4n), r = (int)(i / c4n % a.bmt), ti = (int)(i / ((int64_t)c4n * a.bmt));
+    int mtile, ntile;
+    tile_coords(pl.n_full + ti, n_m, a.group_m, a.n_ntiles, mtile, ntile);
+    const int slot = a.sorted_slot[mtile * a.bmt + r];
+    if (slot >= a.S) continue;
+    const float* src = a.tail_part + ((size_t)ti * a.bmt + r) * a.wgn + c4 * 4;
+    float4 acc = *reinterpret_cast<const float4*>(src);
+    for (int p = 1; p < pl.split; ++p) {
+      const float4 v = *reinterpret_cast<const float4*>(src + p * piece_stride);
+      acc.x = acc.x + v.x;
+      acc.y = acc.y + v.y;
+      acc.z = acc.z + v.z;
+      acc.w = acc.w + v.w;
+    }
+    *reinterpret_cast<float4*>(a.part + (size_t)slot * a.N + ntile * a.wgn + c4 * 4) = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1121,9 +1167,27 @@ hipError_t launch_gemm(int dt, int stage, const GemmCfg& c, const GemmArgs& a, h
   return dispatch(dt, stage, c, a, st);
 }
 
+hipError_t launch_tail_reduce(const TailReduceArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3(1024), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const QuantArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(quant_act_kernel, dim3(a.cap), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_act_mx(const QuantMxArgs& a, hipStream_t st) {
   const int64_t n = (int64_t)a.cap * (a.I / 32);
   hipLaunchKernelGGL(quant_act_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+  int64_t n4 = (int64_t)a.T * a.H / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -73,42 +73,13 @@ __device__ __forceinline__ float mx_inv_scale(int x) {
   return __uint_as_float((uint32_t)(127 - x) << 23);
 }
 
-// Release of this thread's earlier global writes to every workgroup of the
-// device (agent scope), and the matching acquire. Workgroups that hand results
-// to each other through a ticket (an integer counter, no floating-point
-// atomics) use them around it: the writers release before taking the ticket,
-// and the workgroup that finds itself last acquires before reading.
-__device__ __forceinline__ void release_device() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-}
-__device__ __forceinline__ void acquire_device() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-__device__ __forceinline__ int ticket_add(int32_t* t, int v) {
-  return __hip_atomic_fetch_add(t, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void ticket_reset(int32_t* t) {
-  __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Whether this workgroup is the last of n to arrive at `ticket` (the same
-// answer in every thread). Every thread's global writes made before the call
-// are visible to the last workgroup after it; the last workgroup resets the
-// ticket to zero, so the next launch finds it as this one did. `flag` is one
-// int of LDS.
-__device__ __forceinline__ bool last_workgroup(int32_t* ticket, int n, int* flag) {
-  release_device();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const bool last = ticket_add(ticket, 1) == n - 1;
-    if (last) {
-      acquire_device();
-      ticket_reset(ticket);
-    }
-    *flag = last;
-  }
-  __syncthreads();
-  return *flag != 0;
+// n / k for 0 <= n < 2^30 and 1 <= k <= 32 with magic = ceil(2^35 / k):
+// n*magic / 2^35 = n/k + n*(magic*k - 2^35)/(k*2^35), and the added term is
+// below (k-1)/(32k), too small to carry the fraction of n/k (at most
+// (k-1)/k) past the next integer, so the quotient is exact. A multiply
+// instead of a division keeps the compiler from branching around it.
+__device__ __forceinline__ uint32_t div_k(int n, uint64_t magic) {
+  return (uint32_t)(((uint64_t)(uint32_t)n * magic) >> 35);
 }
 
 // Physical workgroup id -> logical tile id so that each XCD (workgroups are

@@ -6,20 +6,6 @@
 
 namespace moe {
 
-struct AlignArgs {
-  const int32_t* ids;  // [S]
-  int S, E, bm;
-  int32_t* sorted_slot;
-  int32_t* tile_expert;
-  int32_t* count;
-  int32_t* offset;
-  int32_t* total;
-};
-hipError_t launch_align(const AlignArgs& a, hipStream_t st);
-// Largest grouping the router launch can build in its last-arriving workgroup
-// (256 threads, runs of up to 8 slots); larger ones take launch_align.
-constexpr int kFusedAlignSlots = 2048;
-
 struct RouteArgs {
   const uint16_t* x;         // bf16 [T,H]
   const uint16_t* w_router;  // bf16 [E,H]
@@ -31,13 +17,19 @@ struct RouteArgs {
   uint8_t* x_q;              // [T,H] or null
   float* x_scale;            // [T] (per-token FP8)
   uint8_t* x_mx;             // [T][H/32] E8M0 codes (MXFP8: x_q holds block-scaled codes), or null
-  // Grouping built by the last workgroup to finish (ticket != null; the ids
-  // are topk_ids; T*k <= kFusedAlignSlots, at most 16 experts). The ticket is
-  // one int that is zero on entry; the last workgroup resets it.
-  AlignArgs al;
-  int32_t* ticket;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+struct AlignArgs {
+  const int32_t* ids;  // [S]
+  int S, E, bm;
+  int32_t* sorted_slot;
+  int32_t* tile_expert;
+  int32_t* count;
+  int32_t* offset;
+  int32_t* total;
+};
+hipError_t launch_align(const AlignArgs& a, hipStream_t st);
 
 // Byte relayout of one row-major [R, K] matrix per expert into fragment order.
 // For the gate/up pair (two sources) composite rows alternate 32-row blocks.
@@ -73,9 +65,9 @@ struct GemmCfg {
 };
 
 // Tiles of a partial last round of a stage-2 launch are cut along the
-// reduction into pieces, so that the round fills the device; the last piece
-// of a tile to finish sums the pieces' partials in piece order. At most
-// kTailPieces pieces per launch (workspace). A round is GemmCfg::round workgroups: the
+// reduction into pieces, so that the round fills the device; the pieces'
+// partials are summed in piece order by tail_reduce. At most kTailPieces
+// pieces per launch (workspace). A round is GemmCfg::round workgroups: the
 // MI355X's 256 compute units times the workgroups of the configuration one
 // of them holds.
 constexpr int kTailPieces = 256;
@@ -85,10 +77,8 @@ GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm);
 bool gemm_cfg_ok(int dt, int stage, const GemmCfg& c, int N, int K);
 
 struct GemmArgs {
-  const uint8_t* X;        // stage 1: x / x_q [T][K] (rows gathered by token); stage 2: act
-                           // bf16 [cap][I] (BF16 and FP8: FP8 requantises it as it loads it)
-                           // or the MX codes act_q [cap][I]
-  const float* x_scale;    // FP8 stage 1: per-token activation scale
+  const uint8_t* X;        // stage 1: x / x_q [T][K] (rows gathered by token); stage 2: act / act_q [cap][K]
+  const float* x_scale;    // FP8: per-token (stage 1) or per-row (stage 2) activation scale
   const uint8_t* W;        // preshuffled weights
   const float* w_scale;    // FP8: s13 [E][2][I] (stage 1) or s2 [E][H] (stage 2)
   const uint8_t* x_mx;     // MXFP8/MXFP4: E8M0 codes of X's rows, [rows of X][K/32]
@@ -98,28 +88,53 @@ struct GemmArgs {
   const int32_t* total_padded;
   const float* topk_w;     // stage 2
   void* out;               // stage 1: act bf16 [cap][I]; stage 2: part fp32 [kg][T*k][H]
-  float* amax_part;        // FP8 [cap][nparts] row maxima over stage 1's feature tiles
-                           // (stage 1 writes them, stage 2 reduces them to the row scale)
-  int nparts;
+  float* amax_part;        // stage 1 FP8: [cap][N/wg_n]
   int T, k, N, I, cap, bm;
-  int K_bytes;             // reduction bytes of one row in the matrix-core format (H or I
-                           // times the element size; FP8 stage 2: I, its source rows are 2I)
+  int K_bytes;             // reduction bytes of one row (H or I times the element size)
   int64_t x_bytes;         // size of X in bytes (< 2 GiB): loads past it read zeros
   int n_mtiles, n_ntiles;  // row tiles (32*mt rows) and feature tiles (wg_n rows)
   int kg, group_m;         // reduction split over workgroups; M-tiles per schedule group
   uint64_t k_magic;        // ceil(2^35 / k): slot / k as a multiply
   float* tail_part;        // stage 2 tail pieces: [kTailPieces][32*mt][wg_n] (tail_split > 0)
   int round;               // GemmCfg::round
+  // Backward pass (BF16 only): epi 1 = stage 1 writes the gate and up
+  // pre-activations g, u to out (bf16 [cap][2I]: g in columns 0..I-1, u in
+  // I..2I-1) instead of the SwiGLU; epi 2 = stage 1 over W2^T and the gathered
+  // output gradient rows computes z = W2^T dout and writes dg, du to out (bf16
+  // [cap][2I]) from act_in, gu and topk_w, and each row's partial <z, act>
+  // over the workgroup's columns to dwpart [T*k][n_ntiles]; unit_w = stage 2
+  // weighs every row by 1 instead of its routing weight.
+  int epi;
+  const uint16_t* act_in;
+  const uint16_t* gu;
+  float* dwpart;
+  int unit_w;
   int tail_split;          // GemmCfg::tail_split
   int live_order;          // index the live tiles first (decode shapes) instead of the capacity
-  // Stage 2 combine: out[t,:] = bf16(sum_j sum_g part[g][t*k+j][:]) by the last
-  // workgroup to finish each (token, feature tile); tickets [T][n_ntiles] and,
-  // with tail pieces, tile_tickets [kTailPieces]: zero on entry, left zero.
-  uint16_t* y;             // bf16 [T][N]
-  int32_t* tickets;
-  int32_t* tile_tickets;
 };
 hipError_t launch_gemm(int dt, int stage, const GemmCfg& c, const GemmArgs& a, hipStream_t st);
+
+// Sum of the tail pieces of a stage-2 launch, in piece order, into the per-slot
+// partials (the same tile plan as the GEMM, from the device-side total).
+struct TailReduceArgs {
+  const float* tail_part;
+  const int32_t* sorted_slot;
+  const int32_t* total_padded;
+  float* part;             // [T*k][N]
+  int S, N, bmt, wgn, n_ntiles, group_m, round, tail_split, nchunks;
+};
+hipError_t launch_tail_reduce(const TailReduceArgs& a, hipStream_t st);
+
+// FP8 stage 2 prologue: per-row amax from the partials, scale, requantise.
+struct QuantArgs {
+  const uint16_t* act;     // bf16 [cap][I]
+  const float* amax_part;  // [cap][nparts] (row-major: a row's partial maxima together)
+  int nparts, cap, I;
+  const int32_t* total_padded;
+  uint8_t* act_q;          // [cap][I]
+  float* act_scale;        // [cap]
+};
+hipError_t launch_quant_act(const QuantArgs& a, hipStream_t st);
 
 // MXFP8 stage 2 prologue: the MX block quantisation of every row p < total of
 // the bf16 intermediate (32 values per E8M0 code).
@@ -137,5 +152,64 @@ hipError_t launch_quant_act_mx(const QuantMxArgs& a, hipStream_t st);
 // (at most 8192), stage 2 over I (at most 16384).
 constexpr int kMxMaxH = 8192;
 constexpr int kMxMaxI = 16384;
+
+// out[t,:] = bf16(sum_j sum_g part[g][t*k+j,:]), j ascending, then g ascending.
+struct CombineArgs {
+  const float* part;  // [kg][T*k][H]
+  const int32_t* total_padded;  // 0: an empty grouping (invalid ids), the output is zero
+  int T, k, H, kg;
+  uint16_t* out;      // [T][H]
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+// --- backward pass (bf16) ---
+
+// Load-time relayout of the transposed weights (mode 0: W2^T [E][I rows][H];
+// mode 1: [W1^T | W3^T] [E][H rows][2I]) into the bf16 fragment order.
+struct PreshuffleTArgs {
+  const uint16_t* w1;  // [E][I][H]
+  const uint16_t* w3;  // [E][I][H]
+  const uint16_t* w2;  // [E][H][I]
+  uint16_t* dst;
+  int E, H, I, mode;
+};
+hipError_t launch_preshuffle_t(const PreshuffleTArgs& a, hipStream_t st);
+
+// C[e][m][n] = sum over the rows p of expert e (offset[e] .. offset[e+1]) of
+// A[p][m] B[p][n]; rows m < m_split go to C0 [E][m_split][N], the rest to C1
+// [E][M - m_split][N]. a_mode/b_mode: 0 = the grouped row p; 1 = the token row
+// of its slot (A: times the slot's routing weight).
+struct WgradArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  int a_stride, b_stride;      // elements per row
+  int a_mode, b_mode;
+  int64_t a_bytes, b_bytes;    // buffer sizes (< 2 GiB)
+  int M, N, E, m_split;
+  const int32_t* offset;       // [E+1]
+  const int32_t* sorted_slot;
+  const float* topk_w;
+  int S;
+  uint64_t k_magic;
+  float* C0;
+  float* C1;
+};
+hipError_t launch_wgrad(const WgradArgs& a, hipStream_t st);
+
+// Router gradient and dx (bwd_dl_kernel, bwd_dx_kernel, bwd_router_kernel).
+struct BwdArgs {
+  int T, H, k, E, nparts, kg;
+  const float* dwpart;     // [T*k][nparts]
+  const float* topk_w;     // [T*k]
+  const int32_t* ids;      // [T*k]
+  const float* part;       // [kg][T*k][H] per-slot W1^T dg + W3^T du (kg reduction splits)
+  const uint16_t* w_router;  // bf16 [E][H]
+  const uint16_t* x;       // bf16 [T][H]
+  float* dl;               // [T*k]
+  float* dx;               // [T][H]
+  float* dw_router;        // [E][H]
+  float* dbias;            // [E] or null
+};
+hipError_t launch_bwd_router(const BwdArgs& a, hipStream_t st);
 
 }  // namespace moe

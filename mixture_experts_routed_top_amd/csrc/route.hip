@@ -18,7 +18,8 @@
 //  - large batches (E <= 16): one wave per two tokens (four for H <= 2048),
 //    W_r staged once per workgroup in LDS (batched 16-byte copies), the
 //    experts' logits folded together (fold_many).
-#include "align_device.h"
+#include "moe_device.h"
+#include "moe_launch.h"
 
 namespace moe {
 
@@ -203,29 +204,8 @@ __device__ __forceinline__ void load_row(const uint16_t* xr, int lane, int nchun
                 : make_uint4(0, 0, 0, 0);
 }
 
-// The grouping of the slots (FUSE = 1: one wave, S <= kSmallSlots; FUSE = 2:
-// runs of up to 8 slots on the 256 threads) by the last workgroup to finish,
-// from the ids every workgroup wrote.
-constexpr int kFusedRun = kFusedAlignSlots / 256;
-
-template <int FUSE>
-__device__ __forceinline__ void fused_align(const RouteArgs& a) {
-  __shared__ int last;
-  if (!last_workgroup(a.ticket, gridDim.x, &last)) return;
-  if constexpr (FUSE == 1) {
-    if (threadIdx.x < 64) align_small(a.al, threadIdx.x);
-  } else if constexpr (FUSE == 2) {
-    __shared__ __align__(16) AlignRunsLds<256, kFusedRun> lds;
-    if (a.al.E <= 8)
-      align_runs<4, 256, kFusedRun>(a.al, lds);
-    else
-      align_runs<8, 256, kFusedRun>(a.al, lds);
-  }
-}
-
 // One workgroup per token; wave w computes the logits of experts w, w+4, ...
-// FUSE != 0: the last workgroup then groups the slots (fused_align).
-template <int NCH, int FUSE>
+template <int NCH>
 __global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
   __shared__ float logit[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -245,7 +225,6 @@ __global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
     }
     __syncthreads();
   }
-  if constexpr (FUSE != 0) fused_align<FUSE>(a);
 }
 
 // The fixed fold (p[l] += p[l+off], off = 32 .. 1) of M experts' lane partials
@@ -387,12 +366,7 @@ hipError_t launch_nch(const RouteArgs& a, hipStream_t st) {
                          a);
   } else {
     const int blocks = a.T < 4096 ? a.T : 4096;
-    if (!a.ticket)
-      hipLaunchKernelGGL((route_block_kernel<NCH, 0>), dim3(blocks), dim3(256), 0, st, a);
-    else if (a.al.S <= kSmallSlots)
-      hipLaunchKernelGGL((route_block_kernel<NCH, 1>), dim3(blocks), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((route_block_kernel<NCH, 2>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((route_block_kernel<NCH>), dim3(blocks), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -400,10 +374,6 @@ hipError_t launch_nch(const RouteArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
-  // The grouping runs in the router launch only for the small-batch kernel
-  // (one workgroup per token) and groupings it can hold.
-  if (a.ticket && (a.T >= 1024 || a.al.S > kFusedAlignSlots || a.al.E > 16))
-    return hipErrorInvalidValue;
   const int nch = (a.H / 8 + 63) / 64;  // chunks per lane
   if (nch <= 4) return launch_nch<4>(a, st);
   if (nch <= 8) return launch_nch<8>(a, st);
