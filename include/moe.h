@@ -32,7 +32,8 @@
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers owned by the caller, allocated
  *     with at least the documented size, 16-byte aligned unless noted. The
- *     library never allocates or frees memory and keeps no state between calls.
+ *     library never allocates or frees memory and keeps no state between calls,
+ *     except moe_stage2_noalloc's scratch array (and its address per device).
  *   - Calls are asynchronous and ordered on `stream` (hipStream_t, may be 0).
  *     Nothing is copied back to the host; device-side counts (total_padded)
  *     stay on the device and later kernels read them there.
@@ -246,6 +247,28 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
                       const int32_t* total_padded, const float* topk_w, int T, int k, int E,
                       int H, int I, int block_m, void* out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_stage2_noalloc - moe_stage2 for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. The same launches and results as moe_stage2, bit for bit;
+ * the caller passes the inputs and the output and no workspace: the partials
+ * and the requantised intermediate live in one scratch array of 128 MiB inside
+ * the library (a file-scope device array; every GPU the library runs on holds
+ * its own copy until the process ends). The call allocates and frees nothing.
+ *
+ * Limit: shapes whose moe_stage2_workspace_bytes() exceeds 128 MiB are
+ * rejected with MOE_ERR_WORKSPACE and a message (for the Mixtral shape: every
+ * FP8 decode batch up to T = 256 fits; the T = 8192 prefill does not and takes
+ * moe_stage2 with a workspace). Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (different streams, or host threads without ordering)
+ * race and must not be issued. Arguments and errors otherwise as moe_stage2.
+ */
+moe_status moe_stage2_noalloc(moe_dtype dt, const void* act, const float* act_amax,
+                              const void* w2, const void* s2, const int32_t* sorted_slot,
+                              const int32_t* tile_expert, const int32_t* total_padded,
+                              const float* topk_w, int T, int k, int E, int H, int I,
+                              int block_m, void* out, hipStream_t stream);
 
 /*
  * Backward pass of the bf16 layer: the custom VJP the talk summary names as

@@ -27,6 +27,8 @@ SIGNATURES = {
     "moe_stage2_workspace_bytes": (_I64, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_stage2": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P,
                         _SZ, _P]),
+    "moe_stage2_noalloc": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                _P, _P]),
     "moe_backward_preshuffle_bytes": (_I64, [_I, _I, _I, _I]),
     "moe_backward_preshuffle": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_backward_workspace_bytes": (_I64, [_I, _I, _I, _I, _I, _I]),

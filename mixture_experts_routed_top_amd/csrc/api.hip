@@ -2,8 +2,14 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "../../include/moe.h"
 #include "moe_launch.h"
+
+// Scratch memory of moe_stage2_noalloc (scratch_address).
+constexpr int64_t kScratchBytes = (int64_t)128 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -83,6 +89,22 @@ moe_status check_stage(int dt, int T, int k, int E, int H, int I, int bm) {
         MOE_ERR_UNSUPPORTED, "no kernel configuration for H=%d I=%d block_m=%d", H, I, bm);
   return ok();
 }
+
+moe_status stage2_run(int dt, const void* act, const float* act_amax, const void* w2,
+                      const void* s2, const int32_t* sorted_slot, const int32_t* tile_expert,
+                      const int32_t* total_padded, const float* topk_w, int T, int k, int E,
+                      int H, int I, int block_m, void* out, char* ws, hipStream_t stream);
+
+// Scratch memory of moe_stage2_noalloc: one file-scope device array (below,
+// outside this namespace), which every GPU the library runs on holds, its own
+// copy, until the process ends. In host code `scratch` only names the symbol:
+// its device address comes from hipGetSymbolAddress, taken once per device
+// with that device current and kept here. Nothing in it must start at zero:
+// every call writes the parts it reads.
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch[kMaxDevices];
+
+moe_status scratch_address(char** out);
 
 }  // namespace
 
@@ -327,11 +349,52 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
   const int64_t need = moe_stage2_workspace_bytes(dt, T, k, E, H, I, block_m);
   CHECK((int64_t)workspace_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu bytes < %lld needed",
         workspace_bytes, (long long)need);
+  return stage2_run(dt, act, act_amax, w2, s2, sorted_slot, tile_expert, total_padded, topk_w, T,
+                    k, E, H, I, block_m, out, (char*)workspace, stream);
+}
 
+moe_status moe_stage2_noalloc(moe_dtype dt, const void* act, const float* act_amax,
+                              const void* w2, const void* s2, const int32_t* sorted_slot,
+                              const int32_t* tile_expert, const int32_t* total_padded,
+                              const float* topk_w, int T, int k, int E, int H, int I,
+                              int block_m, void* out, hipStream_t stream) {
+  moe_status s = check_stage(dt, T, k, E, H, I, block_m);
+  if (s != MOE_OK) return s;
+  if (T == 0) return ok();
+  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = is_mx(dt);
+  CHECK(act && w2 && sorted_slot && tile_expert && total_padded && topk_w && out,
+        MOE_ERR_INVALID_ARG, "null pointer argument");
+  CHECK(!fp8 || (act_amax && s2), MOE_ERR_INVALID_ARG, "FP8 needs act_amax and s2");
+  CHECK(!mx || s2, MOE_ERR_INVALID_ARG, "MXFP8/MXFP4 need s2");
+  CHECK(aligned(act, 16) && aligned(w2, 16) && aligned(out, 8) && aligned(s2, mx ? 4 : 16),
+        MOE_ERR_INVALID_ARG, "act/w2/s2 16-byte, out 8-byte alignment");
+  const int64_t need = moe_stage2_workspace_bytes(dt, T, k, E, H, I, block_m);
+  CHECK(need <= kScratchBytes, MOE_ERR_WORKSPACE,
+        "moe_stage2_noalloc: this shape needs %lld bytes of scratch; the library's scratch "
+        "array holds %lld (use moe_stage2 with a workspace)",
+        (long long)need, (long long)kScratchBytes);
+  char* sp = nullptr;
+  s = scratch_address(&sp);
+  if (s != MOE_OK) return s;
+  return stage2_run(dt, act, act_amax, w2, s2, sorted_slot, tile_expert, total_padded, topk_w, T,
+                    k, E, H, I, block_m, out, sp, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The launches of stage 2 (arguments already checked) on a workspace of
+// moe_stage2_workspace_bytes(): the requantisation pass (FP8, MXFP8, MXFP4),
+// the GEMM, the tail-piece sum and the combine.
+moe_status stage2_run(int dt, const void* act, const float* act_amax, const void* w2,
+                      const void* s2, const int32_t* sorted_slot, const int32_t* tile_expert,
+                      const int32_t* total_padded, const float* topk_w, int T, int k, int E,
+                      int H, int I, int block_m, void* out, char* ws, hipStream_t stream) {
+  const bool fp8 = dt == MOE_FP8_E4M3FN, mx = is_mx(dt);
   const int64_t cap = capacity(T, k, E, block_m);
   auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
   moe::GemmCfg c = moe::stage2_cfg(dt, T, k, E, H, I, block_m);
-  char* ws = (char*)workspace;
   float* part = (float*)ws;
   ws += up((int64_t)c.kg * T * k * H * 4);
   const void* x = act;
@@ -406,6 +469,10 @@ moe_status moe_stage2(moe_dtype dt, const void* act, const float* act_amax, cons
   moe::CombineArgs cb{part, total_padded, T, k, H, c.kg, (uint16_t*)out};
   return hip_status(moe::launch_combine(cb, stream), "moe_stage2 combine launch");
 }
+
+}  // namespace
+
+extern "C" {
 
 // --- backward pass (bf16) ---------------------------------------------------
 
@@ -619,3 +686,26 @@ moe_status moe_backward(const void* x, const void* w_router, const int32_t* topk
 }
 
 }  // extern "C"
+
+namespace {
+
+moe_status scratch_address(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "moe_stage2_noalloc: hipGetDevice");
+  CHECK(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED, "device %d (at most %d devices)",
+        dev, kMaxDevices);
+  char* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "moe_stage2_noalloc: hipGetSymbolAddress");
+    CHECK(q, MOE_ERR_HIP, "moe_stage2_noalloc: null scratch address");
+    p = (char*)q;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return ok();
+}
+
+}  // namespace
