@@ -48,10 +48,14 @@ __device__ __forceinline__ float clamp448(float v) {
 // (Markstein's correction): q0 = RN(x * r) is within one ulp of x / s, the
 // remainder x - s * q0 is exact in one fma, and RN(q0 + rem * r) = RN(x / s)
 // whenever the quotient is a normal number. Smaller quotients encode to a
-// (signed) zero code either way; copysign keeps the sign of a zero x.
+// (signed) zero code either way. The last step is taken negated,
+// -RN(-rem * r - q0): rounding to nearest even is symmetric, so the value is
+// the same, and a zero x (q0 = x, rem = +0) comes out with x's sign, which
+// RN(rem * r + q0) would turn into +0 for x = -0.
 __device__ __forceinline__ float quant_div(float x, float s, float r) {
   const float q0 = x * r;
-  return clamp448(copysignf(fmaf(fmaf(-q0, s, x), r, q0), x));
+  const float rem = fmaf(-q0, s, x);
+  return clamp448(-fmaf(-rem, r, -q0));
 }
 
 // Shared exponent of an MX block with E4M3 elements (OCP Microscaling): the

@@ -17,7 +17,8 @@
 //    once, then wave 0 selects the top-k and quantises the row;
 //  - large batches (E <= 16): one wave per two tokens (four for H <= 2048),
 //    W_r staged once per workgroup in LDS (batched 16-byte copies), the
-//    experts' logits folded together (fold_many).
+//    experts' logits folded together (fold_many); for E <= 8 and H <= 4096,
+//    W_r is staged as fp32 and each wave prefetches its next rows.
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -38,6 +39,47 @@ __device__ __forceinline__ void unpack8(uint4 q, float v[8]) {
 // (value, index) ordering of the top-k: larger value first, then lower index.
 __device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
+}
+
+// Lane exchanges without the LDS crossbar. dpp<CTRL>(v): v from another lane
+// of the same 16-lane row (CTRL: 0xB1 / 0x4E quad permutes = lane ^ 1 / ^ 2,
+// 0x141 / 0x140 half-row / row mirror, 0x128 rotate by 8 = lane ^ 8,
+// 0x101..0x104 shift: lane l reads l + 1..4, 0 where that leaves the row).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Row swaps of two registers: swap32 exchanges the upper 32 lanes of a with the
+// lower 32 lanes of b; swap16 exchanges the odd 16-lane rows of a with the
+// even rows of b. Afterwards lane l of a and of b hold the two values that
+// lanes l and l ^ 32 (l ^ 16) of a held, if l is in the lower half (an even
+// row), and those of b otherwise.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r =
+      __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Largest of a non-negative value over the wave, in every lane: in-row
+// reduction by DPP, then the four row results (max is exact in any order).
+__device__ __forceinline__ float wave_max_nonneg(float m) {
+  m = fmaxf(m, dpp<0xB1>(m));
+  m = fmaxf(m, dpp<0x4E>(m));
+  m = fmaxf(m, dpp<0x141>(m));
+  m = fmaxf(m, dpp<0x140>(m));
+  const int i = __float_as_int(m);
+  const int r0 = __builtin_amdgcn_readlane(i, 0), r1 = __builtin_amdgcn_readlane(i, 16);
+  const int r2 = __builtin_amdgcn_readlane(i, 32), r3 = __builtin_amdgcn_readlane(i, 48);
+  // non-negative floats order like their bit patterns
+  return __int_as_float(max(max(r0, r1), max(r2, r3)));
 }
 
 // This lane's partial of one logit: its chunks in ascending order, products
@@ -117,22 +159,12 @@ __device__ __forceinline__ void select_topk(const RouteArgs& a, int t, int lane,
 }
 
 // Per-token FP8 quantisation from the row chunks held in registers:
-// s = amax/448 (1 if zero), code = e4m3fn(clamp(x/s)), fp32 divide.
+// s = amax/448 (1 if zero), code = e4m3fn(clamp(x/s)), fp32 divide. lane_amax
+// is this lane's largest |x| over its chunks; the row maximum is its fold.
 template <int NCH>
-__device__ __forceinline__ void quantise_row(const RouteArgs& a, int t, int lane, int nchunk,
-                                             const uint4 (&xv)[NCH]) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    if (lane + 64 * i < nchunk) {
-      float xf[8];
-      unpack8(xv[i], xf);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(xf[j]));
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+__device__ __forceinline__ void quantise_row_amax(const RouteArgs& a, int t, int lane, int nchunk,
+                                                  const uint4 (&xv)[NCH], float lane_amax) {
+  const float amax = wave_max_nonneg(lane_amax);
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   if (lane == 0) a.x_scale[t] = s;
   // Correctly rounded x / s from one reciprocal per row (quant_div).
@@ -152,6 +184,22 @@ __device__ __forceinline__ void quantise_row(const RouteArgs& a, int t, int lane
   }
 }
 
+template <int NCH>
+__device__ __forceinline__ void quantise_row(const RouteArgs& a, int t, int lane, int nchunk,
+                                             const uint4 (&xv)[NCH]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (lane + 64 * i < nchunk) {
+      float xf[8];
+      unpack8(xv[i], xf);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(xf[j]));
+    }
+  }
+  quantise_row_amax<NCH>(a, t, lane, nchunk, xv, amax);
+}
+
 // MX block quantisation of the token row (MXFP8): each block of 32 values is
 // four consecutive 8-value chunks, held by four adjacent lanes (chunk c on lane
 // c mod 64), so the block maximum is two lane exchanges away. H is a multiple
@@ -169,8 +217,8 @@ __device__ __forceinline__ void quantise_row_mx(const RouteArgs& a, int t, int l
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(xf[j]));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    m = fmaxf(m, dpp<0xB1>(m));  // lane ^ 1
+    m = fmaxf(m, dpp<0x4E>(m));  // lane ^ 2
     const int x = mx_exponent(m);
     const float inv = mx_inv_scale(x);
     if (c < nchunk) {
@@ -194,14 +242,18 @@ __device__ __forceinline__ void quantise(const RouteArgs& a, int t, int lane, in
     quantise_row<NCH>(a, t, lane, nchunk, xv);
 }
 
+// The row's chunks c = lane + 64 i, zero past the row. Every load is issued
+// (from a clamped address) and the zeros are selected afterwards, so the
+// loads are all in flight together instead of one guarded load at a time.
 template <int NCH>
 __device__ __forceinline__ void load_row(const uint16_t* xr, int lane, int nchunk,
                                          uint4 (&xv)[NCH]) {
 #pragma unroll
-  for (int i = 0; i < NCH; ++i)
-    xv[i] = lane + 64 * i < nchunk
-                ? *reinterpret_cast<const uint4*>(xr + (size_t)(lane + 64 * i) * 8)
-                : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + (size_t)min(c, nchunk - 1) * 8);
+    xv[i] = c < nchunk ? v : make_uint4(0, 0, 0, 0);
+  }
 }
 
 // One workgroup per token; wave w computes the logits of experts w, w+4, ...
@@ -348,11 +400,241 @@ __global__ __launch_bounds__(256) void route_wave_kernel(RouteArgs a) {
   }
 }
 
+// Large batches with E <= 8 and H <= 4096: W_r staged once per workgroup in
+// LDS as fp32, in two planes (the first and the last four values of every
+// 8-element chunk, so that a wave's 16-byte reads of one plane are contiguous
+// and need no conversion per token), expert e's chunks at a fixed stride of
+// 64 * NCH (so every read address is one register plus an immediate), eight
+// waves per workgroup. Each wave takes TPW tokens per pass and loads the rows
+// of its next pass before computing the current one; its first rows are
+// requested before W_r is staged. The FP8 row maxima are taken in the logit
+// loop from the values unpacked there. The fold and the top-k exchange values
+// through row swaps and DPP moves rather than LDS permutes. Sums, folds, top-k
+// and quantisation are those of the kernels above, bit for bit.
+constexpr int kWideWaves = 8;
+
+template <int NCH, int TPW>
+__device__ __forceinline__ void load_rows(const RouteArgs& a, int t0, int lane, int nchunk,
+                                          uint4 (&xv)[TPW][NCH]) {
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)  // rows past T repeat the last one (not written)
+    load_row<NCH>(a.x + (size_t)min(t0 + u, a.T - 1) * a.H, lane, nchunk, xv[u]);
+}
+
+// fold_many<8> with its exchanges done by row swaps and DPP moves: the steps
+// at distance 32 and 16 are exactly what swap32 / swap16 leave in a register
+// pair (each lane then adds the two values it holds), the step at 8 is a
+// rotate within the row, and the last three steps need the correct sum only
+// in lanes l = 0 mod 8, which read lane l + off. The pairs added are the
+// canonical ones, so each logit is bit-identical to fold64's; expert e's sits
+// in lane fold_lane<8>(e).
+__device__ __forceinline__ float fold8_swaps(float (&v)[8], int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    swap32(v[i], v[4 + i]);
+    v[i] = v[i] + v[4 + i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    swap16(v[i], v[2 + i]);
+    v[i] = v[i] + v[2 + i];
+  }
+  const bool up = (lane & 8) != 0;
+  const float keep = up ? v[1] : v[0], send = up ? v[0] : v[1];
+  float r = keep + dpp<0x128>(send);
+  r = r + dpp<0x104>(r);
+  r = r + dpp<0x102>(r);
+  r = r + dpp<0x101>(r);
+  return r;
+}
+
+// Order-preserving integer key of a finite float (larger value, larger key);
+// -0 is taken as +0 first, so equal values get equal keys. Key 0 is below
+// every finite value's.
+__device__ __forceinline__ unsigned order_key(float v) {
+  const unsigned b = __float_as_uint(v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ unsigned dppu(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, true);
+}
+
+// Largest / smallest over each group of eight lanes (quad permutes, then the
+// half-row mirror, which pairs the two quads of a group).
+__device__ __forceinline__ unsigned max8(unsigned m) {
+  m = max(m, dppu<0xB1>(m));
+  m = max(m, dppu<0x4E>(m));
+  return max(m, dppu<0x141>(m));
+}
+__device__ __forceinline__ unsigned min8(unsigned m) {
+  m = min(m, dppu<0xB1>(m));
+  m = min(m, dppu<0x4E>(m));
+  return min(m, dppu<0x141>(m));
+}
+
+// select_topk for E <= 8 from the folded logits r (expert e's in lane
+// fold_lane<8>(e)): lane e < E takes expert e's logit plus its bias and an
+// integer key of it; each of the k rounds finds the largest key over lanes
+// 0..7, then the lowest lane holding it (the lower index wins a tie), and
+// retires that lane. Lane 0 writes ids and weights, lanes e < E the logits.
+__device__ __forceinline__ void select_topk8(const RouteArgs& a, int t, int lane, float r) {
+  const int E = a.E, k = a.k;
+  float lv = __shfl(r, fold_lane<8>(lane & 7), 64);
+  if (a.bias && lane < E) lv = lv + a.bias[lane];
+  if (a.logits && lane < E) a.logits[(size_t)t * E + lane] = lv;
+  unsigned key = lane < E ? order_key(lv) : 0u;
+  float top_l[8];
+  int top_i[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    const unsigned m = max8(key);
+    const unsigned w = __builtin_amdgcn_readfirstlane(min8(key == m ? (unsigned)lane : 8u));
+    top_i[j] = (int)w;
+    top_l[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), w));
+    if ((unsigned)lane == w) key = 0u;
+  }
+  if (lane == 0) {
+    float num[8], den = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) break;
+      num[j] = expf(top_l[j] - top_l[0]);
+      den += num[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) break;
+      a.topk_ids[(size_t)t * k + j] = top_i[j];
+      a.topk_w[(size_t)t * k + j] = num[j] / den;
+    }
+  }
+}
+
+template <int NCH, int TPW>
+__device__ __forceinline__ void route_rows(const RouteArgs& a, const float4* plo,
+                                           const float4* phi, int t0, int lane, int nchunk,
+                                           const uint4 (&xv)[TPW][NCH]) {
+  float acc[TPW][8], amax[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    amax[u] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
+  }
+  // Experts past E have zero planes: their sums stay +0 and are masked after
+  // the fold, so the expert loop needs no branch and a chunk's eight W_r reads
+  // are issued together. The chunk guard (lanes past the row, only where H is
+  // not a multiple of 512) also keeps each chunk a block of its own, so the
+  // compiler does not hoist every read of the pass (512 values per lane).
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nchunk) {
+      float xf[TPW][8];
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        unpack8(xv[u][i], xf[u]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax[u] = fmaxf(amax[u], fabsf(xf[u][j]));
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float4 lo = plo[e * (64 * NCH) + c], hi = phi[e * (64 * NCH) + c];
+        const float wf[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          float s = acc[u][e];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s = s + xf[u][j] * wf[j];
+          acc[u][e] = s;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = t0 + u;
+    const float r = fold8_swaps(acc[u], lane);
+    if (t < a.T) {
+      select_topk8(a, t, lane, r);
+      if (a.x_q) {
+        if (a.x_mx)
+          quantise_row_mx<NCH>(a, t, lane, nchunk, xv[u]);
+        else
+          quantise_row_amax<NCH>(a, t, lane, nchunk, xv[u], amax[u]);
+      }
+    }
+  }
+}
+
+template <int NCH, int TPW>
+__global__ __launch_bounds__(64 * kWideWaves) void route_wide_kernel(RouteArgs a) {
+  constexpr int kPlane = 8 * NCH * 64;  // chunks of E <= 8 rows of H <= 512 * NCH
+  __shared__ float4 wl[2 * kPlane];
+  const int lane = threadIdx.x & 63;
+  const int nchunk = a.H / 8;
+  const int step = gridDim.x * kWideWaves * TPW;
+  int t0 = (blockIdx.x * kWideWaves + (threadIdx.x >> 6)) * TPW;
+  uint4 xa[TPW][NCH], xb[TPW][NCH];
+  if (t0 < a.T) load_rows<NCH, TPW>(a, t0, lane, nchunk, xa);
+  {
+    // Stage W_r: plane index e * 64 * NCH + c holds chunk c of expert e's row
+    // (the first four values in the low plane, the last four in the high
+    // one), zero for c >= H/8 or e >= E; NCH 16-byte loads per thread.
+    const uint4* src = reinterpret_cast<const uint4*>(a.w_router);
+    uint4 tmp[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int at = threadIdx.x + 64 * kWideWaves * i;  // < kPlane
+      const int e = at / (64 * NCH), c = at % (64 * NCH);
+      tmp[i] = e < a.E && c < nchunk ? src[e * nchunk + c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int at = threadIdx.x + 64 * kWideWaves * i;
+      float f[8];
+      unpack8(tmp[i], f);
+      wl[at] = make_float4(f[0], f[1], f[2], f[3]);
+      wl[kPlane + at] = make_float4(f[4], f[5], f[6], f[7]);
+    }
+    __syncthreads();
+  }
+  const float4* plo = wl;
+  const float4* phi = wl + kPlane;
+  while (t0 < a.T) {  // wave-uniform: t0 is the same for all lanes of a wave
+    const int t1 = t0 + step;
+    if (t1 < a.T) load_rows<NCH, TPW>(a, t1, lane, nchunk, xb);
+    route_rows<NCH, TPW>(a, plo, phi, t0, lane, nchunk, xa);
+    if (t1 >= a.T) break;
+    const int t2 = t1 + step;
+    if (t2 < a.T) load_rows<NCH, TPW>(a, t2, lane, nchunk, xa);
+    route_rows<NCH, TPW>(a, plo, phi, t1, lane, nchunk, xb);
+    t0 = t2;
+  }
+}
+
 namespace {
 
 template <int NCH>
 hipError_t launch_nch(const RouteArgs& a, hipStream_t st) {
   const size_t wbytes = (size_t)a.E * a.H * 2;
+  if constexpr (NCH <= 8) {
+    if (a.T >= 1024 && a.E <= 8) {
+      // One workgroup per CU (128 KiB of LDS at H = 4096), two per CU below;
+      // one token per wave and pass (more, shorter passes overlap the row
+      // loads with the arithmetic better than two tokens per pass).
+      constexpr int TPW = 1;
+      const int cap = NCH <= 4 ? 512 : 256;
+      int blocks = (a.T + kWideWaves * TPW - 1) / (kWideWaves * TPW);
+      if (blocks > cap) blocks = cap;
+      hipLaunchKernelGGL((route_wide_kernel<NCH, TPW>), dim3(blocks), dim3(64 * kWideWaves), 0,
+                         st, a);
+      return hipGetLastError();
+    }
+  }
   if (a.T >= 1024 && a.E <= 16 && wbytes <= (size_t)kRouteLdsBytes) {
     // W_r fits in LDS: TPW tokens per wave per pass, two workgroups per CU
     // (the LDS limit), so at most 512 workgroups each staging W_r once.

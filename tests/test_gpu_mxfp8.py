@@ -19,9 +19,10 @@ def bf16_bits(a):
         torch.int16).numpy().view(np.uint16)
 
 
-def test_route_mx_codes_bitexact():
+@pytest.mark.parametrize("T", [300, 1100])  # one workgroup per token; eight waves per CU
+def test_route_mx_codes_bitexact(T):
     rng = np.random.default_rng(21)
-    T, H, E = 300, 4096, 8
+    H, E = 4096, 8
     x = rng.standard_normal((T, H)).astype(np.float32)
     x[1] *= 1e-3
     x[2] *= 300.0
