@@ -506,7 +506,7 @@ namespace {
 // dl fp32 [T*k]; part fp32 [kg][T*k][H]; tail pieces (prefill sizes).
 struct BwdLayout {
   moe::GemmCfg c1, cz, c3;  // recompute (stage 1), z (stage 1 over W2^T), dx (stage 2)
-  int64_t gu, dgu, dwpart, dl, part, tail, bytes;
+  int64_t gu, dgu, dwpart, dl, part, tail, rpart, bytes;
 };
 
 BwdLayout bwd_layout(int T, int k, int E, int H, int I, int bm) {
@@ -532,6 +532,8 @@ BwdLayout bwd_layout(int T, int k, int E, int H, int I, int bm) {
     L.tail = o;
     o += up((int64_t)moe::kTailPieces * 32 * L.c3.mt * L.c3.wg_n * 4);
   }
+  L.rpart = o;
+  o += up((cap / bm) * (int64_t)(H + 1) * 4);
   L.bytes = o;
   return L;
 }
@@ -667,7 +669,8 @@ moe_status moe_backward(const void* x, const void* w_router, const int32_t* topk
   {
     moe::BwdArgs b{T, H, k, E, I / L.cz.wg_n, L.c3.kg, dwpart, topk_w, topk_ids, part,
                    (const uint16_t*)w_router, (const uint16_t*)x, (float*)(ws + L.dl), dx,
-                   dw_router, dbias};
+                   dw_router, dbias, sorted_slot, expert_offset, total_padded, block_m,
+                   (int)(cap / block_m), k_magic(k), (float*)(ws + L.rpart)};
     hipError_t err = moe::launch_bwd_router(b, stream);
     if (err != hipSuccess) return hip_status(err, "moe_backward router-gradient launch");
   }

@@ -10,7 +10,8 @@
 //   part_s = W1^T dg + W3^T du         (stage 2 over [W1^T | W3^T], weight 1)
 //   dl    = w (dw - sum_i w_i dw_i),  dw_j = <z_j, a_j>   (bwd_dl_kernel)
 //   dx_t  = sum_j part_{t,j} + sum_j dl_j W_r[e_j]        (bwd_dx_kernel)
-//   dW_r[e], db[e] = sums over the slots of e of dl x_t, dl (bwd_router_kernel)
+//   dW_r[e], db[e] = sums over the slots of e of dl x_t, dl (per tile of
+//                    grouped rows, then over the tiles: bwd_router_*_kernel)
 //   dW2[e]  = sum_p (w dout_t) a_p^T,  dW1|dW3[e] = sum_p [dg|du]_p x_t^T
 //                                       (wgrad_kernel: reductions over the rows
 //                                        of each expert's group)
@@ -121,6 +122,20 @@ __device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]
   }
 }
 
+// Column c of an 8x8 bf16 block as one 16-byte row (one output of transpose8).
+__device__ __forceinline__ uint4 transpose8_col(const uint4 (&in)[8], int c) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 r0 = in[2 * j], r1 = in[2 * j + 1];
+    const uint32_t lo = (c / 2 == 0) ? r0.x : (c / 2 == 1) ? r0.y : (c / 2 == 2) ? r0.z : r0.w;
+    const uint32_t hi = (c / 2 == 0) ? r1.x : (c / 2 == 1) ? r1.y : (c / 2 == 2) ? r1.z : r1.w;
+    o[j] = (c & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                   : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a) {
   __shared__ __align__(16) uint8_t lds[2][2][kWgLdsHalf];  // [buffer][A, B]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -227,7 +242,149 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a) {
     }
 }
 
+// The same reduction in 256 x 256 workgroup tiles (M and N multiples of 256):
+// eight waves of 128 (m) x 64 (n), one 8x8 block per thread and 64-row step
+// (threads 0..255 operand A, 256..511 operand B), 128 KiB of LDS (one
+// workgroup per CU). The grouped rows' slots are read two steps ahead and
+// their data one step ahead, and A's routing weights (a_mode 1) are applied
+// when the block goes to LDS, so no load waits on another inside a step. The tile order keeps the operand panels in
+// L2: each XCD takes one contiguous run of logical tiles (xcd_remap), and
+// within an expert the tiles go in groups of four m-tiles with m fastest, so
+// that the 32 workgroups an XCD runs at once read four A panels and eight B
+// panels, row step by row step.
+constexpr int kWg2Tile = 256;
+constexpr int kWg2Half = kWg2Tile * kWgRows * 2;  // one operand of one buffer, bytes
+constexpr int kWg2GroupM = 4;
+
+__global__ __launch_bounds__(512) void wgrad256_kernel(WgradArgs a) {
+  __shared__ __align__(16) uint8_t lds[2][2][kWg2Half];  // [buffer][A, B]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int mtiles = a.M / kWg2Tile, ntiles = a.N / kWg2Tile;
+  const int per_e = mtiles * ntiles;
+  const int L = xcd_remap(blockIdx.x, a.E * per_e);
+  const int e = L / per_e, r = L % per_e;
+  const int g = r / (kWg2GroupM * ntiles), rg = r % (kWg2GroupM * ntiles);
+  const int gm = min(kWg2GroupM, mtiles - g * kWg2GroupM);
+  const int mt = g * kWg2GroupM + rg % gm, nt = rg / gm;
+  const int r0 = a.offset[e], r1 = a.offset[e + 1];
+  const int S = a.S;
+
+  const bool isB = tid >= 256;
+  const int bt = tid & 255;
+  const int cblk = bt % 32, rblk = bt / 32;  // 32 column blocks x 8 row blocks
+  const int stride = isB ? a.b_stride : a.a_stride;
+  const int mode = isB ? a.b_mode : a.a_mode;
+  const bool weighted = !isB && a.a_mode == 1;
+  const int col0 = (isB ? nt : mt) * kWg2Tile + cblk * 8;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(isB ? a.B : a.A), (short)0, (int)(isB ? a.b_bytes : a.a_bytes), 0x00020000);
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  uint4 blk[8];
+  float wq[8];
+  int sl[8];
+  // Row p = r0 + c*64 + rblk*8 + q. Its slot is read a step before its data
+  // (load_slots, then load_rows), so the data loads do not wait on the index
+  // loads; rows past the group and pad rows read as zero (weight 0 in a_mode 1).
+  auto load_slots = [&](int c) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int p = r0 + c * kWgRows + rblk * 8 + q;
+      sl[q] = p < r1 ? a.sorted_slot[p] : S;
+    }
+  };
+  auto load_rows = [&](int c) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int p = r0 + c * kWgRows + rblk * 8 + q;
+      const int slot = sl[q];
+      const uint32_t row = mode == 0 ? (uint32_t)p : div_k(min(slot, S - 1), a.k_magic);
+      const uint32_t off = slot < S ? (row * (uint32_t)stride + (uint32_t)col0) * 2u : 0x80000000u;
+      blk[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+      if (weighted) wq[q] = slot < S ? a.topk_w[slot] : 0.0f;
+    }
+  };
+  auto store = [&](int buf) {
+    if (weighted) {  // dout row times the routing weight, back to bf16
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        uint32_t x[4] = {blk[q].x, blk[q].y, blk[q].z, blk[q].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          x[h] = f32x2_to_bf16x2(bf16_bits_to_f32(x[h] & 0xffffu) * wq[q],
+                                 bf16_bits_to_f32(x[h] >> 16) * wq[q]);
+        blk[q] = make_uint4(x[0], x[1], x[2], x[3]);
+      }
+    }
+    uint8_t* base = lds[buf][isB ? 1 : 0];
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)  // column cc of the block = row cc of the transpose
+      *reinterpret_cast<uint4*>(base + wg_swz(cblk * 8 + cc, rblk)) = transpose8_col(blk, cc);
+  };
+
+  const int nsteps = (r1 - r0 + kWgRows - 1) / kWgRows;
+  if (nsteps > 0) {
+    load_slots(0);
+    load_rows(0);
+    if (nsteps > 1) load_slots(1);
+    store(0);
+  }
+  __syncthreads();
+  for (int c = 0; c < nsteps; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nsteps) load_rows(c + 1);
+    if (c + 2 < nsteps) load_slots(c + 2);
+    const uint8_t* At = lds[buf][0];
+    const uint8_t* Bt = lds[buf][1];
+#pragma unroll
+    for (int ks = 0; ks < kWgRows / 16; ++ks) {
+      const int cg = ks * 2 + (lane >> 5);
+      bf16x8 av[4], bv[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        av[i] = *reinterpret_cast<const bf16x8*>(At + wg_swz(wm * 128 + i * 32 + (lane & 31), cg));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bv[j] = *reinterpret_cast<const bf16x8*>(Bt + wg_swz(wn * 64 + j * 32 + (lane & 31), cg));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+    if (c + 1 < nsteps) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // acc[i][j][q]: m = wm*128 + i*32 + 8*(q/4) + 4*(lane/32) + q%4, n = wn*64 + j*32 + lane%32
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int m = mt * kWg2Tile + wm * 128 + i * 32 + 8 * (q / 4) + 4 * (lane >> 5) + (q & 3);
+      float* crow = m < a.m_split
+                        ? a.C0 + (int64_t)e * a.m_split * a.N + (int64_t)m * a.N
+                        : a.C1 + (int64_t)e * (a.M - a.m_split) * a.N +
+                              (int64_t)(m - a.m_split) * a.N;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) crow[nt * kWg2Tile + wn * 64 + j * 32 + (lane & 31)] = acc[i][j][q];
+    }
+}
+
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t st) {
+  if (a.M % kWg2Tile == 0 && a.N % kWg2Tile == 0) {
+    const int64_t blocks = (int64_t)a.E * (a.M / kWg2Tile) * (a.N / kWg2Tile);
+    hipLaunchKernelGGL(wgrad256_kernel, dim3((unsigned)blocks), dim3(512), 0, st, a);
+    return hipGetLastError();
+  }
   if (a.M % kWgTile || a.N % kWgTile) return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)a.E * (a.M / kWgTile) * (a.N / kWgTile);
   hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
@@ -284,21 +441,51 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdArgs a) {
   }
 }
 
-// dW_r[e][h] = sum over tokens t (ascending) and ranks j with ids[t][j] == e
-// of dl[t*k+j] x[t][h]; db[e] the same sum of dl. Block (e, 256 columns).
-__global__ __launch_bounds__(256) void bwd_router_kernel(BwdArgs a) {
+// dW_r[e][h] = sum over the slots s of expert e of dl[s] x[s/k][h], db[e] the
+// same sum of dl: first one partial per tile of block_m grouped rows (rows in
+// ascending order; a tile holds one expert's rows), then, per expert, its
+// tiles' partials in ascending order. Partial block: (tile, 512 columns), two
+// columns per thread.
+constexpr int kRouterCols = 512;
+
+__global__ __launch_bounds__(256) void bwd_router_part_kernel(BwdArgs a) {
+  const int tile = blockIdx.x;
+  const int p0 = tile * a.bm;
+  if (p0 >= a.total[0]) return;
+  const int h = blockIdx.y * kRouterCols + 2 * threadIdx.x;
+  const int S = a.T * a.k;
+  float acc0 = 0.0f, acc1 = 0.0f, bacc = 0.0f;
+  for (int p = p0; p < p0 + a.bm; ++p) {
+    const int slot = a.sorted_slot[p];
+    if ((unsigned)slot >= (unsigned)S) continue;  // pad row
+    const float d = a.dl[slot];
+    bacc = bacc + d;
+    if (h < a.H) {
+      const uint32_t xv = *reinterpret_cast<const uint32_t*>(
+          a.x + (size_t)div_k((uint32_t)slot, a.k_magic) * a.H + h);
+      acc0 = fmaf(d, bf16_bits_to_f32(xv & 0xffffu), acc0);
+      acc1 = fmaf(d, bf16_bits_to_f32(xv >> 16), acc1);
+    }
+  }
+  if (h < a.H)
+    *reinterpret_cast<float2*>(a.rpart + (size_t)tile * a.H + h) = make_float2(acc0, acc1);
+  if (blockIdx.y == 0 && threadIdx.x == 0) a.rpart[(size_t)a.ntiles * a.H + tile] = bacc;
+}
+
+__global__ __launch_bounds__(256) void bwd_router_sum_kernel(BwdArgs a) {
   const int e = blockIdx.y;
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  float acc = 0.0f, bacc = 0.0f;
-  for (int t = 0; t < a.T; ++t)
-    for (int j = 0; j < a.k; ++j) {
-      if (a.ids[t * a.k + j] != e) continue;
-      const float d = a.dl[t * a.k + j];
-      if (h < a.H) acc = fmaf(d, bf16_bits_to_f32(a.x[(size_t)t * a.H + h]), acc);
-      bacc = bacc + d;
-    }
-  if (h < a.H) a.dw_router[(size_t)e * a.H + h] = acc;
-  if (h == 0 && a.dbias) a.dbias[e] = bacc;
+  const int tb = a.offset[e] / a.bm, te = a.offset[e + 1] / a.bm;
+  if (h < a.H) {
+    float acc = 0.0f;
+    for (int t = tb; t < te; ++t) acc = acc + a.rpart[(size_t)t * a.H + h];
+    a.dw_router[(size_t)e * a.H + h] = acc;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && a.dbias) {
+    float b = 0.0f;
+    for (int t = tb; t < te; ++t) b = b + a.rpart[(size_t)a.ntiles * a.H + t];
+    a.dbias[e] = b;
+  }
 }
 
 hipError_t launch_bwd_router(const BwdArgs& a, hipStream_t st) {
@@ -310,7 +497,11 @@ hipError_t launch_bwd_router(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_router_kernel, dim3((a.H + 255) / 256, a.E), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_router_part_kernel, dim3(a.ntiles, (a.H + kRouterCols - 1) / kRouterCols),
+                     dim3(256), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_router_sum_kernel, dim3((a.H + 255) / 256, a.E), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -209,6 +209,12 @@ struct BwdArgs {
   float* dx;               // [T][H]
   float* dw_router;        // [E][H]
   float* dbias;            // [E] or null
+  const int32_t* sorted_slot;  // [capacity] grouped rows (slot, or T*k for a pad row)
+  const int32_t* offset;   // [E+1] padded row offset of each expert's group
+  const int32_t* total;    // [1] padded rows in use
+  int bm, ntiles;          // rows per tile (block_m); tiles of the capacity
+  uint64_t k_magic;        // ceil(2^35 / k): slot / k as a multiply (div_k)
+  float* rpart;            // [ntiles][H] router-gradient partials, then [ntiles] bias partials
 };
 hipError_t launch_bwd_router(const BwdArgs& a, hipStream_t st);
 
