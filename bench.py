@@ -26,6 +26,9 @@ The same line carries:
   mxfp4         the layer with MXFP4 (E2M1) expert weights and MXFP8 tokens: prefill
                 T=8192 and the decode sweep T = 1 .. 256, weight GB/s over the
                 active experts' codes and scales;
+  backward      the bf16 layer's backward pass (moe_backward) at the Mixtral shape and
+                T=8192: ms per call and TFLOP/s (12*H*I flops per token-slot), with
+                the bf16 forward on the same batch timed beside it;
   cpu_baseline  the CPU oracle on the first tokens of the same workload; per_workload
                 holds its wall time (oracle_s, cores) on up to 16 tokens of each of the
                 other workloads (the tiny layer, the BF16 decode batch, each FP8 decode
@@ -37,6 +40,7 @@ The same line carries:
     python bench.py --decode-only T [--decode-runs N]   (one FP8 decode batch)
     python bench.py --mxfp8-only [--steps K]           (the MXFP8 lines only)
     python bench.py --mxfp4-only [--steps K]           (the MXFP4 lines only)
+    python bench.py --backward-only [--steps K]        (the bf16 backward line only)
     python bench.py --traffic-from FETCH.db WRITE.db   (writes the traffic summary)
 """
 from __future__ import annotations
@@ -260,6 +264,62 @@ def skewed(steps, oracle_tokens=0):
             "pad_fraction": round((total - wl.slots) / total, 4)}
 
 
+def backward_line(steps, T=8192):
+    """The bf16 layer's backward pass (moe_backward: gradients of x, W1, W3, W2, the router
+    weights and the router bias, the top-k selection held fixed) at the Mixtral shape on a
+    prefill batch of T tokens, with the forward timed beside it. Weights and router are the
+    bf16 decode workload's (seed 1), x its generator's draw for T tokens, dout seeded normals.
+    TFLOP/s count 6*H*I flops per token-slot for the forward and 12*H*I for the backward."""
+    import torch
+    import mixture_experts_routed_top_amd as moe
+    import workloads
+    wl = workloads.scaled(workloads.config(1), name=f"mixtral-bf16-T{T}", T=T)
+    log(f"[bench] generating {wl.name} (backward)")
+    inp = workloads.generate(wl, threads=16)
+    w1, w3, w2 = dev(inp.w1), dev(inp.w3), dev(inp.w2)
+    layer = moe.Layer("bf16", dev(inp.w_router), w1, w3, w2, None, None, None, None, wl.k, T)
+    w2t, w13t = moe.preshuffle_backward(w1, w3, w2)
+    del w1, w3, w2
+    x = dev(inp.x)
+    dout = dev(workloads.to_bf16_bits(
+        np.random.default_rng(7).standard_normal((T, wl.H)).astype(np.float32)))
+
+    def bw():
+        return moe.backward(x, layer.w_router, layer.ids, layer.w, layer.grp, layer.act,
+                            layer.pw, w2t, w13t, dout)
+
+    layer(x)
+    for _ in range(2):
+        g = bw()
+    torch.cuda.synchronize()
+    del g
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        layer(x)
+    t1.record()
+    torch.cuda.synchronize()
+    fwd = t0.elapsed_time(t1) / steps
+    t0.record()
+    for _ in range(steps):
+        bw()
+    t1.record()
+    torch.cuda.synchronize()
+    bwd = t0.elapsed_time(t1) / steps
+    fl = wl.flops()
+    log(f"[bench] {wl.name}: forward {fwd:.3f} ms, backward {bwd:.3f} ms")
+    out = {"workload": wl.name, "T": T, "block_m": layer.bm,
+           "forward_ms": round(fwd, 4), "forward_tflops": round(fl / (fwd * 1e-3) / 1e12, 2),
+           "backward_ms": round(bwd, 4),
+           "backward_tflops": round(2 * fl / (bwd * 1e-3) / 1e12, 2),
+           "backward_frac_of_bf16_peak": round(2 * fl / (bwd * 1e-3) / 1e12 / PEAK["bf16"], 4),
+           "tokens_per_s_forward_backward": round(T / ((fwd + bwd) * 1e-3), 1)}
+    del layer, w2t, w13t, x, dout
+    torch.cuda.empty_cache()
+    return out
+
+
 def timed_steps(layer, x, steps):
     """Mean whole-layer ms over `steps` back-to-back calls and the mean stage-1 kernel ms
     (HIP events on the stream the stages run on)."""
@@ -375,6 +435,8 @@ def main():
                     help="only the MXFP8 prefill and decode lines (for profiler runs)")
     ap.add_argument("--mxfp4-only", action="store_true",
                     help="only the MXFP4 prefill and decode lines (for profiler runs)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the bf16 backward line at T=8192 (for profiler runs)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
@@ -392,6 +454,9 @@ def main():
         return
     if args.mxfp4_only:
         print(json.dumps({"mxfp4": mxfp4(args.steps, args.decode_runs)}), flush=True)
+        return
+    if args.backward_only:
+        print(json.dumps({"backward": backward_line(args.steps)}), flush=True)
         return
 
     if args.decode_only is not None:
@@ -467,6 +532,7 @@ def main():
         rec["skewed"] = skewed(max(5, args.steps // 2), ot)
         rec["mxfp8"] = mxfp8(max(5, args.steps // 2), args.decode_runs)
         rec["mxfp4"] = mxfp4(max(5, args.steps // 2), args.decode_runs)
+        rec["backward"] = backward_line(max(5, args.steps // 2))
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
