@@ -247,11 +247,13 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a) {
 // (threads 0..255 operand A, 256..511 operand B), 128 KiB of LDS (one
 // workgroup per CU). The grouped rows' slots are read two steps ahead and
 // their data one step ahead, and A's routing weights (a_mode 1) are applied
-// when the block goes to LDS, so no load waits on another inside a step. The tile order keeps the operand panels in
-// L2: each XCD takes one contiguous run of logical tiles (xcd_remap), and
-// within an expert the tiles go in groups of four m-tiles with m fastest, so
-// that the 32 workgroups an XCD runs at once read four A panels and eight B
-// panels, row step by row step.
+// when the block goes to LDS, so no load waits on another inside a step. The
+// tiles go in launch order, which the hardware deals round robin over the 8
+// XCDs: all XCDs work on one expert at a time, whose operand panels (about
+// 140 MB at the Mixtral shape) then fit the 256 MB Infinity Cache behind the
+// L2s; within an expert the tiles go in groups of four m-tiles with m fastest,
+// so that the 32 workgroups an XCD runs at once read four A panels and eight
+// B panels, row step by row step.
 constexpr int kWg2Tile = 256;
 constexpr int kWg2Half = kWg2Tile * kWgRows * 2;  // one operand of one buffer, bytes
 constexpr int kWg2GroupM = 4;
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(512) void wgrad256_kernel(WgradArgs a) {
   const int wm = wave >> 2, wn = wave & 3;
   const int mtiles = a.M / kWg2Tile, ntiles = a.N / kWg2Tile;
   const int per_e = mtiles * ntiles;
-  const int L = xcd_remap(blockIdx.x, a.E * per_e);
+  const int L = blockIdx.x;
   const int e = L / per_e, r = L % per_e;
   const int g = r / (kWg2GroupM * ntiles), rg = r % (kWg2GroupM * ntiles);
   const int gm = min(kWg2GroupM, mtiles - g * kWg2GroupM);
@@ -338,10 +340,23 @@ __global__ __launch_bounds__(512) void wgrad256_kernel(WgradArgs a) {
     store(0);
   }
   __syncthreads();
+  // Rows that are not gathered (operand mode 0) are also touched two steps
+  // ahead, one 128-byte line per thread (row bt / 4, line bt % 4 of the tile's
+  // columns), so that the row loads a step later find them in L2.
+  auto touch = [&](int c) {
+    const int p = r0 + c * kWgRows + bt / 4;
+    const uint32_t off =
+        p < r1 ? ((uint32_t)p * (uint32_t)stride + (uint32_t)(col0 - cblk * 8 + (bt % 4) * 64)) * 2u
+               : 0x80000000u;
+    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
+  };
+  uint32_t touched = 0;
   for (int c = 0; c < nsteps; ++c) {
     const int buf = c & 1;
     if (c + 1 < nsteps) load_rows(c + 1);
     if (c + 2 < nsteps) load_slots(c + 2);
+    const uint32_t prev = touched;
+    if (mode == 0 && c + 2 < nsteps) touched = touch(c + 2);
     const uint8_t* At = lds[buf][0];
     const uint8_t* Bt = lds[buf][1];
 #pragma unroll
@@ -361,6 +376,7 @@ __global__ __launch_bounds__(512) void wgrad256_kernel(WgradArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
     if (c + 1 < nsteps) store(buf ^ 1);
+    asm volatile("" : : "v"(prev));  // the touch of a step ago has arrived; its value is unused
     __syncthreads();
   }
 
