@@ -506,7 +506,7 @@ namespace {
 // dl fp32 [T*k]; part fp32 [kg][T*k][H]; tail pieces (prefill sizes).
 struct BwdLayout {
   moe::GemmCfg c1, cz, c3;  // recompute (stage 1), z (stage 1 over W2^T), dx (stage 2)
-  int64_t gu, dgu, dwpart, dl, part, tail, rpart, bytes;
+  int64_t gu, dgu, dwpart, dl, part, tail, rpart, xg, wdg, bytes;
 };
 
 BwdLayout bwd_layout(int T, int k, int E, int H, int I, int bm) {
@@ -534,6 +534,10 @@ BwdLayout bwd_layout(int T, int k, int E, int H, int I, int bm) {
   }
   L.rpart = o;
   o += up((cap / bm) * (int64_t)(H + 1) * 4);
+  L.xg = o;
+  o += up(cap * H * 2);
+  L.wdg = o;
+  o += up(cap * H * 2);
   L.bytes = o;
   return L;
 }
@@ -674,16 +678,21 @@ moe_status moe_backward(const void* x, const void* w_router, const int32_t* topk
     hipError_t err = moe::launch_bwd_router(b, stream);
     if (err != hipSuccess) return hip_status(err, "moe_backward router-gradient launch");
   }
-  // 5. dW2[e] = sum over e's rows of (w dout) act^T; dW1 | dW3 = sum of [dg | du] x^T.
+  // 5. the token rows of the grouping (x and w dout), pad rows of dg, du zeroed;
+  //    dW2[e] = sum over e's rows of (w dout) act^T; dW1 | dW3 = sum of [dg | du] x^T.
   {
-    moe::WgradArgs w{(const uint16_t*)dout, (const uint16_t*)act, H, I, 1, 0,
-                     (int64_t)T * H * 2, cap * I * 2, H, I, E, H, expert_offset, sorted_slot,
-                     topk_w, S, k_magic(k), dw2, dw2};
-    hipError_t err = moe::launch_wgrad(w, stream);
+    uint16_t* xg = (uint16_t*)(ws + L.xg);
+    uint16_t* wdg = (uint16_t*)(ws + L.wdg);
+    moe::GatherArgs ga{(const uint16_t*)x, (const uint16_t*)dout, topk_w, sorted_slot,
+                       total_padded, H, I, S, (int)cap, k_magic(k), xg, wdg, dgu};
+    hipError_t err = moe::launch_bwd_gather(ga, stream);
+    if (err != hipSuccess) return hip_status(err, "moe_backward gather launch");
+    moe::WgradArgs w{wdg, (const uint16_t*)act, H, I, 0, 0, cap * H * 2, cap * I * 2, H, I, E,
+                     H, expert_offset, sorted_slot, topk_w, S, k_magic(k), dw2, dw2};
+    err = moe::launch_wgrad(w, stream);
     if (err != hipSuccess) return hip_status(err, "moe_backward dW2 launch");
-    moe::WgradArgs w13g{dgu, (const uint16_t*)x, 2 * I, H, 0, 1, cap * 4 * I,
-                        (int64_t)T * H * 2, 2 * I, H, E, I, expert_offset, sorted_slot, topk_w,
-                        S, k_magic(k), dw1, dw3};
+    moe::WgradArgs w13g{dgu, xg, 2 * I, H, 0, 0, cap * 4 * I, cap * H * 2, 2 * I, H, E, I,
+                        expert_offset, sorted_slot, topk_w, S, k_magic(k), dw1, dw3};
     return hip_status(moe::launch_wgrad(w13g, stream), "moe_backward dW1/dW3 launch");
   }
 }

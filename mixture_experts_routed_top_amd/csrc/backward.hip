@@ -122,20 +122,6 @@ __device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]
   }
 }
 
-// Column c of an 8x8 bf16 block as one 16-byte row (one output of transpose8).
-__device__ __forceinline__ uint4 transpose8_col(const uint4 (&in)[8], int c) {
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint4 r0 = in[2 * j], r1 = in[2 * j + 1];
-    const uint32_t lo = (c / 2 == 0) ? r0.x : (c / 2 == 1) ? r0.y : (c / 2 == 2) ? r0.z : r0.w;
-    const uint32_t hi = (c / 2 == 0) ? r1.x : (c / 2 == 1) ? r1.y : (c / 2 == 2) ? r1.z : r1.w;
-    o[j] = (c & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
-                   : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a) {
   __shared__ __align__(16) uint8_t lds[2][2][kWgLdsHalf];  // [buffer][A, B]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -242,24 +228,53 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a) {
     }
 }
 
-// The same reduction in 256 x 256 workgroup tiles (M and N multiples of 256):
-// eight waves of 128 (m) x 64 (n), one 8x8 block per thread and 64-row step
-// (threads 0..255 operand A, 256..511 operand B), 128 KiB of LDS (one
-// workgroup per CU). The grouped rows' slots are read two steps ahead and
-// their data one step ahead, and A's routing weights (a_mode 1) are applied
-// when the block goes to LDS, so no load waits on another inside a step. The
-// tiles go in launch order, which the hardware deals round robin over the 8
-// XCDs: all XCDs work on one expert at a time, whose operand panels (about
-// 140 MB at the Mixtral shape) then fit the 256 MB Infinity Cache behind the
-// L2s; within an expert the tiles go in groups of four m-tiles with m fastest,
-// so that the 32 workgroups an XCD runs at once read four A panels and eight
-// B panels, row step by row step.
+// The same reduction in 256 x 256 workgroup tiles (M and N multiples of 256)
+// for operands whose rows are the grouped rows themselves (a_mode = b_mode =
+// 0: the token rows are gathered beforehand, bwd_gather_kernel). A stage is
+// 32 rows; each thread loads four 16-byte row chunks per stage (a wave loads
+// two whole rows of the tile per instruction), and four stages are in flight
+// in registers. Stages go to LDS row-major, each row's 16-byte chunks
+// XOR-permuted by the row (chunk c at c ^ 4 (row mod 4)), so that the
+// transposing reads below are conflict free; two LDS buffers. The matrix cores
+// take 8 consecutive rows of one column per lane, which ds_read_b64_tr_b16
+// delivers from the row-major tile: in each 16-lane group, lane 4j + q reads 4
+// columns of row j, and lane i receives column i of the 4 rows. Eight waves
+// of 128 (m) x 64 (n); tiles in launch order (the hardware deals them round
+// robin over the XCDs, so all XCDs work on one expert at a time, whose
+// operands then fit the Infinity Cache), in groups of four m-tiles with m
+// fastest.
 constexpr int kWg2Tile = 256;
-constexpr int kWg2Half = kWg2Tile * kWgRows * 2;  // one operand of one buffer, bytes
 constexpr int kWg2GroupM = 4;
+constexpr int kWlRows = 32;                      // rows per stage
+constexpr int kWlHalf = kWlRows * kWg2Tile * 2;  // one operand of one stage, bytes
 
-__global__ __launch_bounds__(512) void wgrad256_kernel(WgradArgs a) {
-  __shared__ __align__(16) uint8_t lds[2][2][kWg2Half];  // [buffer][A, B]
+typedef short wl_v4s __attribute__((ext_vector_type(4)));
+
+// Byte offset of (row, column) in a stage's operand tile.
+__device__ __forceinline__ int wl_addr(int row, int col) {
+  return row * (kWg2Tile * 2) + (((col >> 3) ^ (4 * (row & 3))) << 4) + (col & 7) * 2;
+}
+
+// The matrix-core operand of rows k0 .. k0 + 15 and columns c0 .. c0 + 31 for
+// this lane (column c0 + lane % 32, rows k0 + 8 (lane / 32) + 0..7).
+__device__ __forceinline__ bf16x8 wl_frag(const uint8_t* tile, int k0, int c0, int lane) {
+  const int g = lane >> 4, t = lane & 15;
+  const int row = k0 + 8 * (g >> 1) + (t >> 2);
+  const int col = c0 + 16 * (g & 1) + 4 * (t & 3);
+  typedef __attribute__((address_space(3))) wl_v4s* lds_v4s;
+  const wl_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(tile + wl_addr(row, col)));
+  const wl_v4s hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(tile + wl_addr(row + 4, col)));
+  const wl_v4s v8[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v8);
+}
+
+struct WlStage {
+  uint4 v[4];
+};
+
+__global__ __launch_bounds__(512) void wgrad_lds_kernel(WgradArgs a) {
+  __shared__ __align__(16) uint8_t lds[2][2][kWlHalf];  // [buffer][A, B]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int mtiles = a.M / kWg2Tile, ntiles = a.N / kWg2Tile;
@@ -270,17 +285,34 @@ __global__ __launch_bounds__(512) void wgrad256_kernel(WgradArgs a) {
   const int gm = min(kWg2GroupM, mtiles - g * kWg2GroupM);
   const int mt = g * kWg2GroupM + rg % gm, nt = rg / gm;
   const int r0 = a.offset[e], r1 = a.offset[e + 1];
-  const int S = a.S;
 
-  const bool isB = tid >= 256;
-  const int bt = tid & 255;
-  const int cblk = bt % 32, rblk = bt / 32;  // 32 column blocks x 8 row blocks
-  const int stride = isB ? a.b_stride : a.a_stride;
-  const int mode = isB ? a.b_mode : a.a_mode;
-  const bool weighted = !isB && a.a_mode == 1;
-  const int col0 = (isB ? nt : mt) * kWg2Tile + cblk * 8;
+  // Loader role: threads 0..255 operand A, 256..511 operand B; chunk t + 256 u
+  // (u = 0..3) of the stage's 32 rows x 32 chunks: row (t + 256 u) / 32,
+  // chunk position t % 32.
+  const int opnd = tid >> 8;
+  const int t = tid & 255;
+  const int stride = opnd ? a.b_stride : a.a_stride;
+  const int colbase = (opnd ? nt : mt) * kWg2Tile + (t & 31) * 8;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(isB ? a.B : a.A), (short)0, (int)(isB ? a.b_bytes : a.a_bytes), 0x00020000);
+      (void*)(opnd ? a.B : a.A), (short)0, (int)(opnd ? a.b_bytes : a.a_bytes), 0x00020000);
+  auto load = [&](int s, WlStage& R) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = (t >> 5) + 8 * u;
+      const int p = r0 + s * kWlRows + row;
+      const uint32_t off =
+          p < r1 ? ((uint32_t)p * (uint32_t)stride + (uint32_t)colbase) * 2u : 0x80000000u;
+      R.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+    }
+  };
+  auto store = [&](int buf, const WlStage& R) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = (t >> 5) + 8 * u;
+      *reinterpret_cast<uint4*>(lds[buf][opnd] + row * (kWg2Tile * 2) +
+                                (((t & 31) ^ (4 * (row & 3))) << 4)) = R.v[u];
+    }
+  };
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -290,93 +322,52 @@ __global__ __launch_bounds__(512) void wgrad256_kernel(WgradArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  uint4 blk[8];
-  float wq[8];
-  int sl[8];
-  // Row p = r0 + c*64 + rblk*8 + q. Its slot is read a step before its data
-  // (load_slots, then load_rows), so the data loads do not wait on the index
-  // loads; rows past the group and pad rows read as zero (weight 0 in a_mode 1).
-  auto load_slots = [&](int c) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int p = r0 + c * kWgRows + rblk * 8 + q;
-      sl[q] = p < r1 ? a.sorted_slot[p] : S;
-    }
-  };
-  auto load_rows = [&](int c) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int p = r0 + c * kWgRows + rblk * 8 + q;
-      const int slot = sl[q];
-      const uint32_t row = mode == 0 ? (uint32_t)p : div_k(min(slot, S - 1), a.k_magic);
-      const uint32_t off = slot < S ? (row * (uint32_t)stride + (uint32_t)col0) * 2u : 0x80000000u;
-      blk[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
-      if (weighted) wq[q] = slot < S ? a.topk_w[slot] : 0.0f;
-    }
-  };
-  auto store = [&](int buf) {
-    if (weighted) {  // dout row times the routing weight, back to bf16
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        uint32_t x[4] = {blk[q].x, blk[q].y, blk[q].z, blk[q].w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          x[h] = f32x2_to_bf16x2(bf16_bits_to_f32(x[h] & 0xffffu) * wq[q],
-                                 bf16_bits_to_f32(x[h] >> 16) * wq[q]);
-        blk[q] = make_uint4(x[0], x[1], x[2], x[3]);
-      }
-    }
-    uint8_t* base = lds[buf][isB ? 1 : 0];
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc)  // column cc of the block = row cc of the transpose
-      *reinterpret_cast<uint4*>(base + wg_swz(cblk * 8 + cc, rblk)) = transpose8_col(blk, cc);
-  };
-
-  const int nsteps = (r1 - r0 + kWgRows - 1) / kWgRows;
-  if (nsteps > 0) {
-    load_slots(0);
-    load_rows(0);
-    if (nsteps > 1) load_slots(1);
-    store(0);
-  }
-  __syncthreads();
-  // Rows that are not gathered (operand mode 0) are also touched two steps
-  // ahead, one 128-byte line per thread (row bt / 4, line bt % 4 of the tile's
-  // columns), so that the row loads a step later find them in L2.
-  auto touch = [&](int c) {
-    const int p = r0 + c * kWgRows + bt / 4;
-    const uint32_t off =
-        p < r1 ? ((uint32_t)p * (uint32_t)stride + (uint32_t)(col0 - cblk * 8 + (bt % 4) * 64)) * 2u
-               : 0x80000000u;
-    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
-  };
-  uint32_t touched = 0;
-  for (int c = 0; c < nsteps; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nsteps) load_rows(c + 1);
-    if (c + 2 < nsteps) load_slots(c + 2);
-    const uint32_t prev = touched;
-    if (mode == 0 && c + 2 < nsteps) touched = touch(c + 2);
+  auto compute = [&](int buf) {
     const uint8_t* At = lds[buf][0];
     const uint8_t* Bt = lds[buf][1];
 #pragma unroll
-    for (int ks = 0; ks < kWgRows / 16; ++ks) {
-      const int cg = ks * 2 + (lane >> 5);
+    for (int ks = 0; ks < kWlRows / 16; ++ks) {
       bf16x8 av[4], bv[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(At + wg_swz(wm * 128 + i * 32 + (lane & 31), cg));
+      for (int i = 0; i < 4; ++i) av[i] = wl_frag(At, ks * 16, wm * 128 + i * 32, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bv[j] = *reinterpret_cast<const bf16x8*>(Bt + wg_swz(wn * 64 + j * 32 + (lane & 31), cg));
+      for (int j = 0; j < 2; ++j) bv[j] = wl_frag(Bt, ks * 16, wn * 64 + j * 32, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
-    if (c + 1 < nsteps) store(buf ^ 1);
-    asm volatile("" : : "v"(prev));  // the touch of a step ago has arrived; its value is unused
+  };
+
+  // Stage s is computed from LDS buffer s % 2. Register stage s % 4 receives
+  // stage s three steps before, and is written to LDS at the end of step
+  // s - 1, behind the barrier that follows the last step reading that buffer.
+  // The guards (not breaks) keep the four register stages in registers; the
+  // barriers run on every path (n is the same for the whole workgroup).
+  const int n = (r1 - r0 + kWlRows - 1) / kWlRows;
+  WlStage R0, R1, R2, R3;
+  if (n > 0) load(0, R0);
+  if (n > 1) load(1, R1);
+  if (n > 2) load(2, R2);
+  if (n > 0) store(0, R0);
+  __syncthreads();
+  for (int c = 0; c < n; c += 4) {
+    if (c + 3 < n) load(c + 3, R3);
+    compute(0);
+    if (c + 1 < n) store(1, R1);
+    __syncthreads();
+    if (c + 4 < n) load(c + 4, R0);
+    if (c + 1 < n) compute(1);
+    if (c + 2 < n) store(0, R2);
+    __syncthreads();
+    if (c + 5 < n) load(c + 5, R1);
+    if (c + 2 < n) compute(0);
+    if (c + 3 < n) store(1, R3);
+    __syncthreads();
+    if (c + 6 < n) load(c + 6, R2);
+    if (c + 3 < n) compute(1);
+    if (c + 4 < n) store(0, R0);
     __syncthreads();
   }
 
@@ -395,10 +386,50 @@ __global__ __launch_bounds__(512) void wgrad256_kernel(WgradArgs a) {
     }
 }
 
+// xg, wdg rows and the zeroed pad rows of dgu (GatherArgs). One 16-byte chunk
+// of one row per thread and step.
+__global__ __launch_bounds__(256) void bwd_gather_kernel(GatherArgs a) {
+  const int total = a.total[0];
+  const int cpr = a.H / 8;                 // chunks per token row
+  const int cpr2 = 2 * a.I / 8;            // chunks per dgu row
+  const int64_t n = (int64_t)total * cpr;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int p = (int)(i / cpr), c = (int)(i % cpr);
+    const int slot = a.sorted_slot[p];
+    uint4 xv = make_uint4(0, 0, 0, 0), dv = make_uint4(0, 0, 0, 0);
+    if (slot < a.S) {
+      const size_t t = div_k(slot, a.k_magic);
+      xv = *reinterpret_cast<const uint4*>(a.x + t * a.H + c * 8);
+      const uint4 d = *reinterpret_cast<const uint4*>(a.dout + t * a.H + c * 8);
+      const float w = a.topk_w[slot];
+      const uint32_t in[4] = {d.x, d.y, d.z, d.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        o[h] = f32x2_to_bf16x2(bf16_bits_to_f32(in[h] & 0xffffu) * w,
+                               bf16_bits_to_f32(in[h] >> 16) * w);
+      dv = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      for (int cc = c; cc < cpr2; cc += cpr)  // pad row: zero its dg, du
+        *reinterpret_cast<uint4*>(a.dgu + (size_t)p * 2 * a.I + cc * 8) = make_uint4(0, 0, 0, 0);
+    }
+    *reinterpret_cast<uint4*>(a.xg + (size_t)p * a.H + c * 8) = xv;
+    *reinterpret_cast<uint4*>(a.wdg + (size_t)p * a.H + c * 8) = dv;
+  }
+}
+
+hipError_t launch_bwd_gather(const GatherArgs& a, hipStream_t st) {
+  int64_t blocks = ((int64_t)a.cap * (a.H / 8) + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(bwd_gather_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t st) {
-  if (a.M % kWg2Tile == 0 && a.N % kWg2Tile == 0) {
+  if (a.M % kWg2Tile == 0 && a.N % kWg2Tile == 0 && a.a_mode == 0 && a.b_mode == 0) {
     const int64_t blocks = (int64_t)a.E * (a.M / kWg2Tile) * (a.N / kWg2Tile);
-    hipLaunchKernelGGL(wgrad256_kernel, dim3((unsigned)blocks), dim3(512), 0, st, a);
+    hipLaunchKernelGGL(wgrad_lds_kernel, dim3((unsigned)blocks), dim3(512), 0, st, a);
     return hipGetLastError();
   }
   if (a.M % kWgTile || a.N % kWgTile) return hipErrorInvalidValue;

@@ -196,6 +196,23 @@ struct WgradArgs {
 };
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t st);
 
+// Grouped operand rows of the weight gradients: for each padded row p of the
+// grouping (slot s = sorted_slot[p], token t = s / k), xg[p] = x[t] and
+// wdg[p] = bf16(topk_w[s] * dout[t]); pad rows get zeros there and in dgu.
+struct GatherArgs {
+  const uint16_t* x;           // bf16 [T][H]
+  const uint16_t* dout;        // bf16 [T][H]
+  const float* topk_w;         // [T*k]
+  const int32_t* sorted_slot;  // [capacity]
+  const int32_t* total;        // [1]
+  int H, I, S, cap;
+  uint64_t k_magic;
+  uint16_t* xg;                // bf16 [capacity][H]
+  uint16_t* wdg;               // bf16 [capacity][H]
+  uint16_t* dgu;               // bf16 [capacity][2I]: pad rows zeroed
+};
+hipError_t launch_bwd_gather(const GatherArgs& a, hipStream_t st);
+
 // Router gradient and dx (bwd_dl_kernel, bwd_dx_kernel, bwd_router_kernel).
 struct BwdArgs {
   int T, H, k, E, nparts, kg;
