@@ -269,7 +269,9 @@ def backward_line(steps, T=8192):
     weights and the router bias, the top-k selection held fixed) at the Mixtral shape on a
     prefill batch of T tokens, with the forward timed beside it. Weights and router are the
     bf16 decode workload's (seed 1), x its generator's draw for T tokens, dout seeded normals.
-    TFLOP/s count 6*H*I flops per token-slot for the forward and 12*H*I for the backward."""
+    TFLOP/s count 6*H*I flops per token-slot for the forward and 12*H*I for the backward.
+    The forward is the training one (it keeps the pre-activations g, u) and the backward
+    uses them; backward_recompute_ms is the backward that recomputes them instead."""
     import torch
     import mixture_experts_routed_top_amd as moe
     import workloads
@@ -277,16 +279,17 @@ def backward_line(steps, T=8192):
     log(f"[bench] generating {wl.name} (backward)")
     inp = workloads.generate(wl, threads=16)
     w1, w3, w2 = dev(inp.w1), dev(inp.w3), dev(inp.w2)
-    layer = moe.Layer("bf16", dev(inp.w_router), w1, w3, w2, None, None, None, None, wl.k, T)
+    layer = moe.Layer("bf16", dev(inp.w_router), w1, w3, w2, None, None, None, None, wl.k, T,
+                      save_preact=True)
     w2t, w13t = moe.preshuffle_backward(w1, w3, w2)
     del w1, w3, w2
     x = dev(inp.x)
     dout = dev(workloads.to_bf16_bits(
         np.random.default_rng(7).standard_normal((T, wl.H)).astype(np.float32)))
 
-    def bw():
+    def bw(gu=layer.gu):
         return moe.backward(x, layer.w_router, layer.ids, layer.w, layer.grp, layer.act,
-                            layer.pw, w2t, w13t, dout)
+                            layer.pw, w2t, w13t, dout, gu=gu)
 
     layer(x)
     for _ in range(2):
@@ -307,13 +310,21 @@ def backward_line(steps, T=8192):
     t1.record()
     torch.cuda.synchronize()
     bwd = t0.elapsed_time(t1) / steps
+    t0.record()
+    for _ in range(steps):
+        bw(None)
+    t1.record()
+    torch.cuda.synchronize()
+    bwd_rc = t0.elapsed_time(t1) / steps
     fl = wl.flops()
-    log(f"[bench] {wl.name}: forward {fwd:.3f} ms, backward {bwd:.3f} ms")
+    log(f"[bench] {wl.name}: forward {fwd:.3f} ms, backward {bwd:.3f} ms "
+        f"({bwd_rc:.3f} ms recomputing the pre-activations)")
     out = {"workload": wl.name, "T": T, "block_m": layer.bm,
            "forward_ms": round(fwd, 4), "forward_tflops": round(fl / (fwd * 1e-3) / 1e12, 2),
            "backward_ms": round(bwd, 4),
            "backward_tflops": round(2 * fl / (bwd * 1e-3) / 1e12, 2),
            "backward_frac_of_bf16_peak": round(2 * fl / (bwd * 1e-3) / 1e12 / PEAK["bf16"], 4),
+           "backward_recompute_ms": round(bwd_rc, 4),
            "tokens_per_s_forward_backward": round(T / ((fwd + bwd) * 1e-3), 1)}
     del layer, w2t, w13t, x, dout
     torch.cuda.empty_cache()

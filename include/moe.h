@@ -219,6 +219,21 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, co
                       int block_m, void* act, float* act_amax, hipStream_t stream);
 
 /*
+ * moe_stage1_save_preact - moe_stage1 for the bf16 layer in a training step
+ * (the custom VJP of the talk summary's "Ausblick und Roadmap", 10:07): the
+ * same act, and also the pre-activations the backward needs, so that
+ * moe_backward need not recompute them: gu bf16 [capacity, 2I], g = W1[e] x_t in
+ * columns 0..I-1 and u = W3[e] x_t in I..2I-1 of row p, for the real rows only
+ * (pad rows are left as they are). The values are bit-identical to those
+ * moe_backward recomputes. gu 16-byte aligned, caller-owned; other arguments
+ * and errors as moe_stage1 with dt = MOE_BF16.
+ */
+moe_status moe_stage1_save_preact(const void* x, const void* w13, const int32_t* sorted_slot,
+                                  const int32_t* tile_expert, const int32_t* total_padded, int T,
+                                  int k, int E, int H, int I, int block_m, void* act, void* gu,
+                                  hipStream_t stream);
+
+/*
  * moe_stage2 - grouped down GEMM + weighted scatter-combine (talk summary 5:56,
  * "Scatter"). For each real row p (slot s, token t = s / k, expert e):
  *   y = W2[e] act_p   (FP8: act_p requantised per row, scale = max|act_p|/448,
@@ -297,8 +312,11 @@ moe_status moe_stage2_noalloc(moe_dtype dt, const void* act, const float* act_am
  * moe_backward - the gradients. Inputs from the forward call on the same
  * tokens: x bf16 [T,H], w_router bf16 [E,H], topk_ids / topk_w (moe_route),
  * sorted_slot, tile_expert, expert_offset, total_padded (moe_align with
- * block_m), act bf16 [capacity, I] (moe_stage1), w13 (moe_preshuffle, bf16),
- * w2t, w13t (moe_backward_preshuffle); dout bf16 [T,H].
+ * block_m), act bf16 [capacity, I] (moe_stage1), gu_saved: the pre-activations
+ * from moe_stage1_save_preact on the same call (bf16 [capacity, 2I]), or NULL to
+ * recompute them (one more stage-1 GEMM; the results are the same bits either
+ * way), w13 (moe_preshuffle, bf16), w2t, w13t (moe_backward_preshuffle); dout
+ * bf16 [T,H].
  * Outputs (fp32, overwritten): dx [T,H]; dw1, dw3 [E,I,H]; dw2 [E,H,I];
  * dw_router [E,H]; dbias [E] or NULL. Experts without a slot get zero
  * gradients. workspace [moe_backward_workspace_bytes()] bytes, 256-byte
@@ -313,8 +331,9 @@ int64_t moe_backward_workspace_bytes(int T, int k, int E, int H, int I, int bloc
 moe_status moe_backward(const void* x, const void* w_router, const int32_t* topk_ids,
                         const float* topk_w, const int32_t* sorted_slot,
                         const int32_t* tile_expert, const int32_t* expert_offset,
-                        const int32_t* total_padded, const void* act, const void* w13,
-                        const void* w2t, const void* w13t, const void* dout, int T, int k,
+                        const int32_t* total_padded, const void* act, const void* gu_saved,
+                        const void* w13, const void* w2t, const void* w13t, const void* dout,
+                        int T, int k,
                         int E, int H, int I, int block_m, float* dx, float* dw1, float* dw3,
                         float* dw2, float* dw_router, float* dbias, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);

@@ -215,10 +215,11 @@ def preshuffle_backward(w1, w3, w2):
 
 
 def backward(x, w_router, ids, w, grp: Grouping, act, pw: Weights, w2t, w13t, dout,
-             want_dbias=True):
+             want_dbias=True, gu=None):
     """Gradients of sum <dout, out> of the bf16 layer (moe_backward), from the forward's
-    tokens x, router weights, routing (ids, w), grouping, stage-1 output act and
-    preshuffled weights. -> dict(dx, dw1, dw3, dw2, dw_router, dbias), fp32 device tensors."""
+    tokens x, router weights, routing (ids, w), grouping, stage-1 output act, its saved
+    pre-activations gu (Layer(save_preact=True); None: recomputed) and preshuffled
+    weights. -> dict(dx, dw1, dw3, dw2, dw_router, dbias), fp32 device tensors."""
     T, H = x.shape
     E, I, k, bm = pw.E, pw.I, grp.k, grp.block_m
     dev = x.device
@@ -230,7 +231,8 @@ def backward(x, w_router, ids, w, grp: Grouping, act, pw: Weights, w2t, w13t, do
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
     check(L.moe_backward(_ptr(x), _ptr(w_router), _ptr(ids), _ptr(w), _ptr(grp.sorted_slot),
                          _ptr(grp.tile_expert), _ptr(grp.offset), _ptr(grp.total), _ptr(act),
-                         _ptr(pw.w13), _ptr(w2t), _ptr(w13t), _ptr(dout), T, k, E, H, I, bm,
+                         _ptr(gu), _ptr(pw.w13), _ptr(w2t), _ptr(w13t), _ptr(dout), T, k, E, H,
+                         I, bm,
                          _ptr(g["dx"]), _ptr(g["dw1"]), _ptr(g["dw3"]), _ptr(g["dw2"]),
                          _ptr(g["dw_router"]), _ptr(g["dbias"]), _ptr(ws), ws.numel(),
                          _stream()))
@@ -241,11 +243,16 @@ class Layer:
     """The whole routed MoE layer with buffers allocated once for a fixed batch size.
 
     Weights are preshuffled at construction (load time). __call__ runs route, align,
-    stage 1 and stage 2 on the current stream with no host synchronisation."""
+    stage 1 and stage 2 on the current stream with no host synchronisation. With
+    save_preact (bf16 only, for training), stage 1 also keeps the pre-activations g, u in
+    self.gu for backward(..., gu=layer.gu)."""
 
     def __init__(self, dtype, w_router, w1, w3, w2, s1=None, s3=None, s2=None, bias=None,
-                 k=2, T=None, block_m=None):
+                 k=2, T=None, block_m=None, save_preact=False):
         self.dt = _dt(dtype)
+        if save_preact and self.dt != BF16:
+            raise ValueError("save_preact is for the bf16 layer (the backward is bf16)")
+        self.save_preact = save_preact
         self.fp8 = self.dt == FP8
         self.mx = self.dt in (MXFP8, MXFP4)
         self.E, self.I, self.H = _expert_shape(self.dt, w1)
@@ -276,6 +283,8 @@ class Layer:
                             torch.empty(E + 1, dtype=torch.int32, device=dev),
                             torch.empty(1, dtype=torch.int32, device=dev), T, k, E, self.bm)
         self.act = torch.empty((cap, I), dtype=torch.int16, device=dev)
+        self.gu = torch.empty((cap, 2 * I), dtype=torch.int16, device=dev) \
+            if self.save_preact else None
         n = int(L.moe_stage1_amax_floats(self.dt, T, k, E, H, I, self.bm)) if self.fp8 else 0
         self.amax = torch.empty(max(n, 1), dtype=torch.float32, device=dev) if self.fp8 else None
         nws = stage2_workspace_bytes(self.dt, T, k, E, H, I, self.bm)
@@ -298,9 +307,15 @@ class Layer:
         xin = x if self.dt == BF16 else self.xq
         if events is not None:
             events[0].record()
-        check(L.moe_stage1(self.dt, _ptr(xin), _ptr(self.xs), _ptr(self.pw.w13), _ptr(self.pw.s13),
-                           _ptr(g.sorted_slot), _ptr(g.tile_expert), _ptr(g.total), T, k, E, H,
-                           I, bm, _ptr(self.act), _ptr(self.amax), st))
+        if self.save_preact:
+            check(L.moe_stage1_save_preact(_ptr(xin), _ptr(self.pw.w13), _ptr(g.sorted_slot),
+                                           _ptr(g.tile_expert), _ptr(g.total), T, k, E, H, I,
+                                           bm, _ptr(self.act), _ptr(self.gu), st))
+        else:
+            check(L.moe_stage1(self.dt, _ptr(xin), _ptr(self.xs), _ptr(self.pw.w13),
+                               _ptr(self.pw.s13), _ptr(g.sorted_slot), _ptr(g.tile_expert),
+                               _ptr(g.total), T, k, E, H, I, bm, _ptr(self.act), _ptr(self.amax),
+                               st))
         if events is not None:
             events[1].record()
         check(L.moe_stage2(self.dt, _ptr(self.act), _ptr(self.amax), _ptr(self.pw.w2),

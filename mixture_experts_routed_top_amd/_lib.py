@@ -32,8 +32,9 @@ SIGNATURES = {
     "moe_backward_preshuffle_bytes": (_I64, [_I, _I, _I, _I]),
     "moe_backward_preshuffle": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_backward_workspace_bytes": (_I64, [_I, _I, _I, _I, _I, _I]),
-    "moe_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
-                          _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_stage1_save_preact": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                          _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 

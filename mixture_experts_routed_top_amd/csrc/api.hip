@@ -260,10 +260,12 @@ int64_t moe_stage1_amax_floats(moe_dtype dt, int T, int k, int E, int H, int I, 
   return capacity(T, k, E, block_m) * (2 * (int64_t)I / c.wg_n);
 }
 
-moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, const void* w13,
+namespace {
+
+moe_status stage1_run(moe_dtype dt, const void* x_or_xq, const void* x_scale, const void* w13,
                       const void* s13, const int32_t* sorted_slot, const int32_t* tile_expert,
                       const int32_t* total_padded, int T, int k, int E, int H, int I, int block_m,
-                      void* act, float* act_amax, hipStream_t stream) {
+                      void* act, float* act_amax, void* gu_out, hipStream_t stream) {
   moe_status s = check_stage(dt, T, k, E, H, I, block_m);
   if (s != MOE_OK) return s;
   if (T == 0) return ok();
@@ -309,7 +311,28 @@ moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, co
   a.group_m = group_m(c.mt);
   a.k_magic = k_magic(k);
   a.live_order = c.mt * c.nf < 16;
+  a.gu_out = (uint16_t*)gu_out;
   return hip_status(moe::launch_gemm(dt, 1, c, a, stream), "moe_stage1 launch");
+}
+
+}  // namespace
+
+moe_status moe_stage1(moe_dtype dt, const void* x_or_xq, const void* x_scale, const void* w13,
+                      const void* s13, const int32_t* sorted_slot, const int32_t* tile_expert,
+                      const int32_t* total_padded, int T, int k, int E, int H, int I, int block_m,
+                      void* act, float* act_amax, hipStream_t stream) {
+  return stage1_run(dt, x_or_xq, x_scale, w13, s13, sorted_slot, tile_expert, total_padded, T, k,
+                    E, H, I, block_m, act, act_amax, nullptr, stream);
+}
+
+moe_status moe_stage1_save_preact(const void* x, const void* w13, const int32_t* sorted_slot,
+                                  const int32_t* tile_expert, const int32_t* total_padded, int T,
+                                  int k, int E, int H, int I, int block_m, void* act, void* gu,
+                                  hipStream_t stream) {
+  CHECK(gu, MOE_ERR_INVALID_ARG, "null pointer argument");
+  CHECK(aligned(gu, 16), MOE_ERR_INVALID_ARG, "gu must be 16-byte aligned");
+  return stage1_run(MOE_BF16, x, nullptr, w13, nullptr, sorted_slot, tile_expert, total_padded,
+                    T, k, E, H, I, block_m, act, nullptr, gu, stream);
 }
 
 int64_t moe_stage2_workspace_bytes(moe_dtype dt, int T, int k, int E, int H, int I, int block_m) {
@@ -564,8 +587,9 @@ int64_t moe_backward_workspace_bytes(int T, int k, int E, int H, int I, int bloc
 moe_status moe_backward(const void* x, const void* w_router, const int32_t* topk_ids,
                         const float* topk_w, const int32_t* sorted_slot,
                         const int32_t* tile_expert, const int32_t* expert_offset,
-                        const int32_t* total_padded, const void* act, const void* w13,
-                        const void* w2t, const void* w13t, const void* dout, int T, int k,
+                        const int32_t* total_padded, const void* act, const void* gu_saved,
+                        const void* w13, const void* w2t, const void* w13t, const void* dout,
+                        int T, int k,
                         int E, int H, int I, int block_m, float* dx, float* dw1, float* dw3,
                         float* dw2, float* dw_router, float* dbias, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
@@ -576,6 +600,7 @@ moe_status moe_backward(const void* x, const void* w_router, const int32_t* topk
             total_padded && act && w13 && w2t && w13t && dout && dx && dw1 && dw3 && dw2 &&
             dw_router && workspace,
         MOE_ERR_INVALID_ARG, "null pointer argument");
+  CHECK(aligned(gu_saved, 16), MOE_ERR_INVALID_ARG, "gu_saved must be 16-byte aligned");
   CHECK(aligned(x, 16) && aligned(w_router, 16) && aligned(act, 16) && aligned(w13, 16) &&
             aligned(w2t, 16) && aligned(w13t, 16) && aligned(dout, 16) && aligned(dx, 16) &&
             aligned(dw1, 16) && aligned(dw3, 16) && aligned(dw2, 16) && aligned(dw_router, 16) &&
@@ -587,7 +612,7 @@ moe_status moe_backward(const void* x, const void* w_router, const int32_t* topk
   char* ws = (char*)workspace;
   const int64_t cap = capacity(T, k, E, block_m);
   const int S = T * k;
-  uint16_t* gu = (uint16_t*)(ws + L.gu);
+  const uint16_t* gu = gu_saved ? (const uint16_t*)gu_saved : (const uint16_t*)(ws + L.gu);
   uint16_t* dgu = (uint16_t*)(ws + L.dgu);
   float* dwpart = (float*)(ws + L.dwpart);
   float* part = (float*)(ws + L.part);
@@ -607,13 +632,14 @@ moe_status moe_backward(const void* x, const void* w_router, const int32_t* topk
     a.kg = c.kg;
     a.live_order = c.mt * c.nf < 16;
   };
-  // 1. g, u recomputed from x (the forward's stage 1, pre-activations out).
-  {
+  // 1. g, u recomputed from x (the forward's stage 1, pre-activations out),
+  //    unless the forward kept them (moe_stage1_save_preact).
+  if (!gu_saved) {
     moe::GemmArgs a{};
     common(a, L.c1);
     a.X = (const uint8_t*)x;
     a.W = (const uint8_t*)w13;
-    a.out = gu;
+    a.out = ws + L.gu;
     a.N = 2 * I;
     a.K_bytes = 2 * H;
     a.x_bytes = (int64_t)T * H * 2;

@@ -754,6 +754,21 @@ void gemm_kernel(GemmArgs a) {
           const float uv = acc[m][2 * q + 1][4 * g + r] * us[r];
           h[r] = silu(gv) * uv;
         }
+        if constexpr (DT == 0) {
+          // Training forward: the pre-activations for the backward, stored as
+          // the backward's recompute (epi 1) stores them.
+          if (a.gu_out && rslot[m] < S) {
+            const f32x16& ga = acc[m][2 * q];
+            const f32x16& ua = acc[m][2 * q + 1];
+            uint16_t* grow = a.gu_out + (size_t)(row0 + m * 32 + tok) * 2 * a.I;
+            *reinterpret_cast<uint2*>(grow + i0) =
+                make_uint2(f32x2_to_bf16x2(ga[4 * g], ga[4 * g + 1]),
+                           f32x2_to_bf16x2(ga[4 * g + 2], ga[4 * g + 3]));
+            *reinterpret_cast<uint2*>(grow + a.I + i0) =
+                make_uint2(f32x2_to_bf16x2(ua[4 * g], ua[4 * g + 1]),
+                           f32x2_to_bf16x2(ua[4 * g + 2], ua[4 * g + 3]));
+          }
+        }
         // The row maximum is taken on the fp32 values, before their bf16
         // storage rounding (the requantisation clamps the few stored values
         // that round above it).

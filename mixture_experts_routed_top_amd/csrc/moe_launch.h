@@ -107,6 +107,7 @@ struct GemmArgs {
   int epi;
   const uint16_t* act_in;
   const uint16_t* gu;
+  uint16_t* gu_out;        // BF16 forward stage 1: also stores g, u as epi 1 does, or null
   float* dwpart;
   int unit_w;
   int tail_split;          // GemmCfg::tail_split

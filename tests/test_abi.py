@@ -125,6 +125,14 @@ def test_stage_argument_checks():
     assert status("moe_stage1", *a) == _lib.ERR_INVALID_ARG         # FP8 without act_amax
     a = list(s1); a[9] = 9
     assert status("moe_stage1", *a) == _lib.ERR_UNSUPPORTED         # k > 8
+    # the training forward's stage 1 (bf16): gu is required and 16-byte aligned
+    sp = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 8, 4096, 14336, 32, FAKE, FAKE, None]
+    a = list(sp); a[12] = None
+    assert status("moe_stage1_save_preact", *a) == _lib.ERR_INVALID_ARG
+    a = list(sp); a[12] = FAKE + 8
+    assert status("moe_stage1_save_preact", *a) == _lib.ERR_INVALID_ARG
+    a = list(sp); a[10] = 48
+    assert status("moe_stage1_save_preact", *a) == _lib.ERR_UNSUPPORTED   # block_m
     need = _lib.lib().moe_stage2_workspace_bytes(1, 16, 2, 8, 4096, 14336, 32)
     assert need >= 16 * 2 * 4096 * 4
     assert status("moe_stage2", *stage2_args(need - 1)) == _lib.ERR_WORKSPACE

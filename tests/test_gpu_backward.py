@@ -4,7 +4,8 @@ max|err|/max|ref| <= 2e-2 (the bf16 layer's bound: g, u, dg, du and the
 weighted output gradient are held in bf16 between the launches, a few bf16
 roundings of 2^-9 each), on small and ragged shapes that span several tiles of
 every backward kernel, and on the Mixtral expert shape at the BF16 decode batch
-(T=16). Repeated calls give the same bits."""
+(T=16). Repeated calls give the same bits, and so does the backward from the
+pre-activations the training forward keeps (moe_stage1_save_preact)."""
 import numpy as np
 import pytest
 import torch
@@ -20,23 +21,26 @@ NAMES = ("dx", "dw1", "dw3", "dw2", "dw_router", "dbias")
 
 
 def run_backward(inp, dout, bm):
+    """Gradients with the pre-activations recomputed, twice (the same bits), and with the
+    ones the training forward kept (moe_stage1_save_preact: the same bits again)."""
     wl = inp.wl
     w1, w3, w2 = dev(inp.w1), dev(inp.w3), dev(inp.w2)
     layer = moe.Layer("bf16", dev(inp.w_router), w1, w3, w2, None, None, None, dev(inp.bias),
-                      wl.k, wl.T, bm)
+                      wl.k, wl.T, bm, save_preact=True)
     x = dev(inp.x)
     layer(x)
     w2t, w13t = moe.preshuffle_backward(w1, w3, w2)
     del w1, w3, w2
     d = dev(dout)
-    g = moe.backward(x, layer.w_router, layer.ids, layer.w, layer.grp, layer.act, layer.pw, w2t,
-                     w13t, d)
+    args = (x, layer.w_router, layer.ids, layer.w, layer.grp, layer.act, layer.pw, w2t, w13t, d)
+    g = moe.backward(*args)
     torch.cuda.synchronize()
-    again = moe.backward(x, layer.w_router, layer.ids, layer.w, layer.grp, layer.act, layer.pw,
-                         w2t, w13t, d)
+    again = moe.backward(*args)
+    saved = moe.backward(*args, gu=layer.gu)
     torch.cuda.synchronize()
     for n in NAMES:
         assert torch.equal(g[n], again[n]), f"{n} not reproducible bit for bit"
+        assert torch.equal(g[n], saved[n]), f"{n}: saved pre-activations give other bits"
     return {n: host(g[n]) for n in NAMES}
 
 
