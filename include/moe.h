@@ -148,6 +148,24 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
                      int32_t* expert_offset, int32_t* total_padded, hipStream_t stream);
 
 /*
+ * moe_route_align - moe_route (mx = 0) or moe_route_mx (mx = 1) followed by
+ * moe_align of the ids it writes, for a decode step: the outputs are bit for
+ * bit those of the two calls (x_scale is then moe_route's float x_scale or
+ * moe_route_mx's uint8 x_scale_e8m0). A single token (T = 1) with
+ * H <= 4096 takes one launch (one workgroup routes the token, then groups its
+ * slots, ordered by its own barrier); larger batches take the two calls'
+ * launches. For callers that run the layer at decode batch sizes, where a
+ * launch costs several microseconds of a call of about a hundred.
+ * Arguments, layouts, ownership and errors: those of both calls; block_m and
+ * the grouping outputs as moe_align's (topk_ids is its input).
+ */
+moe_status moe_route_align(const void* x, const void* w_router, const float* bias, int T, int H,
+                           int E, int k, int mx, int32_t* topk_ids, float* topk_w, float* logits,
+                           void* x_q, void* x_scale, int block_m, int32_t* sorted_slot,
+                           int32_t* tile_expert, int32_t* expert_count, int32_t* expert_offset,
+                           int32_t* total_padded, hipStream_t stream);
+
+/*
  * moe_preshuffle - one-time, load-time relayout of the expert weights into the
  * order the matrix-core kernels read them in (talk summary 8:14). A pure byte
  * permutation: each expert's matrix (rows = output features, a row = the

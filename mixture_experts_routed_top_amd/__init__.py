@@ -25,7 +25,7 @@ import torch
 
 from ._lib import BF16, FP8, MXFP4, MXFP8, MoEError, check, lib
 
-__all__ = ["route", "align", "preshuffle", "stage1", "stage2", "forward", "Layer",
+__all__ = ["route", "align", "route_align", "preshuffle", "stage1", "stage2", "forward", "Layer",
            "preshuffle_backward", "backward", "pick_block_m", "align_capacity", "MoEError"]
 
 
@@ -119,6 +119,35 @@ def align(topk_ids: torch.Tensor, E: int, block_m: int) -> Grouping:
     check(lib().moe_align(_ptr(topk_ids), T, k, E, block_m, _ptr(ss), _ptr(te), _ptr(cnt),
                           _ptr(off), _ptr(tot), _stream()))
     return Grouping(ss, te, cnt, off, tot, T, k, E, block_m)
+
+
+def route_align(x: torch.Tensor, w_router: torch.Tensor, k: int, block_m: int,
+                bias: torch.Tensor | None = None, fp8: bool = False, mx: bool = False,
+                want_logits: bool = False):
+    """route() then align() of its ids in one call (one launch for a single token):
+    -> (topk_ids, topk_w, x_q | None, x_scale | None, logits | None, Grouping)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    xq = torch.empty((T, H), dtype=torch.uint8, device=dev) if fp8 or mx else None
+    if mx:
+        xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    else:
+        xs = torch.empty((T,), dtype=torch.float32, device=dev) if fp8 else None
+    cap = max(align_capacity(T, k, E, block_m), 0)
+    g = Grouping(torch.empty(cap, dtype=torch.int32, device=dev),
+                 torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev),
+                 torch.empty(E, dtype=torch.int32, device=dev),
+                 torch.empty(E + 1, dtype=torch.int32, device=dev),
+                 torch.empty(1, dtype=torch.int32, device=dev), T, k, E, block_m)
+    check(lib().moe_route_align(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, int(mx),
+                                _ptr(ids), _ptr(w), _ptr(lg), _ptr(xq), _ptr(xs), block_m,
+                                _ptr(g.sorted_slot), _ptr(g.tile_expert), _ptr(g.count),
+                                _ptr(g.offset), _ptr(g.total), _stream()))
+    return ids, w, xq, xs, lg, g
 
 
 @dataclass
@@ -299,11 +328,11 @@ class Layer:
             self._alloc(T)
         L, st = lib(), _stream()
         E, H, I, k, bm, g = self.E, self.H, self.I, self.k, self.bm, self.grp
-        route_fn = L.moe_route_mx if self.mx else L.moe_route
-        check(route_fn(_ptr(x), _ptr(self.w_router), _ptr(self.bias), T, H, E, k,
-                       _ptr(self.ids), _ptr(self.w), None, _ptr(self.xq), _ptr(self.xs), st))
-        check(L.moe_align(_ptr(self.ids), T, k, E, bm, _ptr(g.sorted_slot), _ptr(g.tile_expert),
-                          _ptr(g.count), _ptr(g.offset), _ptr(g.total), st))
+        # route + align (one launch for a single-token batch)
+        check(L.moe_route_align(_ptr(x), _ptr(self.w_router), _ptr(self.bias), T, H, E, k,
+                                int(self.mx), _ptr(self.ids), _ptr(self.w), None, _ptr(self.xq),
+                                _ptr(self.xs), bm, _ptr(g.sorted_slot), _ptr(g.tile_expert),
+                                _ptr(g.count), _ptr(g.offset), _ptr(g.total), st))
         xin = x if self.dt == BF16 else self.xq
         if events is not None:
             events[0].record()

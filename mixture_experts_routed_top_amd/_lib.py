@@ -20,6 +20,8 @@ SIGNATURES = {
     "moe_route_mx": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_align_capacity": (_I64, [_I, _I, _I, _I]),
     "moe_align": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_route_align": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P,
+                             _P, _P]),
     "moe_preshuffle_bytes": (_I64, [_I, _I, _I, _I, _I]),
     "moe_preshuffle": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_stage1_amax_floats": (_I64, [_I, _I, _I, _I, _I, _I, _I]),

@@ -185,6 +185,37 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
   return hip_status(moe::launch_align(a, stream), "moe_align launch");
 }
 
+moe_status moe_route_align(const void* x, const void* w_router, const float* bias, int T, int H,
+                           int E, int k, int mx, int32_t* topk_ids, float* topk_w, float* logits,
+                           void* x_q, void* x_scale, int block_m, int32_t* sorted_slot,
+                           int32_t* tile_expert, int32_t* expert_count, int32_t* expert_offset,
+                           int32_t* total_padded, hipStream_t stream) {
+  CHECK(mx == 0 || mx == 1, MOE_ERR_INVALID_ARG, "mx=%d (0 or 1)", mx);
+  CHECK(T >= 0 && H > 0, MOE_ERR_INVALID_ARG, "sizes T=%d H=%d", T, H);
+  CHECK(E >= 1 && k >= 1, MOE_ERR_INVALID_ARG, "E=%d k=%d", E, k);
+  CHECK(E <= 64 && k <= E && k <= 8, MOE_ERR_UNSUPPORTED, "E=%d k=%d (need E<=64, k<=min(E,8))",
+        E, k);
+  CHECK(H % 128 == 0 && H <= 8192, MOE_ERR_UNSUPPORTED,
+        "H=%d must be a multiple of 128, at most 8192", H);
+  CHECK((int64_t)T * H <= ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED, "T*H too large");
+  CHECK(valid_bm(block_m), MOE_ERR_UNSUPPORTED, "block_m=%d (need 32, 64, 128 or 256)", block_m);
+  CHECK((int64_t)T * k <= (1 << 30), MOE_ERR_UNSUPPORTED, "T*k too large");
+  if (T == 0) return ok();
+  CHECK(x && w_router && topk_ids && topk_w, MOE_ERR_INVALID_ARG, "null x/w_router/topk_ids/topk_w");
+  CHECK(!x_q || x_scale, MOE_ERR_INVALID_ARG, "x_q given without x_scale");
+  CHECK(!mx || x_q, MOE_ERR_INVALID_ARG, "mx=1 needs x_q and x_scale");
+  CHECK(aligned(x, 16) && aligned(w_router, 16) && aligned(x_q, 8), MOE_ERR_INVALID_ARG,
+        "x and w_router must be 16-byte aligned, x_q 8-byte aligned");
+  CHECK(sorted_slot && tile_expert && expert_count && expert_offset && total_padded,
+        MOE_ERR_INVALID_ARG, "null grouping pointer");
+  moe::RouteArgs a{(const uint16_t*)x, (const uint16_t*)w_router, bias, T, H, E, k, topk_ids,
+                   topk_w, logits, (uint8_t*)x_q, mx ? nullptr : (float*)x_scale,
+                   mx ? (uint8_t*)x_scale : nullptr};
+  moe::AlignArgs g{topk_ids, T * k, E, block_m, sorted_slot, tile_expert,
+                   expert_count, expert_offset, total_padded};
+  return hip_status(moe::launch_route_align(a, g, stream), "moe_route_align launch");
+}
+
 int64_t moe_preshuffle_bytes(moe_dtype dt, int E, int H, int I, int which) {
   if (!valid_dt(dt) || E < 1 || H < 1 || I < 1) return -1;
   const int64_t es = dt == MOE_BF16 ? 2 : 1;

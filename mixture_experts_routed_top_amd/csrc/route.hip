@@ -19,6 +19,7 @@
 //    W_r staged once per workgroup in LDS (batched 16-byte copies), the
 //    experts' logits folded together (fold_many); for E <= 8 and H <= 4096,
 //    W_r is staged as fp32 and each wave prefetches its next rows.
+#include "align_small.h"
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -114,7 +115,9 @@ __device__ __forceinline__ float fold64(float v) {
 
 // Top-k over the logits held by lanes e < E (lane e holds logit e), weights,
 // outputs (lane 0 writes).
-__device__ __forceinline__ void select_topk(const RouteArgs& a, int t, int lane, float mine) {
+// With lds_ids, lane 0 also leaves the ids there, at t*k + j.
+__device__ __forceinline__ void select_topk(const RouteArgs& a, int t, int lane, float mine,
+                                            int32_t* lds_ids = nullptr) {
   const int E = a.E, k = a.k;
   int off0 = 32;
   while (off0 > 1 && off0 >= E) off0 >>= 1;
@@ -154,6 +157,7 @@ __device__ __forceinline__ void select_topk(const RouteArgs& a, int t, int lane,
       if (j >= k) break;
       a.topk_ids[(size_t)t * k + j] = top_i[j];
       a.topk_w[(size_t)t * k + j] = num[j] / den;
+      if (lds_ids) lds_ids[t * k + j] = top_i[j];
     }
   }
 }
@@ -277,6 +281,37 @@ __global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
     }
     __syncthreads();
   }
+}
+
+// Tiny batches (T <= kTinyRouteTokens) with their grouping in the same launch:
+// one workgroup of 4T waves; waves 4t .. 4t+3 do for token t what
+// route_block_kernel does, then one wave sorts the T*k slots
+// (align_small_wave) from the ids the top-k left in LDS. The workgroup
+// barrier orders the two steps, so no synchronisation between workgroups is
+// needed; the grouping is read by the next launch only. This saves a
+// single-token decode call one launch.
+template <int NCH>
+__global__ __launch_bounds__(256 * kTinyRouteTokens) void route_align_tiny_kernel(RouteArgs a,
+                                                                                 AlignArgs g) {
+  __shared__ float logit[kTinyRouteTokens][64];
+  __shared__ int32_t ids[kTinyRouteTokens * 8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = wave >> 2, w4 = wave & 3;  // blockDim = 256 * T: t < T
+  const int nchunk = a.H / 8;
+  uint4 xv[NCH];
+  load_row<NCH>(a.x + (size_t)t * a.H, lane, nchunk, xv);
+  for (int e = w4; e < a.E; e += 4) {
+    float l = fold64(lane_partial<NCH>(xv, a.w_router + (size_t)e * a.H, lane, nchunk));
+    if (a.bias) l = l + a.bias[e];
+    if (lane == 0) logit[t][e] = l;
+  }
+  __syncthreads();
+  if (w4 == 0) {
+    select_topk(a, t, lane, lane < a.E ? logit[t][lane] : -__builtin_inff(), ids);
+    if (a.x_q) quantise<NCH>(a, t, lane, nchunk, xv);
+  }
+  __syncthreads();
+  if (wave == 0) align_small_wave(g, ids, lane);
 }
 
 // The fixed fold (p[l] += p[l+off], off = 32 .. 1) of M experts' lane partials
@@ -654,6 +689,21 @@ hipError_t launch_nch(const RouteArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_route_align(const RouteArgs& a, const AlignArgs& g, hipStream_t st) {
+  const int nch = (a.H / 8 + 63) / 64;
+  if (a.T >= 1 && a.T <= kTinyRouteTokens && a.k <= 8 && g.S <= kSmallSlots && nch <= 8) {
+    const dim3 block(256 * a.T);
+    if (nch <= 4)
+      hipLaunchKernelGGL((route_align_tiny_kernel<4>), dim3(1), block, 0, st, a, g);
+    else
+      hipLaunchKernelGGL((route_align_tiny_kernel<8>), dim3(1), block, 0, st, a, g);
+    return hipGetLastError();
+  }
+  hipError_t err = launch_route(a, st);
+  if (err != hipSuccess) return err;
+  return launch_align(g, st);
+}
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   const int nch = (a.H / 8 + 63) / 64;  // chunks per lane

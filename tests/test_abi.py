@@ -99,6 +99,31 @@ def test_align_argument_checks():
     assert status("moe_align", *a) == _lib.OK
 
 
+def test_route_align_argument_checks():
+    # x, w_router, bias, T, H, E, k, mx, ids, w, logits, x_q, x_scale, block_m,
+    # sorted_slot, tile_expert, count, offset, total, stream
+    base = [FAKE, FAKE, None, 4, 4096, 8, 2, 0, FAKE, FAKE, None, FAKE, FAKE, 32,
+            FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    a = list(base); a[7] = 2
+    assert status("moe_route_align", *a) == _lib.ERR_INVALID_ARG      # mx is 0 or 1
+    a = list(base); a[13] = 48
+    assert status("moe_route_align", *a) == _lib.ERR_UNSUPPORTED      # block_m
+    a = list(base); a[4] = 100
+    assert status("moe_route_align", *a) == _lib.ERR_UNSUPPORTED      # H % 128
+    a = list(base); a[6] = 9
+    assert status("moe_route_align", *a) == _lib.ERR_UNSUPPORTED      # k > E
+    a = list(base); a[7] = 1; a[11] = None; a[12] = None
+    assert status("moe_route_align", *a) == _lib.ERR_INVALID_ARG      # MX needs x_q, scales
+    a = list(base); a[12] = None
+    assert status("moe_route_align", *a) == _lib.ERR_INVALID_ARG      # x_q without x_scale
+    a = list(base); a[16] = None
+    assert status("moe_route_align", *a) == _lib.ERR_INVALID_ARG      # null grouping output
+    a = list(base); a[1] = FAKE + 4
+    assert status("moe_route_align", *a) == _lib.ERR_INVALID_ARG      # misaligned w_router
+    a = list(base); a[3] = 0; a[0] = None; a[14] = None
+    assert status("moe_route_align", *a) == _lib.OK                  # T = 0: nothing to do
+
+
 def test_preshuffle_argument_checks():
     base = [1, 8, 4096, 14336, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
     a = list(base); a[0] = 7
