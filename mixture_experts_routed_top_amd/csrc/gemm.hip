@@ -1083,17 +1083,20 @@ GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
   }
   if (c.mt == 1 && kbytes % (4 * 128) == 0) {
     c.ksplit = 4;
-    // Split the reduction over workgroups too until the launch has a full
-    // round of live workgroups (each split g adds a partial, summed in order).
-    // Measured, FP8 decode on the Mixtral shape: T=1 102 -> 98 us with 4
-    // splits instead of 7 (the former target of 1024 from a looser estimate
-    // of the live tiles), T=16 and T=64 2-4 us faster.
+    // When the live workgroups do not fill a round, split the reduction over
+    // workgroups too (each split g adds a partial, summed in order) until they
+    // fill two, with at most four splits. Measured, FP8 decode on the Mixtral
+    // shape: T=1 102 -> 98 us with 4 splits instead of 7; T=4 (five live
+    // experts, 320 workgroups unsplit) 185 -> 183 us with 4 splits instead of
+    // 2 (1.25 rounds); T=16 and T=64 fill a round unsplit (2 splits: no gain).
     const int chunks = kbytes / (4 * 128);
     const int64_t base = live_mtiles(T, k, E, 32) * (H / (32 * c.nf));
-    for (int cand = 2; cand <= 16; ++cand) {
-      if (chunks % cand) continue;
-      if (base * c.kg >= kDecodeRound) break;
-      c.kg = cand;
+    if (base < kDecodeRound) {
+      for (int cand = 2; cand <= 4; ++cand) {
+        if (chunks % cand) continue;
+        if (base * c.kg >= 2 * kDecodeRound) break;
+        c.kg = cand;
+      }
     }
   }
   set_pipeline(c, dt);
