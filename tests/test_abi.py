@@ -54,9 +54,14 @@ def test_size_queries():
     cap = L.moe_align_capacity(8192, 2, 8, 128)
     # one partial maximum per row and per stage-1 workgroup column block (512 composite rows)
     assert L.moe_stage1_amax_floats(1, 8192, 2, 8, 4096, 14336, 128) == cap * (2 * 14336 // 512)
-    # decode tiles (32 rows) use 64-row column blocks
+    # decode tiles (32 rows): 64-row column blocks, 128-row ones where the reduction is
+    # split over two waves (one round of workgroups, or every expert live)
+    cap4 = L.moe_align_capacity(4, 2, 8, 32)
+    assert L.moe_stage1_amax_floats(1, 4, 2, 8, 4096, 14336, 32) == cap4 * (2 * 14336 // 64)
     cap32 = L.moe_align_capacity(16, 2, 8, 32)
-    assert L.moe_stage1_amax_floats(1, 16, 2, 8, 4096, 14336, 32) == cap32 * (2 * 14336 // 64)
+    assert L.moe_stage1_amax_floats(1, 16, 2, 8, 4096, 14336, 32) == cap32 * (2 * 14336 // 128)
+    cap1 = L.moe_align_capacity(1, 2, 8, 32)
+    assert L.moe_stage1_amax_floats(1, 1, 2, 8, 4096, 14336, 32) == cap1 * (2 * 14336 // 128)
     assert L.moe_stage2_workspace_bytes(0, 32, 2, 8, 128, 256, 64) == 64 * 128 * 4
     assert L.moe_stage2_workspace_bytes(1, 3, 2, 8, 128, 256, 32) == -1  # FP8 needs H % 256
 
