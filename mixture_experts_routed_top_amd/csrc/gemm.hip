@@ -1107,17 +1107,21 @@ GemmCfg stage2_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
   if (c.mt == 1 && kbytes % (4 * 128) == 0) {
     c.ksplit = 4;
     // When the live workgroups do not fill a round, split the reduction over
-    // workgroups too (each split g adds a partial, summed in order) until they
-    // fill two, with at most four splits. Measured, FP8 decode on the Mixtral
-    // shape: T=1 102 -> 98 us with 4 splits instead of 7; T=4 (five live
-    // experts, 320 workgroups unsplit) 185 -> 183 us with 4 splits instead of
-    // 2 (1.25 rounds); T=16 and T=64 fill a round unsplit (2 splits: no gain).
+    // workgroups too (each split g adds a partial, summed in order): FP8 until
+    // they fill two rounds, with at most four splits; the others until they
+    // fill one. Measured on the Mixtral shape, FP8 decode: T=1 102 -> 98 us
+    // with 4 splits instead of 7; T=4 (five live experts, 320 workgroups
+    // unsplit) 185 -> 183 us with 4 splits instead of 2 (1.25 rounds); T=16
+    // and T=64 fill a round unsplit (2 splits: no gain). MXFP4 (half the
+    // weight bytes per workgroup) at T=4: 2 splits, 4 were 3.6 us slower.
     const int chunks = kbytes / (4 * 128);
     const int64_t base = live_mtiles(T, k, E, 32) * (H / (32 * c.nf));
+    const int64_t target = dt == 1 ? 2 * kDecodeRound : kDecodeRound;
+    const int max_kg = dt == 1 ? 4 : 16;
     if (base < kDecodeRound) {
-      for (int cand = 2; cand <= 4; ++cand) {
+      for (int cand = 2; cand <= max_kg; ++cand) {
         if (chunks % cand) continue;
-        if (base * c.kg >= 2 * kDecodeRound) break;
+        if (base * c.kg >= target) break;
         c.kg = cand;
       }
     }
