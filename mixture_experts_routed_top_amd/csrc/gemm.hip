@@ -1076,14 +1076,15 @@ GemmCfg stage1_cfg(int dt, int T, int k, int E, int H, int I, int bm) {
   if (c.mt == 1 && (H * (dt == 0 ? 2 : 1)) % (4 * 128) == 0) {
     c.ksplit = 4;
     if (dt == 3) c.nf = 4;
-    // FP8: two waves along the reduction instead (128 features, half as many
-    // workgroups, twice the work each) when those workgroups fit one round or
-    // every expert is expected to be live (the weights of all experts
-    // streamed in fewer, longer workgroups). Measured on the Mixtral shape,
-    // median per layer call: T=1 91.0 -> 89.4 us, T=16 273.6 -> 271.5, T=64
-    // 278.9 -> 274.2; at T=4 (five live experts, 1120 workgroups: a thin
-    // last round) 182.9 -> 184.2, so it keeps four.
-    if (dt == 1) {
+    // FP8 and MXFP8: two waves along the reduction instead (128 features,
+    // half as many workgroups, twice the work each) when those workgroups fit
+    // one round or every expert is expected to be live (the weights of all
+    // experts streamed in fewer, longer workgroups). Measured on the Mixtral
+    // shape, median per layer call: FP8 T=1 91.0 -> 89.4 us, T=16 273.6 ->
+    // 271.5, T=64 278.9 -> 274.2, and at T=4 (five live experts, 1120
+    // workgroups: a thin last round) 182.9 -> 184.2, so it keeps four; MXFP8
+    // T=16 282.5 -> 277.8; bf16 T=16 486.7 -> 491.7, so bf16 keeps four.
+    if (dt == 1 || dt == 2) {
       const int64_t live = live_mtiles(T, k, E, 32);
       if (live * (2 * (int64_t)I / 128) <= kDecodeRound || live >= E) c.ksplit = 2;
     }
