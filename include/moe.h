@@ -123,7 +123,8 @@ moe_status moe_route_mx(const void* x, const void* w_router, const float* bias, 
 
 /*
  * moe_align - groups the T*k token-slots by expert and pads each group to the
- * M-tile (the "dynamic expert sizes" of the talk summary, 5:56).
+ * M-tile (the per-expert group sizes that change with every batch, talk
+ * summary 5:56).
  *
  * Slot s = t*k + j is token t's j-th choice. For e = 0..E-1 in turn, the
  * group of e lists every slot with topk_ids[s] == e in ascending s, followed

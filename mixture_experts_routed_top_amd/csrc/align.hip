@@ -1,6 +1,7 @@
 // Grouping of token-slots by expert, padded to the M-tile: a stable counting
-// sort (the "dynamic expert sizes" of the routed MoE GEMM in the FlyDSL-in-JAX
-// talk summary, 5:56). Integer work only: bit-exact by construction. Three
+// sort (the per-expert group sizes that change with every batch in the routed
+// MoE GEMM of the FlyDSL-in-JAX talk summary, 5:56). Integer work only:
+// bit-exact by construction. Three
 // kernels by size, each one workgroup:
 //  - align_small_kernel (S <= 128 slots, decode): one wave, ids in registers,
 //    counts and ranks from ballots, offsets from a shuffle scan;

@@ -1,6 +1,7 @@
 // One-time, load-time relayout of expert weights into matrix-core operand
-// order (the "einmaliger Load-Time-Preshuffle" of the FlyDSL-in-JAX talk
-// summary, 8:14). A byte permutation; each thread moves one 16-byte piece.
+// order (the preshuffle that the FlyDSL-in-JAX talk summary runs once when the
+// weights are loaded, 8:14). A byte permutation; each thread moves one 16-byte
+// piece.
 //
 // Fragment = 32 output rows x 64 reduction bytes (one 32x32 matrix-core step:
 // 64 e4m3fn or 32 bf16 values), 2 KB, stored as two 1 KB pieces. In piece pc,
