@@ -22,6 +22,7 @@ def make(dtype, T, H, I, E, k, seed):
 
 
 @pytest.mark.parametrize("dtype,T,H,I,E,k,bm", [
+    ("fp8", 1, 1024, 1024, 8, 2, 32),      # one token: route and grouping in one launch
     ("fp8", 16, 1024, 1024, 8, 2, 32),     # decode shape: split reductions, one-wave align
     ("bf16", 700, 512, 768, 8, 2, 256),    # stage 2 tail pieces and their reduction
     ("mxfp4", 16, 1024, 1024, 8, 2, 32),   # E2M1 decode: MX token codes, 128-feature stage 1
