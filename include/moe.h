@@ -5,11 +5,11 @@
  * The layer is the one the first page (the FlyDSL-in-JAX talk summary) describes
  * under "Optimierung gerouteter MoE-GEMMs" (5:56) and "End-to-End-Integration in
  * MaxText" (8:14): tokens are routed to their top-2 experts, the selected tokens
- * are gathered, a grouped ("Group") GEMM computes each expert's gate and up
+ * are gathered, a grouped GEMM computes each expert's gate and up
  * projections with a SwiGLU, a second grouped GEMM computes the down
  * projection, and the results are scattered back and combined with the routing
- * weights; expert weights are rearranged once at load time ("einmaliger
- * Load-Time-Preshuffle"). The same talk summary describes the call boundary it
+ * weights; expert weights are rearranged once, when they are loaded (8:14).
+ * The same talk summary describes the call boundary it
  * used ("fly_call", 4:07; the C trampoline that unpacks buffers, scalars and
  * streams, 5:05): this header is the same kind of boundary, a set of C calls
  * taking device pointers, sizes and a stream.
