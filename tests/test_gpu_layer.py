@@ -66,6 +66,9 @@ def run_stages(inp, bm):
     ("fp8", 5, 1024, 1024, 8, 2, 32),      # decode: reduction split over waves and workgroups
     ("fp8", 256, 512, 4096, 8, 2, 128),    # 128-row tiles, one round: stage 2 split over 4 workgroups
     ("bf16", 9, 256, 256, 1, 1, 32),       # E = 1: a plain SwiGLU MLP
+    ("fp8", 48, 256, 512, 16, 4, 32),      # E = 16, k = 4: finer-grained experts
+    ("bf16", 40, 256, 256, 64, 8, 32),     # E = 64, k = 8: the widest routing supported
+    ("fp8", 600, 512, 512, 64, 8, 128),    # E = 64, k = 8 on 128-row tiles (about 75 slots per expert)
 ])
 def test_stages_match_oracle(dtype, T, H, I, E, k, bm):
     inp = make(dtype, T, H, I, E, k, seed=T)

@@ -117,6 +117,7 @@ def run_stages(inp, bm):
     (150, 768, 512, 8, 2, 128),     # H % 512 != 0: stage 2 on 2 fragments per wave
     (130, 1024, 768, 6, 3, 64),     # k = 3 over 6 experts, 64-row tiles
     (17, 256, 256, 4, 1, 32),       # k = 1
+    (48, 256, 512, 16, 4, 32),      # E = 16, k = 4: finer-grained experts
     (5, 1024, 1024, 8, 2, 32),      # decode: reduction split over waves and workgroups
     (33, 8192, 256, 4, 2, 32),      # largest H: the whole stage-1 code tile
     (6, 256, 16384, 2, 1, 32),      # largest I: the whole stage-2 code tile
