@@ -76,6 +76,7 @@ def make(T, H, I, E, k, seed, bias=False):
     (700, 256, 256, 8, 2, 256, True),   # block_m 256, several 128-row tiles per expert
     (17, 256, 256, 4, 1, 32, False),    # k = 1
     (9, 256, 256, 1, 1, 32, False),     # E = 1: a plain SwiGLU MLP, no router gradient
+    (48, 256, 256, 16, 4, 32, True),    # E = 16, k = 4: finer-grained experts
 ])
 def test_backward_matches_oracle(T, H, I, E, k, bm, bias):
     inp, dout = make(T, H, I, E, k, seed=T + I, bias=bias)
