@@ -6,8 +6,7 @@ scales). It holds none of the layer's own arithmetic: no routing, no top-k, no
 GEMM, no SwiGLU, no activation quantisation. Both the CPU oracle and the HIP
 path take their inputs from here, so they see identical bytes.
 
-Shapes and distributions follow the five workloads of the benchmark spec:
-a tiny bf16 layer, and the Mixtral 8x7B expert layer (H=4096, I=14336, E=8,
+Five workloads: a tiny bf16 layer, and the Mixtral 8x7B expert layer (H=4096, I=14336, E=8,
 top-2) in bf16 decode, fp8 prefill, an fp8 decode sweep and an fp8 layer with
 skewed routing. Mixtral 8x7B in FP8 is the model the first page (the FlyDSL-in-JAX
 talk summary, "Wichtigste Punkte", 5:56-9:14) measures on; the pages use no dataset.
@@ -20,8 +19,8 @@ The MXFP8 workloads (the second page, the PyTorch FlyDSL backend news item,
 "Grenzen und Folgen für Anwender": E4M3 values with one E8M0 scale per 32 along
 the reduction; its "Gemessene Leistung" measurements start from quantised
 operands) store the weights the same way per 32-value block of each row, with
-the OCP MX scale 2^(floor(log2 amax) - 8). The MXFP4 workloads (same section:
-"packed FP4-E2M1 operands") store E2M1 weight codes, two per byte, with the
+the OCP MX scale 2^(floor(log2 amax) - 8). The MXFP4 workloads (the packed E2M1
+operands of the same section) store E2M1 weight codes, two per byte, with the
 scale 2^(floor(log2 amax) - 2) (6 = 1.5 * 2^2 is E2M1's largest value).
 """
 from __future__ import annotations

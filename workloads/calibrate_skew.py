@@ -1,7 +1,7 @@
 """Calibrate the router bias of the skewed Mixtral fp8 workload (T=16384).
 
-The task asks for a per-expert router bias under which expert 0 receives about
-40% of the token-slots and experts 6 and 7 under 3% each. With bias
+The skewed workload uses a per-expert router bias under which expert 0 receives
+about 40% of the token-slots and experts 6 and 7 under 3% each. With bias
 b = (beta, 0, 0, 0, 0, 0, -gamma, -gamma), this script routes the workload's
 seeded tokens with the CPU oracle and bisects gamma (shares of experts 6 and 7
 near 2%) and beta (share of expert 0 near 40%), then writes skew_bias.json.
