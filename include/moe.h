@@ -306,8 +306,8 @@ moe_status moe_stage2_noalloc(moe_dtype dt, const void* act, const float* act_am
 
 /*
  * Backward pass of the bf16 layer: the custom VJP the talk summary names as
- * its next step ("Ausblick und Roadmap", 10:07; "broader backward coverage" in
- * the glance summary's "What's Next?"). For an output gradient dout, the
+ * its next step ("Ausblick und Roadmap", 10:07; the glance summary's
+ * "What's Next?" also lists wider backward support). For an output gradient dout, the
  * gradients of sum_t <dout_t, out_t> with respect to x, W1, W3, W2, W_r and the
  * router bias, the forward's top-k selection held fixed (it is piecewise
  * constant). Per slot s = t*k + j of expert e with routing weight w_j:
