@@ -11,7 +11,10 @@
 // the fold is a shuffle tree. A lane keeps its chunks of the token row in
 // registers (16-byte loads, at most kMaxChunks per lane: H <= 64*8*kMaxChunks).
 //
-// Two launch shapes:
+// Three launch shapes:
+//  - a single token routed and grouped in one launch (moe_route_align): one
+//    workgroup of eight waves, one expert each; then wave 0 selects the top-k
+//    and groups the slots while wave 1 quantises the row;
 //  - small batches: one workgroup per token; its four waves split the experts
 //    (expert e on wave e%4) so that all loads of the token are in flight at
 //    once, then wave 0 selects the top-k and quantises the row;
@@ -284,34 +287,41 @@ __global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
 }
 
 // Tiny batches (T <= kTinyRouteTokens) with their grouping in the same launch:
-// one workgroup of 4T waves; waves 4t .. 4t+3 do for token t what
-// route_block_kernel does, then one wave sorts the T*k slots
-// (align_small_wave) from the ids the top-k left in LDS. The workgroup
-// barrier orders the two steps, so no synchronisation between workgroups is
-// needed; the grouping is read by the next launch only. This saves a
-// single-token decode call one launch.
+// one workgroup of 8T waves. Each of waves 8t .. 8t+7 loads token t's row
+// together with the W_r row of one expert (experts w, w+8, ... past eight) and
+// folds that logit; after a barrier wave 8t takes the top-k and then sorts
+// the T*k slots (align_small_wave) from the ids the top-k left in LDS, while
+// wave 8t+1 quantises the row. The workgroup barrier and the wave's own order
+// sequence the steps, so no synchronisation between workgroups is needed;
+// the grouping is read by the next launch only. This saves a single-token
+// decode call one launch.
 template <int NCH>
-__global__ __launch_bounds__(256 * kTinyRouteTokens) void route_align_tiny_kernel(RouteArgs a,
+__global__ __launch_bounds__(512 * kTinyRouteTokens) void route_align_tiny_kernel(RouteArgs a,
                                                                                  AlignArgs g) {
   __shared__ float logit[kTinyRouteTokens][64];
   __shared__ int32_t ids[kTinyRouteTokens * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = wave >> 2, w4 = wave & 3;  // blockDim = 256 * T: t < T
+  const int t = wave >> 3, w8 = wave & 7;  // blockDim = 512 * T: t < T
   const int nchunk = a.H / 8;
   uint4 xv[NCH];
   load_row<NCH>(a.x + (size_t)t * a.H, lane, nchunk, xv);
-  for (int e = w4; e < a.E; e += 4) {
+  for (int e = w8; e < a.E; e += 8) {
     float l = fold64(lane_partial<NCH>(xv, a.w_router + (size_t)e * a.H, lane, nchunk));
     if (a.bias) l = l + a.bias[e];
     if (lane == 0) logit[t][e] = l;
   }
   __syncthreads();
-  if (w4 == 0) {
+  static_assert(kTinyRouteTokens == 1, "the grouping below reads one token's ids");
+  if (w8 == 0) {
     select_topk(a, t, lane, lane < a.E ? logit[t][lane] : -__builtin_inff(), ids);
-    if (a.x_q) quantise<NCH>(a, t, lane, nchunk, xv);
+    // The ids are in LDS from lane 0 of this same wave, whose LDS accesses
+    // complete in order: a wave-scope fence suffices, and the grouping does
+    // not wait for the quantisation running in wave 1.
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    align_small_wave(g, ids, lane);
+  } else if (w8 == 1 && a.x_q) {
+    quantise<NCH>(a, t, lane, nchunk, xv);
   }
-  __syncthreads();
-  if (wave == 0) align_small_wave(g, ids, lane);
 }
 
 // The fixed fold (p[l] += p[l+off], off = 32 .. 1) of M experts' lane partials
@@ -693,7 +703,7 @@ hipError_t launch_nch(const RouteArgs& a, hipStream_t st) {
 hipError_t launch_route_align(const RouteArgs& a, const AlignArgs& g, hipStream_t st) {
   const int nch = (a.H / 8 + 63) / 64;
   if (a.T >= 1 && a.T <= kTinyRouteTokens && a.k <= 8 && g.S <= kSmallSlots && nch <= 8) {
-    const dim3 block(256 * a.T);
+    const dim3 block(512 * a.T);
     if (nch <= 4)
       hipLaunchKernelGGL((route_align_tiny_kernel<4>), dim3(1), block, 0, st, a, g);
     else
