@@ -15,9 +15,9 @@
 //  - a single token routed and grouped in one launch (moe_route_align): one
 //    workgroup of eight waves, one expert each; then wave 0 selects the top-k
 //    and groups the slots while wave 1 quantises the row;
-//  - small batches: one workgroup per token; its four waves split the experts
-//    (expert e on wave e%4) so that all loads of the token are in flight at
-//    once, then wave 0 selects the top-k and quantises the row;
+//  - small batches: one workgroup per token; its eight waves (four for H >
+//    4096) split the experts so that all loads of the token are in flight at
+//    once, then wave 0 selects the top-k while wave 1 quantises the row;
 //  - large batches (E <= 16): one wave per two tokens (four for H <= 2048),
 //    W_r staged once per workgroup in LDS (batched 16-byte copies), the
 //    experts' logits folded together (fold_many); for E <= 8 and H <= 4096,
@@ -263,26 +263,33 @@ __device__ __forceinline__ void load_row(const uint16_t* xr, int lane, int nchun
   }
 }
 
-// One workgroup per token; wave w computes the logits of experts w, w+4, ...
+// One workgroup of W waves per token (eight; four for rows past 4096 values,
+// whose chunk registers would not fit two waves per SIMD); wave w computes the
+// logits of experts w, w+W, ... (for W experts every W_r row is requested at
+// once), then wave 0 takes the top-k while wave 1 quantises the row.
 template <int NCH>
-__global__ __launch_bounds__(256) void route_block_kernel(RouteArgs a) {
+constexpr int block_waves() { return NCH <= 8 ? 8 : 4; }
+
+template <int NCH>
+__global__ __launch_bounds__(64 * block_waves<NCH>()) void route_block_kernel(RouteArgs a) {
+  constexpr int W = block_waves<NCH>();
   __shared__ float logit[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nchunk = a.H / 8;
   for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
     uint4 xv[NCH];
     load_row<NCH>(a.x + (size_t)t * a.H, lane, nchunk, xv);
-    for (int e = wave; e < a.E; e += 4) {
+    for (int e = wave; e < a.E; e += W) {
       float l = fold64(lane_partial<NCH>(xv, a.w_router + (size_t)e * a.H, lane, nchunk));
       if (a.bias) l = l + a.bias[e];
       if (lane == 0) logit[e] = l;
     }
     __syncthreads();
-    if (wave == 0) {
+    if (wave == 0)
       select_topk(a, t, lane, lane < a.E ? logit[lane] : -__builtin_inff());
-      if (a.x_q) quantise<NCH>(a, t, lane, nchunk, xv);
-    }
-    __syncthreads();
+    else if (wave == 1 && a.x_q)
+      quantise<NCH>(a, t, lane, nchunk, xv);
+    __syncthreads();  // logit is rewritten for the next token
   }
 }
 
@@ -693,7 +700,8 @@ hipError_t launch_nch(const RouteArgs& a, hipStream_t st) {
                          a);
   } else {
     const int blocks = a.T < 4096 ? a.T : 4096;
-    hipLaunchKernelGGL((route_block_kernel<NCH>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((route_block_kernel<NCH>), dim3(blocks), dim3(64 * block_waves<NCH>()), 0,
+                       st, a);
   }
   return hipGetLastError();
 }
