@@ -143,3 +143,20 @@ def test_fp8_quantisation_over_many_binades():
     wr = workloads.to_bf16_bits(rng.standard_normal((8, H)) / 64)
     check_route(x, wr, None, 2, tag="many binades")
 
+
+
+@pytest.mark.parametrize("T,H,E,k", [
+    (5, 8192, 8, 2),    # rows past 4096 values: four waves per token
+    (3, 6144, 8, 2),    # 12 chunks per lane: the 16-chunk kernel with four chunks past the row
+    (7, 4096, 16, 4),   # sixteen experts: two per wave of the eight-wave kernel
+    (2, 4096, 3, 2),    # fewer experts than waves
+])
+def test_route_small_batches_wave_split(T, H, E, k):
+    """The small-batch launch shape (one workgroup per token, the experts split over its
+    waves, the top-k and the quantisation in separate waves): ids, logits, codes and
+    scales bit-exact, with a bias."""
+    rng = np.random.default_rng(T * 131 + H + E)
+    x = workloads.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wr = workloads.to_bf16_bits((rng.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32))
+    bias = rng.standard_normal(E).astype(np.float32) * 0.1
+    check_route(x, wr, bias, k, tag=f"small batch E={E}")
