@@ -20,6 +20,7 @@ CASES = [
     (1, 4096, 8, 2, "mx", True, 32),
     (1, 4096, 8, 2, "none", False, 128),   # bf16 layer: no token quantisation
     (1, 2048, 64, 8, "fp8", True, 64),     # 8 slots over 64 experts
+    (1, 4096, 16, 4, "fp8", True, 32),     # two experts per wave
     (1, 512, 6, 3, "mx", False, 32),
     (1, 256, 1, 1, "fp8", False, 256),
     # the two calls' launches
